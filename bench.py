@@ -1,0 +1,232 @@
+#!/usr/bin/env python3
+"""Benchmark of the attention hot path on one MI355X.
+
+One step = one pass of the whole path over one batch of synthetic input:
+  * the causal prefill workload B=4, H=16 (MHA), Sq=Skv=2048, d=128, through
+    attn_fwd (Q tile load, K/V tile streaming, Q*K^T, mask, online softmax,
+    P*V, epilogue), and
+  * the GQA decode workload B=64, Hq=32, Hkv=8, Skv=4096, d=128, 8 key
+    chunks, through attn_decode (split kernel + log-sum-exp merge).
+Inputs are seeded bf16 N(0,1) draws already resident in HBM when timing
+starts.  ``value`` is the prefill throughput in algorithmic TFLOP/s (4*d per
+allowed query/key pair); the decode rate in algorithmic GB/s (K and V read
+once, plus Q, O and LSE) is reported beside it.  Kernel durations come from
+HIP events on the stream the kernels are launched on.
+
+Prints ONE JSON line.  ``--gpus N`` with N > 1 is refused: this build runs on
+one GPU.
+"""
+from __future__ import annotations
+
+import argparse
+import hashlib
+import json
+import os
+import sys
+import time
+
+import numpy as np
+
+ROOT = os.path.dirname(os.path.abspath(__file__))
+sys.path.insert(0, ROOT)
+
+PEAK_BF16_TFLOPS = 2500.0     # MI355X dense bf16 MFMA
+PEAK_HBM_GBS = 8000.0         # MI355X HBM3E
+METRIC = "attn fwd TFLOP/s (bf16 causal prefill) + decode KV GB/s, % of roofline"
+KERNEL_SOURCES = ["tiled_attention_transformer_amd/csrc/attn_fwd.hip",
+                  "tiled_attention_transformer_amd/csrc/attn_decode.hip",
+                  "tiled_attention_transformer_amd/csrc/tile_common.h",
+                  "tiled_attention_transformer_amd/csrc/kernels.h"]
+
+
+def kernel_hash() -> str:
+    h = hashlib.sha256()
+    for f in KERNEL_SOURCES:
+        with open(os.path.join(ROOT, f), "rb") as fh:
+            h.update(fh.read())
+    return h.hexdigest()[:16]
+
+
+def prefill_flops(B, H, Sq, Skv, d, causal):
+    if causal:
+        off = Skv - Sq
+        pairs = sum(max(0, min(Skv, i + off + 1)) for i in range(Sq))
+    else:
+        pairs = Sq * Skv
+    return 4.0 * d * pairs * B * H
+
+
+def decode_bytes(B, Hq, Hkv, Skv, d):
+    kv = 2 * B * Skv * Hkv * d * 2
+    return kv + B * Hq * d * 2 + B * Hq * d * 2 + B * Hq * 4
+
+
+def load_traffic(kind: str):
+    """HBM bytes per launch measured with rocprofv3 counters, if taken on this kernel."""
+    path = os.path.join(ROOT, "profiles", "traffic.json")
+    if not os.path.exists(path):
+        return None
+    try:
+        t = json.load(open(path))
+    except (OSError, ValueError):
+        return None
+    if t.get("kernel_hash") != kernel_hash() or kind not in t:
+        return None
+    return t[kind]
+
+
+def cpu_baseline(spec, data, max_pairs):
+    """The C oracle on a bounded sample of the prefill workload (rank 0 only)."""
+    from oracle import cpu
+    B, H, S, d = spec["B"], spec["Hq"], spec["Sq"], spec["d"]
+    # whole heads, taken in a fixed order, until the sample holds max_pairs pairs
+    pairs_per_head = S * (S + 1) // 2
+    nheads = max(1, min(B * H, int(max_pairs // pairs_per_head)))
+    heads = [(b, h) for b in range(B) for h in range(H)][:nheads]
+    rows = np.array([(b, h, i) for (b, h) in heads for i in range(S)], dtype=np.int64)
+    threads = cpu.num_threads(0)
+    t0 = time.perf_counter()
+    cpu.attn_rows(data["q"], data["k"], data["v"], spec["scale"], True, rows)
+    dt = time.perf_counter() - t0
+    flops = 4.0 * d * pairs_per_head * nheads
+    return {"value": flops / dt / 1e12, "unit": "TFLOP/s", "cores": threads, "kind": "oracle",
+            "seconds": round(dt, 3),
+            "sample": "%d of %d (batch, head) pairs of the causal prefill workload, all %d rows "
+                      "each (fp64 C loops, OpenMP)" % (nheads, B * H, S)}
+
+
+def main():
+    ap = argparse.ArgumentParser(description=__doc__.split("\n")[0])
+    ap.add_argument("--gpus", type=int, default=1)
+    ap.add_argument("--steps", type=int, default=50)
+    ap.add_argument("--warmup", type=int, default=10)
+    ap.add_argument("--no-cpu-baseline", action="store_true")
+    ap.add_argument("--cpu-pairs", type=float, default=2.0e8,
+                    help="allowed query/key pairs in the CPU-baseline sample")
+    ap.add_argument("--copy-calibration", action="store_true",
+                    help="also run a plain 1 GiB device copy (counter calibration)")
+    args = ap.parse_args()
+    if args.gpus != 1:
+        print("bench.py runs on one GPU only; --gpus %d is not supported by this build"
+              % args.gpus, file=sys.stderr)
+        sys.exit(2)
+    if args.steps < 1 or args.warmup < 0:
+        sys.exit("steps must be >= 1 and warmup >= 0")
+
+    import torch
+    import synth_inputs as si
+    from tiled_attention_transformer_amd import api
+
+    dev = torch.device("cuda:0")
+    api._lib.load()
+
+    def to_dev(bits):
+        return torch.from_numpy(np.ascontiguousarray(bits).view(np.int16)).view(torch.bfloat16).to(dev)
+
+    pspec, pdata = si.make_config(2)
+    dspec, ddata = si.make_config(4)
+    q, k, v = (to_dev(pdata[n]) for n in "qkv")
+    o = torch.empty_like(q)
+    lse = torch.empty((pspec["B"], pspec["Hq"], pspec["Sq"]), dtype=torch.float32, device=dev)
+    dq, dk, dv = (to_dev(ddata[n]) for n in "qkv")
+    do = torch.empty_like(dq)
+    dlse = torch.empty((dspec["B"], dspec["Hq"]), dtype=torch.float32, device=dev)
+    nsplit = dspec["num_splits"]
+    ws = torch.empty(max(1, api.attn_decode_workspace_bytes(dspec["B"], dspec["Hq"], dspec["Hkv"],
+                                                            dspec["Skv"], dspec["d"], nsplit)),
+                     dtype=torch.uint8, device=dev)
+    stream = torch.cuda.current_stream()
+
+    def prefill():
+        api.attn_fwd(q, k, v, o=o, lse=lse, scale=pspec["scale"], causal=True, stream=stream)
+
+    def decode():
+        api.attn_decode(dq, dk, dv, o=do, lse=dlse, scale=dspec["scale"], num_splits=nsplit,
+                        workspace=ws, stream=stream)
+
+    # cold (first) calls, reported apart from the steady state
+    e0, e1, e2 = (torch.cuda.Event(enable_timing=True) for _ in range(3))
+    e0.record(stream)
+    prefill()
+    e1.record(stream)
+    decode()
+    e2.record(stream)
+    torch.cuda.synchronize()
+    cold_prefill_ms, cold_decode_ms = e0.elapsed_time(e1), e1.elapsed_time(e2)
+
+    for _ in range(args.warmup):
+        prefill()
+        decode()
+    if args.copy_calibration:
+        src = torch.empty(1 << 30, dtype=torch.uint8, device=dev)
+        dst = torch.empty_like(src)
+        dst.copy_(src)
+        torch.cuda.synchronize()
+        del src, dst
+
+    K = args.steps
+    ev = [[torch.cuda.Event(enable_timing=True) for _ in range(3)] for _ in range(K)]
+    torch.cuda.synchronize()
+    t0 = time.perf_counter()
+    for i in range(K):
+        ev[i][0].record(stream)
+        prefill()
+        ev[i][1].record(stream)
+        decode()
+        ev[i][2].record(stream)
+    torch.cuda.synchronize()
+    wall = time.perf_counter() - t0
+    pre_ms = np.array([a.elapsed_time(b) for a, b, _ in ev])
+    dec_ms = np.array([b.elapsed_time(c) for _, b, c in ev])
+
+    flops = prefill_flops(pspec["B"], pspec["Hq"], pspec["Sq"], pspec["Skv"], pspec["d"], True)
+    nbytes = decode_bytes(dspec["B"], dspec["Hq"], dspec["Hkv"], dspec["Skv"], dspec["d"])
+    pre_avg, dec_avg = float(pre_ms.mean()), float(dec_ms.mean())
+    tflops = flops / (pre_avg * 1e-3) / 1e12
+    gbs = nbytes / (dec_avg * 1e-3) / 1e9
+
+    traffic = load_traffic("prefill")
+    result = {
+        "metric": METRIC,
+        "value": round(tflops, 2),
+        "unit": "TFLOP/s",
+        "n_gpus": 1,
+        "steps": K,
+        "warmup": args.warmup,
+        "ms_per_step": round(wall * 1e3 / K, 4),
+        "higher_is_better": True,
+        "scaling": "weak",
+        "vs_baseline": None,
+        "dtype": "bf16",
+        "data": "synthetic (seeded bf16 N(0,1))",
+        "config": {
+            "workload": "causal prefill B4 H16 Sq=Skv=2048 d128 + GQA decode B64 Hq32 Hkv8 "
+                        "Skv4096 d128, 8 KV chunks",
+            "prefill": {"B": 4, "Hq": 16, "Hkv": 16, "S": 2048, "d": 128, "causal": True,
+                        "seed": pspec["seed"], "algorithmic_flop": flops},
+            "decode": {"B": 64, "Hq": 32, "Hkv": 8, "Skv": 4096, "d": 128, "num_splits": nsplit,
+                       "seed": dspec["seed"], "algorithmic_bytes": nbytes},
+        },
+        "prefill_ms": {"mean": round(pre_avg, 5), "median": round(float(np.median(pre_ms)), 5),
+                       "min": round(float(pre_ms.min()), 5), "cold": round(cold_prefill_ms, 5)},
+        "roofline": {"bound": "mfma", "achieved": round(tflops, 2), "peak": PEAK_BF16_TFLOPS,
+                     "unit": "TFLOP/s", "frac": round(tflops / PEAK_BF16_TFLOPS, 4),
+                     "traffic": traffic, "kernel": "attn_fwd_kernel<128,causal>"},
+        "decode": {
+            "value": round(gbs, 1), "unit": "GB/s",
+            "ms": {"mean": round(dec_avg, 5), "median": round(float(np.median(dec_ms)), 5),
+                   "min": round(float(dec_ms.min()), 5), "cold": round(cold_decode_ms, 5)},
+            "roofline": {"bound": "hbm", "achieved": round(gbs, 1), "peak": PEAK_HBM_GBS,
+                         "unit": "GB/s", "frac": round(gbs / PEAK_HBM_GBS, 4),
+                         "traffic": load_traffic("decode"),
+                         "kernel": "attn_decode_split_kernel<128> + attn_decode_combine_kernel<128>"},
+        },
+        "kernel_hash": kernel_hash(),
+    }
+    if not args.no_cpu_baseline:
+        result["cpu_baseline"] = cpu_baseline(pspec, pdata, args.cpu_pairs)
+    print(json.dumps(result), flush=True)
+
+
+if __name__ == "__main__":
+    main()

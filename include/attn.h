@@ -1,0 +1,146 @@
+/*
+ * attn.h -- C ABI of the fused, tiled attention forward pass for AMD MI355X
+ * (gfx950).  Library: tiled_attention_transformer_amd/libattn.so.
+ *
+ * What is computed (lecompute.fr, "FlashAttention-4 : limites du calcul
+ * matriciel", section "Entre deux multiplications il faut fabriquer les
+ * poids"): for every query row, scores against the keys, a softmax that turns
+ * them into positive weights summing to one, and the weighted sum of the value
+ * rows:
+ *
+ *     O[i] = sum_j softmax_j(scale * q_i . k_j) * v_j      (j over allowed keys)
+ *     LSE[i] = log(sum_j exp(scale * q_i . k_j))          (natural log)
+ *
+ * The work is cut into query and key tiles and accumulated tile by tile with
+ * an online softmax (same section, and section "Déplacer une partie des
+ * exponentielles": one common scale for the old and the new contributions),
+ * so the score matrix never reaches device memory.
+ *
+ * Conventions shared by every entry point
+ * ---------------------------------------
+ *  * Tensors are contiguous, row-major, bfloat16 (q, k, v, o) and float32
+ *    (lse), passed as raw DEVICE pointers.  The caller allocates and owns
+ *    every buffer; the library allocates nothing and keeps no state between
+ *    calls, so calls are thread-safe.
+ *  * Pointers to bf16 tensors must be 16-byte aligned; lse and the decode
+ *    workspace 4- and 16-byte aligned respectively.
+ *  * Head grouping (GQA/MQA): query head h reads KV head h / (Hq / Hkv);
+ *    Hq must be a multiple of Hkv.
+ *  * Head dimension d must be 64 or 128.  scale must be finite and > 0
+ *    (typically 1/sqrt(d)).
+ *  * Causal masking is bottom-right aligned: query row i (0-based) may see key
+ *    j iff j <= i + (Skv - Sq).  With Sq == Skv this is the usual lower
+ *    triangle (same page, section "Le FP4 ajoute un compromis numérique",
+ *    on the causal mask).  A row with no allowed key gets O = 0 and
+ *    LSE = -inf.
+ *  * lse may be NULL, in which case it is not written.
+ *  * Every call is asynchronous on `stream` (0 = the null stream) and never
+ *    synchronises.  Arguments are validated on the host BEFORE any launch; on
+ *    a nonzero status nothing was launched and no output was written.  A
+ *    launch failure returns ATTN_ERR_HIP (outputs then undefined).
+ *  * Results are deterministic: the same inputs give bitwise the same
+ *    outputs (fixed tile order, no atomics).
+ */
+#ifndef ATTN_H
+#define ATTN_H
+
+#include <stddef.h>
+#include <hip/hip_runtime_api.h>
+
+#ifdef __cplusplus
+extern "C" {
+#endif
+
+typedef enum {
+    ATTN_OK = 0,
+    ATTN_ERR_NULLPTR = 1,        /* a required pointer is NULL                   */
+    ATTN_ERR_SHAPE = 2,          /* a size is < 1 or too large                   */
+    ATTN_ERR_UNSUPPORTED_D = 3,  /* d is not 64 or 128                           */
+    ATTN_ERR_GQA_RATIO = 4,      /* Hq is not a multiple of Hkv                  */
+    ATTN_ERR_ALIGNMENT = 5,      /* a pointer is not suitably aligned            */
+    ATTN_ERR_WORKSPACE = 6,      /* decode workspace missing or too small        */
+    ATTN_ERR_SEQLENS = 7,        /* malformed cumulative sequence offsets        */
+    ATTN_ERR_HIP = 8,            /* the HIP runtime reported an error on launch  */
+    ATTN_ERR_SCALE = 9           /* scale is not finite and > 0                  */
+} attn_status_t;
+
+/*
+ * Prefill / full forward over a fixed batch.
+ *   q, o : [B, Sq, Hq, d]  bf16        k, v : [B, Skv, Hkv, d]  bf16
+ *   lse  : [B, Hq, Sq]     fp32 (or NULL)
+ *   causal: 0 = every key, nonzero = bottom-right causal mask.
+ * Query tiles of 128 rows, key tiles of 64 keys; under the causal mask the
+ * key tiles above a query tile's diagonal are never loaded.
+ */
+attn_status_t attn_fwd(const void *q, const void *k, const void *v, void *o, float *lse,
+                       int B, int Hq, int Hkv, int Sq, int Skv, int d, float scale,
+                       int causal, hipStream_t stream);
+
+/*
+ * Forward over a packed ragged batch (variable lengths).
+ *   q, o : [total_q, Hq, d] bf16      k, v : [total_k, Hkv, d] bf16
+ *   lse  : [Hq, total_q] fp32 (or NULL)
+ *   cu_seqlens_q, cu_seqlens_k : DEVICE int32 arrays of nseq+1 cumulative
+ *   offsets (start at 0, non-decreasing, last = total).  Sequence s owns query
+ *   rows cu_seqlens_q[s] .. cu_seqlens_q[s+1]-1 and keys cu_seqlens_k[s] ..
+ *   cu_seqlens_k[s+1]-1; it never sees another sequence's keys, and the
+ *   causal mask applies inside each sequence.
+ *   max_seqlen_q must be >= every query length (it sizes the grid); rows of a
+ *   longer sequence beyond it are not computed.  The kernels read the offsets
+ *   on the device and treat a sequence whose offsets are decreasing or fall
+ *   outside [0, total] as empty, so malformed offsets cannot cause an
+ *   out-of-bounds access; use attn_varlen_check() on a host copy to reject
+ *   them up front.
+ */
+attn_status_t attn_fwd_varlen(const void *q, const void *k, const void *v, void *o, float *lse,
+                              const int *cu_seqlens_q, const int *cu_seqlens_k, int nseq,
+                              int total_q, int total_k, int max_seqlen_q, int max_seqlen_k,
+                              int Hq, int Hkv, int d, float scale, int causal,
+                              hipStream_t stream);
+
+/*
+ * Host-side check of a HOST copy of cumulative offsets: nseq >= 1,
+ * cu[0] == 0, non-decreasing, cu[nseq] == total.  If max_seqlen is not NULL
+ * it receives the largest length.  Returns ATTN_OK or ATTN_ERR_SEQLENS
+ * (ATTN_ERR_NULLPTR for a NULL cu).  Touches no device.
+ */
+attn_status_t attn_varlen_check(const int *cu_seqlens_host, int nseq, int total,
+                                int *max_seqlen);
+
+/*
+ * Split-KV decode: one query token per sequence against a KV cache.
+ *   q, o : [B, Hq, d] bf16      k_cache, v_cache : [B, Skv, Hkv, d] bf16
+ *   lse  : [B, Hq] fp32 (or NULL)
+ * The query is the newest position, so all Skv cached keys are attended.
+ * The cache is cut into num_splits chunks of ceil(Skv / num_splits) keys;
+ * one kernel computes a normalised partial output and its log-sum-exp per
+ * (sequence, KV head, chunk) -- every query head of a KV group shares one
+ * pass over that chunk of K and V -- and a second kernel merges the chunks:
+ * LSE = M + log(sum_s exp(lse_s - M)), O = sum_s exp(lse_s - LSE) * O_s.
+ * num_splits <= 0 lets the library choose (attn_decode_pick_splits).
+ * workspace: DEVICE scratch of at least attn_decode_workspace_bytes(...)
+ * bytes, 16-byte aligned, owned by the caller, may be reused between calls
+ * on the same stream (not by calls that run concurrently).  With
+ * num_splits == 1 no workspace is needed (may be NULL).
+ */
+attn_status_t attn_decode(const void *q, const void *k_cache, const void *v_cache, void *o,
+                          float *lse, int B, int Hq, int Hkv, int Skv, int d, float scale,
+                          int num_splits, void *workspace, size_t workspace_bytes,
+                          hipStream_t stream);
+
+/* Bytes of decode workspace for these sizes (0 when num_splits resolves to
+ * 1; num_splits <= 0 means the library's choice, as in attn_decode).  Returns
+ * 0 for invalid sizes. */
+size_t attn_decode_workspace_bytes(int B, int Hq, int Hkv, int Skv, int d, int num_splits);
+
+/* The number of KV chunks attn_decode uses when passed num_splits <= 0. */
+int attn_decode_pick_splits(int B, int Hq, int Hkv, int Skv);
+
+/* Static text for a status code (never NULL). */
+const char *attn_status_string(attn_status_t status);
+
+#ifdef __cplusplus
+}
+#endif
+
+#endif /* ATTN_H */

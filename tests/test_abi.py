@@ -1,0 +1,143 @@
+"""The C ABI on a host with no GPU: every declared symbol is exported, and
+invalid arguments are rejected on the host before any launch.
+
+Only argument combinations that FAIL validation are passed here (fake device
+pointers are never launched on), so no HIP call is made.
+"""
+import ctypes
+import os
+import re
+
+import pytest
+
+import tiled_attention_transformer_amd as pkg
+from tiled_attention_transformer_amd import _lib
+
+ROOT = os.path.dirname(os.path.dirname(os.path.abspath(__file__)))
+HEADER = os.path.join(ROOT, "include", "attn.h")
+
+OK, NULLPTR, SHAPE, BAD_D, GQA, ALIGN, WS, SEQ, HIP, SCALE = range(10)
+P = 1 << 20          # a 16-byte aligned fake address (never dereferenced)
+
+
+def declared_functions():
+    text = open(HEADER).read()
+    text = re.sub(r"/\*.*?\*/", "", text, flags=re.S)
+    return sorted(set(re.findall(r"\b(attn_[a-z0-9_]+)\s*\(", text)))
+
+
+@pytest.fixture(scope="module")
+def lib():
+    return pkg.load()
+
+
+def test_library_exports_every_declared_symbol(lib):
+    names = declared_functions()
+    assert len(names) == 7, names
+    raw = ctypes.CDLL(_lib.LIB_PATH)
+    for n in names:
+        assert hasattr(raw, n), n
+    assert set(names) == set(_lib.SIGNATURES)
+
+
+def test_status_strings(lib):
+    for s in range(10):
+        text = lib.attn_status_string(s)
+        assert text and text != b"unknown status"
+    assert lib.attn_status_string(99) == b"unknown status"
+
+
+def fwd(lib, q=P, k=P, v=P, o=P, lse=None, B=1, Hq=2, Hkv=2, Sq=8, Skv=8, d=128, scale=0.1,
+        causal=0):
+    return lib.attn_fwd(q, k, v, o, lse, B, Hq, Hkv, Sq, Skv, d, scale, causal, None)
+
+
+def test_fwd_validation(lib):
+    assert fwd(lib, q=None) == NULLPTR
+    assert fwd(lib, o=None) == NULLPTR
+    assert fwd(lib, B=0) == SHAPE
+    assert fwd(lib, Sq=-1) == SHAPE
+    assert fwd(lib, Skv=0) == SHAPE
+    assert fwd(lib, Sq=1 << 30, B=1 << 10) == SHAPE
+    assert fwd(lib, d=96) == BAD_D
+    assert fwd(lib, d=256) == BAD_D
+    assert fwd(lib, Hq=6, Hkv=4) == GQA
+    assert fwd(lib, scale=0.0) == SCALE
+    assert fwd(lib, scale=-1.0) == SCALE
+    assert fwd(lib, scale=float("nan")) == SCALE
+    assert fwd(lib, scale=float("inf")) == SCALE
+    assert fwd(lib, q=P + 8) == ALIGN
+    assert fwd(lib, v=P + 2) == ALIGN
+    assert fwd(lib, lse=P + 2) == ALIGN
+    # the first failing rule wins, in a fixed order
+    assert fwd(lib, q=None, d=96) == NULLPTR
+    assert fwd(lib, d=96, Hq=3, Hkv=2) == BAD_D
+
+
+def varlen(lib, cu_q=P, cu_k=P, nseq=2, tq=10, tk=10, mq=6, mk=6, Hq=2, Hkv=1, d=64,
+           scale=0.1, q=P):
+    return lib.attn_fwd_varlen(q, P, P, P, None, cu_q, cu_k, nseq, tq, tk, mq, mk, Hq, Hkv, d,
+                               scale, 1, None)
+
+
+def test_varlen_validation(lib):
+    assert varlen(lib, cu_q=None) == NULLPTR
+    assert varlen(lib, q=None) == NULLPTR
+    assert varlen(lib, nseq=0) == SHAPE
+    assert varlen(lib, tq=0) == SHAPE
+    assert varlen(lib, mq=11) == SEQ          # longer than the whole batch
+    assert varlen(lib, d=32) == BAD_D
+    assert varlen(lib, Hq=3, Hkv=2) == GQA
+    assert varlen(lib, scale=0.0) == SCALE
+    assert varlen(lib, cu_q=P + 2) == ALIGN
+
+
+def check(lib, cu, total):
+    import numpy as np
+    a = np.asarray(cu, dtype=np.int32)
+    mx = ctypes.c_int(-1)
+    st = lib.attn_varlen_check(a.ctypes.data_as(ctypes.c_void_p), len(a) - 1, total,
+                               ctypes.byref(mx))
+    return st, mx.value
+
+
+def test_varlen_check(lib):
+    assert check(lib, [0, 3, 3, 10], 10) == (OK, 7)
+    assert check(lib, [0, 5], 5) == (OK, 5)
+    assert check(lib, [1, 3, 10], 10)[0] == SEQ      # does not start at 0
+    assert check(lib, [0, 3, 2, 10], 10)[0] == SEQ   # decreasing
+    assert check(lib, [0, 3, 9], 10)[0] == SEQ       # does not end at total
+    assert check(lib, [0], 0)[0] == SEQ              # no sequence
+    assert lib.attn_varlen_check(None, 1, 1, None) == NULLPTR
+
+
+def decode(lib, B=2, Hq=8, Hkv=2, Skv=100, d=128, scale=0.1, splits=4, ws=P, wsb=1 << 30,
+           q=P, o=P):
+    return lib.attn_decode(q, P, P, o, None, B, Hq, Hkv, Skv, d, scale, splits, ws, wsb, None)
+
+
+def test_decode_validation(lib):
+    assert decode(lib, q=None) == NULLPTR
+    assert decode(lib, B=0) == SHAPE
+    assert decode(lib, Skv=0) == SHAPE
+    assert decode(lib, d=80) == BAD_D
+    assert decode(lib, Hq=6, Hkv=4) == GQA
+    assert decode(lib, scale=float("nan")) == SCALE
+    assert decode(lib, o=P + 4) == ALIGN
+    need = lib.attn_decode_workspace_bytes(2, 8, 2, 100, 128, 4)
+    assert need == 4 * 2 * 8 * (128 + 1) * 4
+    assert decode(lib, ws=None) == WS
+    assert decode(lib, wsb=need - 1) == WS
+    assert decode(lib, ws=P + 4, wsb=need) == ALIGN
+    assert lib.attn_decode_workspace_bytes(2, 8, 2, 100, 128, 1) == 0
+    assert lib.attn_decode_workspace_bytes(2, 8, 3, 100, 128, 4) == 0    # bad ratio
+    assert lib.attn_decode_workspace_bytes(2, 8, 2, 100, 96, 4) == 0     # bad d
+
+
+def test_decode_split_choice(lib):
+    assert lib.attn_decode_pick_splits(64, 32, 8, 4096) == 4
+    assert lib.attn_decode_pick_splits(1, 32, 8, 4096) == 16
+    assert lib.attn_decode_pick_splits(1, 1, 1, 100) == 1
+    assert lib.attn_decode_pick_splits(1, 3, 2, 100) == 0
+    auto = lib.attn_decode_workspace_bytes(1, 32, 8, 4096, 128, 0)
+    assert auto == lib.attn_decode_workspace_bytes(1, 32, 8, 4096, 128, 16)

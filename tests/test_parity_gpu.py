@@ -1,0 +1,272 @@
+"""GPU parity: the HIP path (through the C ABI) against the CPU oracle.
+
+O (bf16) must be within 2e-2 max-abs of the unrounded fp64 oracle and LSE
+(fp32) within 1e-3, on the same seeded bf16 inputs.  Small cases compare
+every output; the five workloads at full size compare sampled rows that the
+oracle computes one by one, in the same launch configuration the benchmark
+times.
+"""
+import numpy as np
+import pytest
+
+import synth_inputs as si
+from oracle import cpu, ref
+from tests.gpu_util import (assert_close, bf16_to_np, f32_to_np, sample_rows, to_dev)
+
+pytestmark = pytest.mark.gpu
+
+
+@pytest.fixture(scope="module")
+def api():
+    from tiled_attention_transformer_amd import api as a
+    a._lib.load()
+    return a
+
+
+def run_fwd(api, dev, data, scale, causal):
+    import torch
+    q, k, v = (to_dev(data[n], dev) for n in "qkv")
+    o, lse = api.attn_fwd(q, k, v, scale=scale, causal=causal)
+    torch.cuda.synchronize()
+    return bf16_to_np(o), f32_to_np(lse)
+
+
+# ---------------------------------------------------------------- small, whole
+
+SMALL = [  # B, Sq, Skv, Hq, Hkv, d, causal
+    (1, 256, 256, 2, 2, 64, False),
+    (1, 300, 300, 2, 1, 128, True),      # ragged last query tile and key tile
+    (2, 129, 257, 4, 2, 64, True),       # Sq < Skv, bottom-right causal
+    (1, 200, 77, 2, 2, 128, True),       # Sq > Skv: leading rows fully masked
+    (1, 200, 77, 2, 2, 64, False),
+    (1, 1, 300, 4, 1, 128, False),       # a single query row
+    (1, 1, 1, 1, 1, 64, True),           # smallest case
+    (2, 384, 384, 8, 8, 128, True),      # several full tiles
+    (1, 33, 500, 8, 2, 128, False),
+    (1, 130, 130, 4, 4, 64, True),
+    (3, 65, 200, 6, 3, 128, False),
+]
+
+
+@pytest.mark.parametrize("case", SMALL, ids=lambda c: "B%d_Sq%d_Skv%d_Hq%d_Hkv%d_d%d_%s" % (
+    *c[:6], "causal" if c[6] else "full"))
+def test_small_prefill_matches_oracle(api, dev, case):
+    B, Sq, Skv, Hq, Hkv, d, causal = case
+    data = si.make_prefill(100 + Sq + Skv, B, Hq, Hkv, Sq, Skv, d)
+    scale = si.default_scale(d)
+    o, lse = run_fwd(api, dev, data, scale, causal)
+    o_ref, lse_ref = cpu.attn_full(data["q"], data["k"], data["v"], scale, causal)
+    assert_close(o, o_ref, lse, lse_ref, str(case))
+    if causal and Sq > Skv:
+        assert np.all(o[:, :Sq - Skv] == 0)
+
+
+def test_tiny_config_whole_and_golden(api, dev):
+    """Workload 1 (B1 H2 S256 d64, non-causal) compared in full."""
+    spec, data = si.make_config(1)
+    o, lse = run_fwd(api, dev, data, spec["scale"], False)
+    o_ref, lse_ref = ref.attention(*(si.bf16_to_f64(data[n]) for n in "qkv"), spec["scale"], False)
+    assert_close(o, o_ref, lse, lse_ref, "workload 1")
+
+
+# -------------------------------------------------- the workloads at full size
+
+@pytest.mark.parametrize("n", [2, 3])
+def test_full_size_prefill_sampled_rows(api, dev, n):
+    spec, data = si.make_config(n)
+    o, lse = run_fwd(api, dev, data, spec["scale"], True)
+    rows = sample_rows(spec["B"], spec["Hq"], spec["Sq"], 160, seed=n,
+                       extra_rows=(spec["Sq"] // 2, spec["Sq"] // 2 - 1, 63, 64))
+    o_ref, lse_ref = cpu.attn_rows(data["q"], data["k"], data["v"], spec["scale"], True, rows)
+    b, h, i = rows[:, 0], rows[:, 1], rows[:, 2]
+    assert_close(o[b, i, h], o_ref, lse[b, h, i], lse_ref, "workload %d" % n)
+    # every output finite, and causal row 0 is exactly v_0 rounded to bf16
+    assert np.all(np.isfinite(o)) and np.all(np.isfinite(lse))
+    v = si.bf16_to_f64(data["v"])
+    np.testing.assert_array_equal(o[:, 0], v[:, 0, :, :].repeat(spec["Hq"] // spec["Hkv"], axis=1))
+
+
+def test_decode_workload_whole(api, dev):
+    import torch
+    spec, data = si.make_config(4)
+    q, k, v = (to_dev(data[x], dev) for x in "qkv")
+    o, lse = api.attn_decode(q, k, v, scale=spec["scale"], num_splits=spec["num_splits"])
+    torch.cuda.synchronize()
+    o_ref, lse_ref = cpu.decode_full(data["q"], data["k"], data["v"], spec["scale"])
+    assert_close(bf16_to_np(o), o_ref, f32_to_np(lse), lse_ref, "workload 4")
+
+
+def test_varlen_workload_sampled_rows(api, dev):
+    import torch
+    spec, data = si.make_config(5)
+    cu = data["cu_seqlens"]
+    maxlen = api.attn_varlen_check(cu, int(cu[-1]))
+    q, k, v = (to_dev(data[x], dev) for x in "qkv")
+    cu_d = torch.from_numpy(cu).to(dev)
+    o, lse = api.attn_fwd_varlen(q, k, v, cu_d, cu_d, maxlen, maxlen, scale=spec["scale"],
+                                 causal=True)
+    torch.cuda.synchronize()
+    o, lse = bf16_to_np(o), f32_to_np(lse)
+    rng = np.random.default_rng(5)
+    rows = []
+    for s in range(spec["nseq"]):
+        L = int(cu[s + 1] - cu[s])
+        for i in {0, L - 1, min(L - 1, 127), min(L - 1, 128), int(rng.integers(L)),
+                  int(rng.integers(L))}:
+            rows.append((s, int(rng.integers(spec["H"])), i))
+    rows = np.array(rows, dtype=np.int64)
+    o_ref, lse_ref = cpu.varlen_rows(data["q"], data["k"], data["v"], cu, cu, spec["scale"],
+                                     True, rows)
+    gi = cu[rows[:, 0]] + rows[:, 2]
+    assert_close(o[gi, rows[:, 1]], o_ref, lse[rows[:, 1], gi], lse_ref, "workload 5")
+    assert np.all(np.isfinite(o)) and np.all(np.isfinite(lse))
+
+
+# -------------------------------------------------------------------- decode
+
+DECODE = [  # B, Hq, Hkv, Skv, d, splits
+    (2, 8, 2, 1000, 128, 7),
+    (3, 4, 4, 1, 64, 1),
+    (3, 4, 4, 1, 64, 4),            # more chunks than keys: empty chunks
+    (1, 64, 1, 300, 128, 3),        # MQA group of 64 query heads (two column blocks)
+    (2, 32, 8, 4096, 128, 0),       # library picks the split count
+    (1, 40, 8, 513, 64, 2),
+    (4, 16, 2, 129, 128, 1),
+]
+
+
+@pytest.mark.parametrize("case", DECODE, ids=lambda c: "B%d_Hq%d_Hkv%d_Skv%d_d%d_s%d" % c)
+def test_decode_matches_oracle(api, dev, case):
+    import torch
+    B, Hq, Hkv, Skv, d, splits = case
+    data = si.make_decode(7 + Skv, B, Hq, Hkv, Skv, d)
+    scale = si.default_scale(d)
+    q, k, v = (to_dev(data[x], dev) for x in "qkv")
+    o, lse = api.attn_decode(q, k, v, scale=scale, num_splits=splits)
+    torch.cuda.synchronize()
+    o_ref, lse_ref = cpu.decode_full(data["q"], data["k"], data["v"], scale)
+    assert_close(bf16_to_np(o), o_ref, f32_to_np(lse), lse_ref, str(case))
+
+
+def test_decode_split_counts_agree(api, dev):
+    """1, 2, 8, 64 chunks and the library's choice agree closely (fp32 merge)."""
+    import torch
+    data = si.make_decode(11, 4, 16, 4, 2048, 128)
+    q, k, v = (to_dev(data[x], dev) for x in "qkv")
+    outs = []
+    for s in (1, 2, 8, 64, 0):
+        o, lse = api.attn_decode(q, k, v, num_splits=s)
+        torch.cuda.synchronize()
+        outs.append((bf16_to_np(o), f32_to_np(lse)))
+    for o, lse in outs[1:]:
+        assert np.abs(o - outs[0][0]).max() <= 2 ** -6
+        assert np.abs(lse - outs[0][1]).max() <= 2e-5
+
+
+def test_decode_equals_prefill_last_row(api, dev):
+    """Decode of the newest token == the last row of a causal prefill."""
+    import torch
+    B, Hq, Hkv, S, d = 2, 8, 2, 700, 128
+    data = si.make_prefill(12, B, Hq, Hkv, S, S, d)
+    q, k, v = (to_dev(data[x], dev) for x in "qkv")
+    o_p, l_p = api.attn_fwd(q, k, v, causal=True)
+    o_d, l_d = api.attn_decode(q[:, -1].contiguous(), k, v, num_splits=3)
+    torch.cuda.synchronize()
+    assert np.abs(bf16_to_np(o_d) - bf16_to_np(o_p[:, -1])).max() <= 2 ** -6
+    assert np.abs(f32_to_np(l_d) - f32_to_np(l_p[:, :, -1])).max() <= 1e-4
+
+
+# ------------------------------------------------- invariants and equivalences
+
+def test_constant_v_gives_the_constant(api, dev):
+    """V rows all equal to a bf16 vector c: every output row is c to one bf16 ulp.
+
+    The weights enter the second product rounded to bf16 while the row sum
+    adds them unrounded, so sum(P)/l differs from 1 by at most 2^-9.
+    """
+    import torch
+    B, S, H, d = 2, 300, 4, 128
+    data = si.make_prefill(13, B, H, H, S, S, d)
+    c = data["v"][0, 0, 0].copy()
+    data["v"][:] = c
+    for causal in (False, True):
+        o, _ = run_fwd(api, dev, data, si.default_scale(d), causal)
+        np.testing.assert_allclose(o, np.broadcast_to(si.bf16_to_f64(c), o.shape), rtol=2 ** -7,
+                                   atol=0)
+    q, k, v = (to_dev(data[x], dev) for x in "qkv")
+    od, _ = api.attn_decode(q[:, -1].contiguous(), k, v, num_splits=5)
+    torch.cuda.synchronize()
+    np.testing.assert_allclose(bf16_to_np(od), np.broadcast_to(si.bf16_to_f64(c), od.shape),
+                               rtol=2 ** -7, atol=0)
+
+
+def test_zero_query_gives_mean_and_log_count(api, dev):
+    B, S, H, d = 1, 260, 2, 64
+    data = si.make_prefill(14, B, H, H, S, S, d)
+    data["q"][:] = 0
+    o, lse = run_fwd(api, dev, data, 0.125, True)
+    v = si.bf16_to_f64(data["v"])
+    mean = np.cumsum(v, axis=1) / np.arange(1, S + 1)[None, :, None, None]
+    assert np.abs(o - mean).max() <= 2e-2
+    np.testing.assert_allclose(lse, np.broadcast_to(np.log(np.arange(1, S + 1)), lse.shape),
+                               atol=1e-4)
+
+
+def test_large_scores_do_not_overflow(api, dev):
+    """Scores of several hundred in scaled units: finite and equal to the oracle."""
+    B, S, H, d = 1, 256, 2, 128
+    data = si.make_prefill(15, B, H, H, S, S, d)
+    q = si.bf16_to_f32(data["q"]) * 8.0
+    data["q"] = si.f32_to_bf16_bits(q)
+    o, lse = run_fwd(api, dev, data, 1.0, True)
+    o_ref, lse_ref = cpu.attn_full(data["q"], data["k"], data["v"], 1.0, True)
+    assert lse_ref.max() > 300
+    assert_close(o, o_ref, lse, lse_ref, "large scores")
+
+
+def test_bitwise_deterministic(api, dev):
+    spec = si.CONFIGS[2]
+    data = si.make_prefill(16, 2, 8, 8, 1024, 1024, 128)
+    a = run_fwd(api, dev, data, 0.088, True)
+    for _ in range(3):
+        b = run_fwd(api, dev, data, 0.088, True)
+        assert np.array_equal(a[0], b[0]) and np.array_equal(a[1], b[1])
+
+
+def test_gqa_equals_repeated_mha_bitwise(api, dev):
+    B, S, Hq, Hkv, d = 2, 320, 8, 2, 128
+    data = si.make_prefill(17, B, Hq, Hkv, S, S, d)
+    rep = dict(q=data["q"], k=np.repeat(data["k"], 4, axis=2), v=np.repeat(data["v"], 4, axis=2))
+    for causal in (False, True):
+        a = run_fwd(api, dev, data, 0.09, causal)
+        b = run_fwd(api, dev, rep, 0.09, causal)
+        assert np.array_equal(a[0], b[0]) and np.array_equal(a[1], b[1])
+
+
+def test_varlen_equals_separate_calls_bitwise(api, dev):
+    import torch
+    lengths = [1, 130, 7, 300, 128]
+    data = si.make_varlen(18, len(lengths), 1, 300, H=4, d=128, Hkv=2, lengths=lengths)
+    cu = data["cu_seqlens"]
+    q, k, v = (to_dev(data[x], dev) for x in "qkv")
+    cu_d = torch.from_numpy(cu).to(dev)
+    for causal in (False, True):
+        o, lse = api.attn_fwd_varlen(q, k, v, cu_d, cu_d, max(lengths), max(lengths),
+                                     scale=0.09, causal=causal)
+        torch.cuda.synchronize()
+        o, lse = bf16_to_np(o), f32_to_np(lse)
+        for s, L in enumerate(lengths):
+            a, b = cu[s], cu[s + 1]
+            sub = {x: data[x][a:b][None] for x in "qkv"}
+            os_, ls_ = run_fwd(api, dev, sub, 0.09, causal)
+            assert np.array_equal(o[a:b], os_[0]) and np.array_equal(lse[:, a:b], ls_[0])
+
+
+def test_lse_optional(api, dev):
+    import torch
+    data = si.make_prefill(19, 1, 2, 2, 200, 200, 64)
+    q, k, v = (to_dev(data[x], dev) for x in "qkv")
+    o1, _ = api.attn_fwd(q, k, v, causal=True)
+    o2, l2 = api.attn_fwd(q, k, v, causal=True, want_lse=False)
+    torch.cuda.synchronize()
+    assert l2 is None and torch.equal(o1, o2)

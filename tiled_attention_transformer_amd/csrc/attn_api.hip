@@ -1,0 +1,215 @@
+// C ABI of libattn.so (declared in include/attn.h): argument validation on
+// the host, then the kernel launches.  No allocation, no global state.
+#include <math.h>
+#include <stdint.h>
+
+#include "../../include/attn.h"
+#include "kernels.h"
+
+namespace {
+
+constexpr int64_t kMaxElems = (int64_t)1 << 40;   // sanity cap on tensor sizes
+
+bool aligned(const void *p, uintptr_t a) { return ((uintptr_t)p & (a - 1)) == 0; }
+
+bool d_ok(int d) { return d == 64 || d == 128; }
+
+bool scale_ok(float s) { return isfinite(s) && s > 0.f; }
+
+attn_status_t from_hip(hipError_t e) { return e == hipSuccess ? ATTN_OK : ATTN_ERR_HIP; }
+
+int ceil_div(int a, int b) { return (a + b - 1) / b; }
+
+struct DecodeShape {
+    int nsplit, chunk, ncb;
+};
+
+int pick_splits(int B, int Hq, int Hkv, int Skv) {
+    // Enough workgroups to give every CU several (256 CUs), but chunks of at
+    // least 256 keys so each workgroup streams a useful amount of K/V.
+    const int ncb = ceil_div(Hq / Hkv, attn::kDecCols);
+    const int64_t base = (int64_t)B * Hkv * ncb;
+    int s = (int)((2048 + base - 1) / base);
+    const int max_by_len = ceil_div(Skv, 256);
+    if (s > max_by_len) s = max_by_len;
+    if (s < 1) s = 1;
+    return s;
+}
+
+DecodeShape decode_shape(int B, int Hq, int Hkv, int Skv, int num_splits) {
+    DecodeShape sh;
+    sh.nsplit = num_splits > 0 ? num_splits : pick_splits(B, Hq, Hkv, Skv);
+    sh.chunk = ceil_div(Skv, sh.nsplit);
+    sh.ncb = ceil_div(Hq / Hkv, attn::kDecCols);
+    return sh;
+}
+
+size_t decode_ws_bytes(int B, int Hq, int d, int nsplit) {
+    if (nsplit <= 1) return 0;
+    const size_t o_bytes = (size_t)nsplit * B * Hq * d * sizeof(float);
+    const size_t l_bytes = (size_t)nsplit * B * Hq * sizeof(float);
+    return o_bytes + l_bytes;
+}
+
+bool decode_sizes_ok(int B, int Hq, int Hkv, int Skv, int d) {
+    return B >= 1 && Hq >= 1 && Hkv >= 1 && Skv >= 1 && d >= 1 &&
+           (int64_t)B * Skv * Hkv * d <= kMaxElems && (int64_t)B * Hq * d <= kMaxElems;
+}
+
+}  // namespace
+
+extern "C" {
+
+const char *attn_status_string(attn_status_t s) {
+    switch (s) {
+        case ATTN_OK: return "ok";
+        case ATTN_ERR_NULLPTR: return "a required pointer is NULL";
+        case ATTN_ERR_SHAPE: return "a size is < 1 or too large";
+        case ATTN_ERR_UNSUPPORTED_D: return "head dimension must be 64 or 128";
+        case ATTN_ERR_GQA_RATIO: return "Hq must be a multiple of Hkv";
+        case ATTN_ERR_ALIGNMENT: return "pointer not aligned (bf16 tensors 16 B, lse 4 B, workspace 16 B)";
+        case ATTN_ERR_WORKSPACE: return "decode workspace missing or too small";
+        case ATTN_ERR_SEQLENS: return "malformed cumulative sequence offsets";
+        case ATTN_ERR_HIP: return "HIP runtime error at launch";
+        case ATTN_ERR_SCALE: return "scale must be finite and > 0";
+    }
+    return "unknown status";
+}
+
+attn_status_t attn_fwd(const void *q, const void *k, const void *v, void *o, float *lse, int B,
+                       int Hq, int Hkv, int Sq, int Skv, int d, float scale, int causal,
+                       hipStream_t stream) {
+    if (!q || !k || !v || !o) return ATTN_ERR_NULLPTR;
+    if (B < 1 || Hq < 1 || Hkv < 1 || Sq < 1 || Skv < 1 || d < 1) return ATTN_ERR_SHAPE;
+    if ((int64_t)B * Sq * Hq * d > kMaxElems || (int64_t)B * Skv * Hkv * d > kMaxElems)
+        return ATTN_ERR_SHAPE;
+    if (!d_ok(d)) return ATTN_ERR_UNSUPPORTED_D;
+    if (Hq % Hkv) return ATTN_ERR_GQA_RATIO;
+    if (!scale_ok(scale)) return ATTN_ERR_SCALE;
+    if (!aligned(q, 16) || !aligned(k, 16) || !aligned(v, 16) || !aligned(o, 16) ||
+        (lse && !aligned(lse, 4)))
+        return ATTN_ERR_ALIGNMENT;
+    const int ntiles = ceil_div(Sq, attn::kFwdBr);
+    if ((int64_t)ntiles * B * Hq > 0x7fffffff) return ATTN_ERR_SHAPE;
+    attn::FwdParams p{};
+    p.q = (const __bf16 *)q;
+    p.k = (const __bf16 *)k;
+    p.v = (const __bf16 *)v;
+    p.o = (__bf16 *)o;
+    p.lse = lse;
+    p.nbatch = B;
+    p.Hq = Hq;
+    p.Hkv = Hkv;
+    p.group = Hq / Hkv;
+    p.Sq = Sq;
+    p.Skv = Skv;
+    p.ntiles = ntiles;
+    p.c = scale * attn::kLog2e;
+    return from_hip(attn::launch_fwd(p, d, causal != 0, false, stream));
+}
+
+attn_status_t attn_varlen_check(const int *cu, int nseq, int total, int *max_seqlen) {
+    if (!cu) return ATTN_ERR_NULLPTR;
+    if (nseq < 1 || total < 0 || cu[0] != 0 || cu[nseq] != total) return ATTN_ERR_SEQLENS;
+    int mx = 0;
+    for (int s = 0; s < nseq; ++s) {
+        if (cu[s + 1] < cu[s]) return ATTN_ERR_SEQLENS;
+        if (cu[s + 1] - cu[s] > mx) mx = cu[s + 1] - cu[s];
+    }
+    if (max_seqlen) *max_seqlen = mx;
+    return ATTN_OK;
+}
+
+attn_status_t attn_fwd_varlen(const void *q, const void *k, const void *v, void *o, float *lse,
+                              const int *cu_seqlens_q, const int *cu_seqlens_k, int nseq,
+                              int total_q, int total_k, int max_seqlen_q, int max_seqlen_k,
+                              int Hq, int Hkv, int d, float scale, int causal,
+                              hipStream_t stream) {
+    if (!q || !k || !v || !o || !cu_seqlens_q || !cu_seqlens_k) return ATTN_ERR_NULLPTR;
+    if (nseq < 1 || total_q < 1 || total_k < 1 || max_seqlen_q < 1 || max_seqlen_k < 1 ||
+        Hq < 1 || Hkv < 1 || d < 1)
+        return ATTN_ERR_SHAPE;
+    if (max_seqlen_q > total_q || max_seqlen_k > total_k) return ATTN_ERR_SEQLENS;
+    if ((int64_t)total_q * Hq * d > kMaxElems || (int64_t)total_k * Hkv * d > kMaxElems)
+        return ATTN_ERR_SHAPE;
+    if (!d_ok(d)) return ATTN_ERR_UNSUPPORTED_D;
+    if (Hq % Hkv) return ATTN_ERR_GQA_RATIO;
+    if (!scale_ok(scale)) return ATTN_ERR_SCALE;
+    if (!aligned(q, 16) || !aligned(k, 16) || !aligned(v, 16) || !aligned(o, 16) ||
+        (lse && !aligned(lse, 4)) || !aligned(cu_seqlens_q, 4) || !aligned(cu_seqlens_k, 4))
+        return ATTN_ERR_ALIGNMENT;
+    const int ntiles = ceil_div(max_seqlen_q, attn::kFwdBr);
+    if ((int64_t)ntiles * nseq * Hq > 0x7fffffff) return ATTN_ERR_SHAPE;
+    attn::FwdParams p{};
+    p.q = (const __bf16 *)q;
+    p.k = (const __bf16 *)k;
+    p.v = (const __bf16 *)v;
+    p.o = (__bf16 *)o;
+    p.lse = lse;
+    p.cu_q = cu_seqlens_q;
+    p.cu_k = cu_seqlens_k;
+    p.nbatch = nseq;
+    p.Hq = Hq;
+    p.Hkv = Hkv;
+    p.group = Hq / Hkv;
+    p.total_q = total_q;
+    p.total_k = total_k;
+    p.ntiles = ntiles;
+    p.c = scale * attn::kLog2e;
+    return from_hip(attn::launch_fwd(p, d, causal != 0, true, stream));
+}
+
+int attn_decode_pick_splits(int B, int Hq, int Hkv, int Skv) {
+    if (!decode_sizes_ok(B, Hq, Hkv, Skv, 64) || Hq % Hkv) return 0;
+    return pick_splits(B, Hq, Hkv, Skv);
+}
+
+size_t attn_decode_workspace_bytes(int B, int Hq, int Hkv, int Skv, int d, int num_splits) {
+    if (!decode_sizes_ok(B, Hq, Hkv, Skv, d) || Hq % Hkv || !d_ok(d)) return 0;
+    const DecodeShape sh = decode_shape(B, Hq, Hkv, Skv, num_splits);
+    return decode_ws_bytes(B, Hq, d, sh.nsplit);
+}
+
+attn_status_t attn_decode(const void *q, const void *k_cache, const void *v_cache, void *o,
+                          float *lse, int B, int Hq, int Hkv, int Skv, int d, float scale,
+                          int num_splits, void *workspace, size_t workspace_bytes,
+                          hipStream_t stream) {
+    if (!q || !k_cache || !v_cache || !o) return ATTN_ERR_NULLPTR;
+    if (!decode_sizes_ok(B, Hq, Hkv, Skv, d)) return ATTN_ERR_SHAPE;
+    if (!d_ok(d)) return ATTN_ERR_UNSUPPORTED_D;
+    if (Hq % Hkv) return ATTN_ERR_GQA_RATIO;
+    if (!scale_ok(scale)) return ATTN_ERR_SCALE;
+    if (num_splits > 65536) return ATTN_ERR_SHAPE;
+    if (!aligned(q, 16) || !aligned(k_cache, 16) || !aligned(v_cache, 16) || !aligned(o, 16) ||
+        (lse && !aligned(lse, 4)))
+        return ATTN_ERR_ALIGNMENT;
+    const DecodeShape sh = decode_shape(B, Hq, Hkv, Skv, num_splits);
+    const size_t need = decode_ws_bytes(B, Hq, d, sh.nsplit);
+    if (need > 0) {
+        if (!workspace || workspace_bytes < need) return ATTN_ERR_WORKSPACE;
+        if (!aligned(workspace, 16)) return ATTN_ERR_ALIGNMENT;
+    }
+    if ((int64_t)B * Hkv * sh.ncb * sh.nsplit > 0x7fffffff) return ATTN_ERR_SHAPE;
+    attn::DecParams p{};
+    p.q = (const __bf16 *)q;
+    p.k = (const __bf16 *)k_cache;
+    p.v = (const __bf16 *)v_cache;
+    p.o = (__bf16 *)o;
+    p.lse = lse;
+    if (need > 0) {
+        p.ws_o = (float *)workspace;
+        p.ws_lse = p.ws_o + (size_t)sh.nsplit * B * Hq * d;
+    }
+    p.B = B;
+    p.Hq = Hq;
+    p.Hkv = Hkv;
+    p.group = Hq / Hkv;
+    p.Skv = Skv;
+    p.ncb = sh.ncb;
+    p.nsplit = sh.nsplit;
+    p.chunk = sh.chunk;
+    p.c = scale * attn::kLog2e;
+    return from_hip(attn::launch_decode(p, d, stream));
+}
+
+}  // extern "C"

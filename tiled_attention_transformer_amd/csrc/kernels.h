@@ -1,0 +1,52 @@
+// Launch parameters and launchers of the gfx950 attention kernels.  Internal
+// to libattn.so: the exported C ABI (include/attn.h) validates arguments and
+// then calls these.
+#pragma once
+
+#include <hip/hip_runtime.h>
+#include <stdint.h>
+
+namespace attn {
+
+constexpr float kLn2 = 0.69314718055994530942f;
+constexpr float kLog2e = 1.44269504088896340736f;
+
+// Prefill tile shape: 4 waves x 32 query rows, 64 keys per K/V tile.
+constexpr int kFwdThreads = 256;
+constexpr int kFwdBr = 128;
+constexpr int kFwdBc = 64;
+
+// Decode tile shape: 4 waves, each takes 32 of the 128 keys of a tile; one
+// workgroup serves up to 32 query heads of one KV head.
+constexpr int kDecThreads = 256;
+constexpr int kDecBc = 128;
+constexpr int kDecCols = 32;
+
+struct FwdParams {
+    const __bf16 *q, *k, *v;
+    __bf16 *o;
+    float *lse;              // may be null
+    const int *cu_q, *cu_k;  // varlen only (device)
+    int nbatch;              // B, or nseq for varlen
+    int Hq, Hkv, group;      // group = Hq / Hkv
+    int Sq, Skv;             // fixed batch only
+    int total_q, total_k;    // varlen only
+    int ntiles;              // query tiles per (batch, head) in the grid
+    float c;                 // scale * log2(e)
+};
+
+struct DecParams {
+    const __bf16 *q, *k, *v;
+    __bf16 *o;
+    float *lse;              // may be null
+    float *ws_o, *ws_lse;    // split partials (null when nsplit == 1)
+    int B, Hq, Hkv, group, Skv;
+    int ncb;                 // blocks of <= 32 query heads per KV head
+    int nsplit, chunk;       // key chunks and keys per chunk
+    float c;                 // scale * log2(e)
+};
+
+hipError_t launch_fwd(const FwdParams &p, int d, bool causal, bool varlen, hipStream_t s);
+hipError_t launch_decode(const DecParams &p, int d, hipStream_t s);
+
+}  // namespace attn
