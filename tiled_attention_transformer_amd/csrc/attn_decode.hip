@@ -43,8 +43,10 @@ struct DecLds {
     static constexpr int V_ELEMS = BC * VP;
     static constexpr int ELEMS = K_ELEMS + V_ELEMS;
     static constexpr int CHUNKS = BC * D / 8 / NT;
-    // merge area (reuses the tile area): per wave m[32], l[32], O[32][D] fp32
-    static constexpr int MERGE_FLOATS = 4 * (2 * NCOL + NCOL * D);
+    // merge area (reuses the tile area): per wave m[32], l[32], O[32][D+1]
+    // fp32; the odd column pitch keeps the 32 lanes of a write on 32 banks
+    static constexpr int OP = D + 1;
+    static constexpr int MERGE_FLOATS = 4 * (2 * NCOL + NCOL * OP);
     static_assert(MERGE_FLOATS * 4 <= ELEMS * 2, "merge area must fit in the tile area");
 };
 
@@ -199,14 +201,15 @@ void attn_decode_split_kernel(DecParams p) {
 #pragma unroll
         for (int r = 0; r < 16; ++r) {
             const int dcol = 32 * db + 8 * (r >> 2) + 4 * g + (r & 3);
-            ow[(wave * NCOL + col) * D + dcol] = oacc[db][r];
+            ow[(wave * NCOL + col) * L::OP + dcol] = oacc[db][r];
         }
     __syncthreads();
 
-    // 32 columns x D values over 256 threads.
+    // 32 columns x D values over 256 threads: thread t takes column t % 32
+    // and PER consecutive values (lanes of a wave walk the columns).
     constexpr int PER = NCOL * D / NT;
-    const int mc = tid / (D / PER);                 // column
-    const int d0 = (tid % (D / PER)) * PER;
+    const int mc = tid % NCOL;                      // column
+    const int d0 = (tid / NCOL) * PER;
     if (mc >= ncols) return;
     float M = -__builtin_inff();
 #pragma unroll
@@ -231,7 +234,7 @@ void attn_decode_split_kernel(DecParams p) {
             for (int u = 0; u < 4; ++u) {
                 float acc = 0.f;
 #pragma unroll
-                for (int w = 0; w < 4; ++w) acc += wgt[w] * ow[(w * NCOL + mc) * D + d0 + e + u];
+                for (int w = 0; w < 4; ++w) acc += wgt[w] * ow[(w * NCOL + mc) * L::OP + d0 + e + u];
                 v4[u] = acc * inv;
             }
             *reinterpret_cast<bf16x4 *>(op + e) = to_bf16x4(v4[0], v4[1], v4[2], v4[3]);
@@ -243,7 +246,7 @@ void attn_decode_split_kernel(DecParams p) {
         for (int e = 0; e < PER; ++e) {
             float acc = 0.f;
 #pragma unroll
-            for (int w = 0; w < 4; ++w) acc += wgt[w] * ow[(w * NCOL + mc) * D + d0 + e];
+            for (int w = 0; w < 4; ++w) acc += wgt[w] * ow[(w * NCOL + mc) * L::OP + d0 + e];
             op[e] = acc * inv;
         }
         if (d0 == 0) p.ws_lse[((int64_t)sp * p.B + b) * p.Hq + h] = lse_nat;

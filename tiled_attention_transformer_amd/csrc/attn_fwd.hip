@@ -118,24 +118,36 @@ void attn_fwd_kernel(FwdParams p) {
         }
     }
 
-    // Global -> register staging of one K/V tile.
+    // Global -> register staging of one K/V tile.  Thread tid moves the
+    // 16-byte chunks tid + 256*i of the tile (row = key, 16 chunks per row for
+    // d = 128), so each wave instruction reads whole 256-byte key rows.
     const __bf16 *kbase = p.k + krow0 * hd_k + (int64_t)hk * D;
     const __bf16 *vbase = p.v + krow0 * hd_k + (int64_t)hk * D;
+    const int64_t tile_step = (int64_t)BC * hd_k;
+    int64_t goff[L::CHUNKS];     // element offset of chunk i within a tile
+    int lrow[L::CHUNKS];         // key row of chunk i within a tile
+#pragma unroll
+    for (int i = 0; i < L::CHUNKS; ++i) {
+        const int cidx = tid + NT * i;
+        lrow[i] = cidx / (D / 8);
+        goff[i] = (int64_t)lrow[i] * hd_k + (cidx % (D / 8)) * 8;
+    }
     u32x4 kreg[L::CHUNKS], vreg[L::CHUNKS];
     auto load_tile = [&](int j) {
-        const int key0 = j * BC;
+        const __bf16 *kt = kbase + j * tile_step;
+        const __bf16 *vt = vbase + j * tile_step;
+        if ((j + 1) * BC <= Skv) {                 // whole tile in range (uniform)
 #pragma unroll
-        for (int i = 0; i < L::CHUNKS; ++i) {
-            const int c = tid + NT * i;
-            const int row = c / (D / 8);
-            const int cc = (c % (D / 8)) * 8;
-            const int key = key0 + row;
-            if (key < Skv) {
-                kreg[i] = ld_global16(kbase + (int64_t)key * hd_k + cc);
-                vreg[i] = ld_global16(vbase + (int64_t)key * hd_k + cc);
-            } else {
-                kreg[i] = u32x4{0, 0, 0, 0};
-                vreg[i] = u32x4{0, 0, 0, 0};
+            for (int i = 0; i < L::CHUNKS; ++i) {
+                kreg[i] = ld_global16(kt + goff[i]);
+                vreg[i] = ld_global16(vt + goff[i]);
+            }
+        } else {
+#pragma unroll
+            for (int i = 0; i < L::CHUNKS; ++i) {
+                const bool in = j * BC + lrow[i] < Skv;
+                kreg[i] = in ? ld_global16(kt + goff[i]) : u32x4{0, 0, 0, 0};
+                vreg[i] = in ? ld_global16(vt + goff[i]) : u32x4{0, 0, 0, 0};
             }
         }
     };
@@ -144,11 +156,10 @@ void attn_fwd_kernel(FwdParams p) {
         __bf16 *vs = ks + L::K_ELEMS;
 #pragma unroll
         for (int i = 0; i < L::CHUNKS; ++i) {
-            const int c = tid + NT * i;
-            const int row = c / (D / 8);
-            const int cc = (c % (D / 8)) * 8;
-            st_lds16(ks + row * L::KP + cc, kreg[i]);
-            st_lds16(vs + row * L::VP + cc, vreg[i]);
+            const int cidx = tid + NT * i;
+            const int cc = (cidx % (D / 8)) * 8;
+            st_lds16(ks + lrow[i] * L::KP + cc, kreg[i]);
+            st_lds16(vs + lrow[i] * L::VP + cc, vreg[i]);
         }
     };
 
@@ -177,62 +188,83 @@ void attn_fwd_kernel(FwdParams p) {
         if (wave_live) {
             const __bf16 *ks = lds + st * L::STAGE;
             const __bf16 *vs = ks + L::K_ELEMS;
+            // S^T = K Q^T for the BC/32 key blocks; the independent chains are
+            // interleaved and each K fragment is read from LDS one step ahead.
             f32x16 s[BC / 32];
+            {
+                bf16x8 kf[2][BC / 32];
 #pragma unroll
-            for (int kb = 0; kb < BC / 32; ++kb) {
-                s[kb] = f32x16{};
-                const __bf16 *kr = ks + (32 * kb + col) * L::KP + 8 * g;
+                for (int kb = 0; kb < BC / 32; ++kb) {
+                    s[kb] = f32x16{};
+                    kf[0][kb] = ld_lds_bf16x8(ks + (32 * kb + col) * L::KP + 8 * g);
+                }
 #pragma unroll
-                for (int t = 0; t < D / 16; ++t)
-                    s[kb] = mfma32x32x16(ld_lds_bf16x8(kr + 16 * t), qf[t], s[kb]);
+                for (int t = 0; t < D / 16; ++t) {
+                    if (t + 1 < D / 16) {
+#pragma unroll
+                        for (int kb = 0; kb < BC / 32; ++kb)
+                            kf[(t + 1) & 1][kb] =
+                                ld_lds_bf16x8(ks + (32 * kb + col) * L::KP + 8 * g + 16 * (t + 1));
+                    }
+#pragma unroll
+                    for (int kb = 0; kb < BC / 32; ++kb)
+                        s[kb] = mfma32x32x16(kf[t & 1][kb], qf[t], s[kb]);
+                }
             }
+            // Mask keys past the row's causal limit or past the sequence end
+            // (only tiles that cross the diagonal or the end need it).
             const bool need_mask = key0 + BC > Skv || (CAUSAL && key0 + BC - 1 > wrow0 + off);
             if (need_mask) {
+                int lim = Skv - 1;
+                if (CAUSAL) lim = min(lim, qr + off);
+                lim -= key0 + 4 * g;                  // this lane's keys: key0 + 4g + const
 #pragma unroll
                 for (int kb = 0; kb < BC / 32; ++kb)
 #pragma unroll
-                    for (int r = 0; r < 16; ++r) {
-                        const int key = key0 + 32 * kb + 8 * (r >> 2) + 4 * g + (r & 3);
-                        if (key >= Skv || (CAUSAL && key > qr + off)) s[kb][r] = -__builtin_inff();
-                    }
+                    for (int r = 0; r < 16; ++r)
+                        if (32 * kb + 8 * (r >> 2) + (r & 3) > lim) s[kb][r] = -__builtin_inff();
             }
             float mx = -__builtin_inff();
 #pragma unroll
             for (int kb = 0; kb < BC / 32; ++kb)
 #pragma unroll
                 for (int r = 0; r < 16; ++r) mx = fmaxf(mx, s[kb][r]);
-            mx = half_swap_max(mx);
-            const float m_new = fmaxf(m, mx * c);
-            const float m_use = m_new == -__builtin_inff() ? 0.f : m_new;
-            const float alpha = fast_exp2(m - m_use);
+            const float mt = half_swap_max(mx) * c;   // tile row max, scaled log2 units
+            // Lazy rescaling: the reference max m only moves when a row's tile
+            // max exceeds it by more than kRescaleSlack, so exp2(s*c - m) stays
+            // <= 2^kRescaleSlack and most tiles skip the O rescale entirely.
+            const bool raise = mt > m + kRescaleSlack;
+            if (__builtin_amdgcn_ballot_w64(raise)) {
+                const float m_new = raise ? mt : m;
+                const float alpha = m_new == -__builtin_inff() ? 1.f : fast_exp2(m - m_new);
+                lsum *= alpha;
+#pragma unroll
+                for (int db = 0; db < D / 32; ++db)
+#pragma unroll
+                    for (int r = 0; r < 16; ++r) oacc[db][r] *= alpha;
+                m = m_new;
+            }
+            const float m_use = m == -__builtin_inff() ? 0.f : m;
             // P = exp2(s*c - m); the row sum adds the fp32 values (the LSE
             // needs them unrounded) and P enters the second product as bf16.
             bf16x8 pk[BC / 16];
-            float rs = 0.f;
 #pragma unroll
             for (int kb = 0; kb < BC / 32; ++kb)
 #pragma unroll
                 for (int r = 0; r < 16; ++r) {
                     s[kb][r] = fast_exp2(__builtin_fmaf(s[kb][r], c, -m_use));
-                    rs += s[kb][r];
+                    lsum += s[kb][r];
                 }
 #pragma unroll
             for (int kk = 0; kk < BC / 16; ++kk) pk[kk] = pack_p8(s[kk >> 1], 8 * (kk & 1));
-            lsum = lsum * alpha + rs;
-            m = m_new;
-#pragma unroll
-            for (int db = 0; db < D / 32; ++db)
-#pragma unroll
-                for (int r = 0; r < 16; ++r) oacc[db][r] *= alpha;
 #pragma unroll
             for (int kk = 0; kk < BC / 16; ++kk) {
-                const bf16x8 pb = pk[kk];
                 const __bf16 *v0 = vs + (16 * kk + 4 * g + tr_e) * L::VP + 16 * tr_dh + 4 * tr_s;
 #pragma unroll
                 for (int db = 0; db < D / 32; ++db) {
                     const s16x4 lo = lds_read_tr(v0 + 32 * db);
                     const s16x4 hi = lds_read_tr(v0 + 8 * L::VP + 32 * db);
-                    oacc[db] = mfma32x32x16(concat_tr(lo, hi), pb, oacc[db]);
+                    oacc[db] = mfma32x32x16(concat_tr(lo, hi), pk[kk], oacc[db]);
                 }
             }
         }

@@ -11,6 +11,10 @@ namespace attn {
 constexpr float kLn2 = 0.69314718055994530942f;
 constexpr float kLog2e = 1.44269504088896340736f;
 
+// Slack (log2 units) before the online softmax moves its reference max:
+// weights exp2(s*c - m) stay <= 2^8, far from fp32/bf16 overflow.
+constexpr float kRescaleSlack = 8.0f;
+
 // Prefill tile shape: 4 waves x 32 query rows, 64 keys per K/V tile.
 constexpr int kFwdThreads = 256;
 constexpr int kFwdBr = 128;

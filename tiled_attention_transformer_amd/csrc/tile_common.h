@@ -81,6 +81,21 @@ __device__ __forceinline__ bf16x8 concat_tr(s16x4 lo, s16x4 hi) {
     return __builtin_bit_cast(bf16x8, v);
 }
 
+// Direct HBM -> LDS load of 16 bytes per lane (global_load_lds_dwordx4):
+// lane L's 16 bytes from `src` land at lds_base + 16*L.  lds_base must be
+// the same in every lane of the wave (it goes to M0).
+__device__ __forceinline__ void lds_dma16(const void *src, void *lds_base) {
+    __builtin_amdgcn_global_load_lds((const __attribute__((address_space(1))) void *)src,
+                                     (__attribute__((address_space(3))) void *)lds_base, 16, 0, 0);
+}
+
+// s_waitcnt on the vector-memory counter only (at most n loads outstanding).
+template <int N>
+__device__ __forceinline__ void wait_vmcnt() {
+    static_assert(N >= 0 && N < 64, "vmcnt range");
+    __builtin_amdgcn_s_waitcnt((N & 15) | ((N >> 4) << 14) | (7 << 4) | (15 << 8));
+}
+
 __device__ __forceinline__ u32x4 ld_global16(const void *p) {
     return *reinterpret_cast<const u32x4 *>(p);
 }
