@@ -15,9 +15,10 @@ constexpr float kLog2e = 1.44269504088896340736f;
 // weights exp2(s*c - m) stay <= 2^8, far from fp32/bf16 overflow.
 constexpr float kRescaleSlack = 8.0f;
 
-// Prefill tile shape: 4 waves x 32 query rows, 64 keys per K/V tile.
-constexpr int kFwdThreads = 256;
-constexpr int kFwdBr = 128;
+// Prefill tile shape: 8 waves x 32 query rows, 64 keys per K/V tile.
+constexpr int kFwdWaves = 8;
+constexpr int kFwdThreads = 64 * kFwdWaves;
+constexpr int kFwdBr = 32 * kFwdWaves;
 constexpr int kFwdBc = 64;
 
 // Decode tile shape: 4 waves, each takes 32 of the 128 keys of a tile; one

@@ -89,11 +89,36 @@ __device__ __forceinline__ void lds_dma16(const void *src, void *lds_base) {
                                      (__attribute__((address_space(3))) void *)lds_base, 16, 0, 0);
 }
 
+// Raw buffer descriptor over [base, base + nbytes): loads past nbytes return
+// zeros (checked per dword), which bounds a tile at the sequence end without
+// any per-lane clamping.  0x00020000 is the gfx9-family buffer format word.
+__device__ __forceinline__ __amdgpu_buffer_rsrc_t buffer_rsrc(const void *base, int nbytes) {
+    return __builtin_amdgcn_make_buffer_rsrc(const_cast<void *>(base), 0, nbytes, 0x00020000);
+}
+
+// Buffer load of 16 bytes per lane straight into LDS (buffer_load_dwordx4 ...
+// lds): lane L's bytes from byte offset voff land at lds_base + 16*L.
+__device__ __forceinline__ void buffer_lds_dma16(__amdgpu_buffer_rsrc_t r, uint32_t voff,
+                                                 void *lds_base) {
+    __builtin_amdgcn_raw_ptr_buffer_load_lds(r, (__attribute__((address_space(3))) void *)lds_base,
+                                             16, voff, 0, 0, 0);
+}
+
 // s_waitcnt on the vector-memory counter only (at most n loads outstanding).
 template <int N>
 __device__ __forceinline__ void wait_vmcnt() {
     static_assert(N >= 0 && N < 64, "vmcnt range");
     __builtin_amdgcn_s_waitcnt((N & 15) | ((N >> 4) << 14) | (7 << 4) | (15 << 8));
+}
+
+// Workgroup barrier for LDS hand-off.  The waits it needs are issued
+// explicitly by the caller (wait_vmcnt for direct loads; reads are consumed
+// before the barrier); the signal fences only stop the compiler from moving
+// memory accesses across it.
+__device__ __forceinline__ void lds_barrier() {
+    __atomic_signal_fence(__ATOMIC_SEQ_CST);
+    __builtin_amdgcn_s_barrier();
+    __atomic_signal_fence(__ATOMIC_SEQ_CST);
 }
 
 __device__ __forceinline__ u32x4 ld_global16(const void *p) {
