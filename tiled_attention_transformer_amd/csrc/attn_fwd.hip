@@ -57,7 +57,7 @@ constexpr int NW = kFwdWaves;
 constexpr int NT = kFwdThreads;
 constexpr int BR = kFwdBr;
 constexpr int BC = kFwdBc;
-constexpr int NS = 3;                 // LDS ring stages
+constexpr int NS = 4;                 // LDS ring stages
 
 template <int D>
 struct FwdLay {
@@ -314,9 +314,18 @@ void attn_fwd_kernel(FwdParams p) {
     // tile j+2, then S_{j+1} on the matrix cores interleaved with the softmax
     // of S_j, then O += P_j V_j.  scur holds S_j, snext receives S_{j+1}.
     auto step = [&](int j, f32x16 (&scur)[BC / 32], f32x16 (&snext)[BC / 32]) {
-        wait_vmcnt<0>();
+        // tile j+1 complete (tile j+2 may still be in flight)
+        if (j + 2 < nt) wait_vmcnt<L::PER_WAVE>();
+        else wait_vmcnt<0>();
         lds_barrier();
-        if (j + 2 < nt) issue(j + 2);
+        if (j + 3 < nt) issue(j + 3);
+        if (j >= ntw) {
+            // no tile for this wave: snext gets a placeholder, so that no score
+            // buffer has to stay live across steps
+#pragma unroll
+            for (int kb = 0; kb < BC / 32; ++kb)
+                snext[kb] = __builtin_nondeterministic_value(snext[kb]);
+        }
         if (j < ntw) {
             mask(j, scur);
             row_max(scur);
@@ -325,10 +334,12 @@ void attn_fwd_kernel(FwdParams p) {
             // the matrix cores compute the next tile's scores (on a wave's
             // last tile those scores are not used; the stage read is always in
             // bounds), then the second product.
+            __builtin_amdgcn_s_setprio(1);
             weights(scur, pk);
             scores(j + 1, snext);
             __builtin_amdgcn_sched_barrier(0);   // keep the V reads out of the fused region
             pv(j, pk);
+            __builtin_amdgcn_s_setprio(0);
         }
     };
 
@@ -337,16 +348,19 @@ void attn_fwd_kernel(FwdParams p) {
     if (nt > 0) {
         issue(0);
         if (nt > 1) issue(1);
-        // tile 0 complete (tile 1 may still be in flight), visible to all waves
-        if (nt > 1) wait_vmcnt<L::PER_WAVE>();
+        if (nt > 2) issue(2);
+        // tile 0 complete (tiles 1, 2 may still be in flight), visible to all waves
+        if (nt > 2) wait_vmcnt<2 * L::PER_WAVE>();
+        else if (nt > 1) wait_vmcnt<L::PER_WAVE>();
         else wait_vmcnt<0>();
         lds_barrier();
         if (ntw > 0) scores(0, sa);
     }
-    // unrolled by two so the score buffers alternate without copies
+    // unrolled by two so the score buffers alternate without copies; the
+    // second step always runs (past the end it only waits at the barrier)
     for (int j = 0; j < nt; j += 2) {
         step(j, sa, sb);
-        if (j + 1 < nt) step(j + 1, sb, sa);
+        step(j + 1, sb, sa);
     }
 
     // Epilogue: O = acc / l (bf16), LSE = (m + log2 l) * ln 2.
