@@ -61,18 +61,70 @@ def decode_bytes(B, Hq, Hkv, Skv, d):
     return kv + B * Hq * d * 2 + B * Hq * d * 2 + B * Hq * 4
 
 
+TRAFFIC_PATH = os.path.join(ROOT, "profiles", "traffic.json")
+# which kernels make up each reported path (substrings of the rocprofv3 names)
+TRAFFIC_KERNELS = {"prefill": ["attn_fwd_kernel<128, true, false>"],
+                   "decode": ["attn_decode_split_kernel<128>", "attn_decode_combine_kernel<128>"]}
+
+
 def load_traffic(kind: str):
     """HBM bytes per launch measured with rocprofv3 counters, if taken on this kernel."""
-    path = os.path.join(ROOT, "profiles", "traffic.json")
-    if not os.path.exists(path):
+    if not os.path.exists(TRAFFIC_PATH):
         return None
     try:
-        t = json.load(open(path))
+        t = json.load(open(TRAFFIC_PATH))
     except (OSError, ValueError):
         return None
     if t.get("kernel_hash") != kernel_hash() or kind not in t:
         return None
-    return t[kind]
+    return t[kind]["bytes"]
+
+
+def write_traffic(fetch_dir: str, write_dir: str):
+    """Turn two ``rocprofv3 --pmc`` runs of ``bench.py --copy-calibration``
+    (FETCH_SIZE, then WRITE_SIZE, KiB per dispatch) into bytes per launch.
+
+    Each counter is scaled by what it reads for the plain 1 GiB device copy
+    in the same run, so that the copy counts as 1 GiB read and 1 GiB written.
+    """
+    import csv
+    import glob
+
+    def per_kernel(d, counter):
+        (path,) = glob.glob(os.path.join(d, "**", "*counter_collection.csv"), recursive=True)
+        acc = {}
+        for r in csv.DictReader(open(path)):
+            if r["Counter_Name"] != counter:
+                continue
+            acc.setdefault(r["Kernel_Name"], []).append(float(r["Counter_Value"]))
+        return {k: sum(v) / len(v) for k, v in acc.items()}
+
+    fetch, write = per_kernel(fetch_dir, "FETCH_SIZE"), per_kernel(write_dir, "WRITE_SIZE")
+    copy_kib = float(1 << 20)
+
+    def copy_value(d):
+        vals = [v for k, v in d.items() if "copyBuffer" in k or "copy" in k.lower()]
+        if len(vals) != 1:
+            sys.exit("expected exactly one copy kernel in the counter run")
+        return vals[0]
+
+    f_scale, w_scale = copy_kib / copy_value(fetch), copy_kib / copy_value(write)
+    out = {"kernel_hash": kernel_hash(),
+           "calibration": {"fetch_scale": round(f_scale, 4), "write_scale": round(w_scale, 4),
+                           "copy_bytes": 1 << 30}}
+    for kind, names in TRAFFIC_KERNELS.items():
+        rd = wr = 0.0
+        for n in names:
+            (kf,) = [k for k in fetch if n in k]
+            (kw,) = [k for k in write if n in k]
+            rd += fetch[kf] * f_scale * 1024
+            wr += write[kw] * w_scale * 1024
+        out[kind] = {"bytes": int(round(rd + wr)), "read_bytes": int(round(rd)),
+                     "write_bytes": int(round(wr)), "kernels": names}
+    with open(TRAFFIC_PATH, "w") as fh:
+        json.dump(out, fh, indent=1)
+        fh.write("\n")
+    print(json.dumps(out))
 
 
 def cpu_baseline(spec, data, max_pairs):
@@ -105,7 +157,13 @@ def main():
                     help="allowed query/key pairs in the CPU-baseline sample")
     ap.add_argument("--copy-calibration", action="store_true",
                     help="also run a plain 1 GiB device copy (counter calibration)")
+    ap.add_argument("--write-traffic", nargs=2, metavar=("FETCH_DIR", "WRITE_DIR"),
+                    help="write profiles/traffic.json from two rocprofv3 --pmc output folders "
+                         "and exit (no GPU use)")
     args = ap.parse_args()
+    if args.write_traffic:
+        write_traffic(*args.write_traffic)
+        return
     if args.gpus != 1:
         print("bench.py runs on one GPU only; --gpus %d is not supported by this build"
               % args.gpus, file=sys.stderr)
