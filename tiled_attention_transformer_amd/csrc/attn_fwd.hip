@@ -18,16 +18,16 @@
 //  * one workgroup = 8 waves = 256 query rows of one (batch, head), one
 //    workgroup per CU (two waves per SIMD); each wave owns 32 rows and keeps
 //    its Q fragment, running max/sum and fp32 output accumulator in registers;
-//  * K and V tiles of 64 keys move HBM -> LDS with direct loads
-//    (global_load_lds_dwordx4, no register staging) into a 3-stage ring:
-//    while tile j is consumed, tile j+1 is ready and tile j+2 is in flight.
-//    A stage is refilled only after the barrier that follows its last read
-//    (the buffer-reuse rule of lecompute.fr, "Flapping Airplanes,
-//    ThunderKittens and megakernels", section "Prepare the next operation
-//    without overwriting the current one").  Rows are padded (K: d+8, V: d+16
-//    elements) so the MFMA operand reads are free of bank conflicts; the
-//    padding slots are filled by harmless duplicate loads so every load
-//    instruction covers whole 1 KB runs of LDS;
+//  * K and V tiles of 64 keys move HBM -> LDS with buffer loads that write
+//    straight to LDS (buffer_load_dwordx4 ... lds, no register staging) into
+//    a 4-stage ring: while tile j is consumed, tile j+1 is ready and tiles
+//    j+2, j+3 are in flight.  A stage is refilled only after the barrier that
+//    follows its last read (the buffer-reuse rule of lecompute.fr, "Flapping
+//    Airplanes, ThunderKittens and megakernels", section "Prepare the next
+//    operation without overwriting the current one").  Rows are padded (K:
+//    d+8, V: d+32 elements) so the MFMA operand reads are free of bank
+//    conflicts; the padding slots are filled by harmless duplicate loads so
+//    every load instruction covers a whole 1 KB run of LDS;
 //  * S^T = K*Q^T and O^T += V^T*P^T on v_mfma_f32_32x32x16_bf16.  In the S^T
 //    layout each lane owns one query row, so the row max/sum are in-lane plus
 //    one v_permlane32_swap, the rescale factor is a per-lane scalar, and P goes
@@ -35,7 +35,9 @@
 //    product (converted to bf16) without touching LDS.  V stays row-major in
 //    LDS and is read as the A operand with ds_read_b64_tr_b16;
 //  * software pipeline inside each wave: iteration j issues the MFMAs of
-//    S_{j+1} and, interleaved with them, the softmax of S_j; then P_j * V_j;
+//    S_{j+1} and, interleaved with them, the softmax of S_j; then P_j * V_j.
+//    Both parts run as groups of four MFMAs split by scheduling barriers, and
+//    every LDS operand read is issued one group ahead of its MFMAs;
 //  * softmax in base 2: P = exp2(s*c - m) with c = scale*log2(e) folded into
 //    one FMA; the reference max m moves only when a row max grows by more
 //    than 2^8, so most tiles skip the output rescale; LSE = (m + log2 l)*ln 2;
@@ -62,20 +64,25 @@ constexpr int NS = 4;                 // LDS ring stages
 template <int D>
 struct FwdLay {
     static constexpr int KP = D + 8;                 // K row pitch (elements)
-    static constexpr int VP = D + 16;                // V row pitch (elements)
+    // V rows are read with transposing reads: a half-wave reads 64 bytes of
+    // each of 4 consecutive rows, and a pitch of 16 (mod 64) dwords puts
+    // those rows on disjoint banks
+    static constexpr int VP = D + 32;                // V row pitch (elements)
     static constexpr int KS = KP / 8, VS = VP / 8;   // 16-byte slots per row
     static constexpr int DS = D / 8;                 // slots holding data
-    static constexpr int K_INSTR = BC * KS / 64;     // wave-wide loads per tile
-    static constexpr int V_INSTR = BC * VS / 64;
-    static constexpr int N_INSTR = K_INSTR + V_INSTR;
-    static constexpr int PER_WAVE = (N_INSTR + NW - 1) / NW;   // loads per wave per tile
+    static constexpr int K_INSTR = BC * KS / 64;     // wave-wide loads per K tile
+    static constexpr int V_INSTR = BC * VS / 64;     // ... per V tile
+    // every wave issues KW K loads, VW V loads and one more: a K load (waves
+    // below KR), a V load (the next VR waves) or a repeat of its own last V
+    // load (same source, same destination, so harmless)
+    static constexpr int KW = K_INSTR / NW, KR = K_INSTR % NW;
+    static constexpr int VW = V_INSTR / NW, VR = V_INSTR % NW;
+    static constexpr int PER_WAVE = KW + VW + 1;     // loads per wave per tile
     static constexpr int K_ELEMS = BC * KP;
     static constexpr int V_ELEMS = BC * VP;
-    // loads n >= N_INSTR (rounding up to a whole number per wave) repeat a
-    // real load into a 1 KB spare area at the end of the stage
-    static constexpr int SPARE = K_ELEMS + V_ELEMS;
-    static constexpr int STAGE = SPARE + 512;
+    static constexpr int STAGE = K_ELEMS + V_ELEMS;
     static_assert(BC * KS % 64 == 0 && BC * VS % 64 == 0, "a tile must be whole wave loads");
+    static_assert(KR + VR <= NW && KW >= 1 && VW >= 1, "load plan");
 };
 
 template <int D, bool CAUSAL, bool VARLEN>
@@ -152,35 +159,31 @@ void attn_fwd_kernel(FwdParams p) {
         }
     }
 
-    // Direct-load plan: the tile's K rows (KS slots each, the last one padding)
-    // then V rows (VS slots) are cut into wave-wide loads of 64 slots; wave w
-    // issues loads w, w+8, ...  Lane L of load n fills slot 64*m + L of its
-    // tensor; a padding slot re-reads the row's last data chunk.
-    // Load n of a tile (n < N_INSTR): tensor (K, then V), slot 64*m + lane of
-    // that tensor -> (row, column); a padding slot re-reads the row's last
-    // chunk.  A wave's loads n >= N_INSTR repeat its load n - NW into the
-    // spare area, so that every wave issues exactly PER_WAVE loads per tile.
-    // Load pp of this wave: tensor (K or V), destination in the stage and
-    // this lane's byte offset within the tile.  Loads past N_INSTR repeat the
-    // wave's load n - NW into the spare area.
-    auto plan_load = [&](int pp, bool &isv, int &ld) -> int {   // returns the slot
-        const int n0 = wave + NW * pp;
-        const bool spare = n0 >= L::N_INSTR;
-        const int n = spare ? n0 - NW : n0;
-        isv = n >= L::K_INSTR;
-        ld = spare ? L::SPARE : (isv ? L::K_ELEMS + 512 * (n - L::K_INSTR) : 512 * n);
-        return 64 * (isv ? n - L::K_INSTR : n) + lane;
+    // Direct-load plan: a tile's K rows (KS 16-byte slots each, the last one
+    // padding that re-reads the row's last chunk) and V rows (VS slots, the
+    // last four padding) are cut into wave-wide loads of 64 slots; lane L of
+    // load n of a tensor fills slot 64n + L.
+    auto load_index = [&](int pp, bool &isv) -> int {   // wave-uniform
+        if (pp < L::KW) { isv = false; return wave + NW * pp; }
+        if (pp < L::KW + L::VW) { isv = true; return wave + NW * (pp - L::KW); }
+        if (wave < L::KR) { isv = false; return NW * L::KW + wave; }
+        isv = true;
+        if (wave < L::KR + L::VR) return NW * L::VW + wave - L::KR;
+        return wave + NW * (L::VW - 1);
     };
     uint32_t goff[L::PER_WAVE];      // byte offset of this lane's chunk within a tile
+    int ldo[L::PER_WAVE];            // LDS element offset of the load within a stage
 #pragma unroll
     for (int pp = 0; pp < L::PER_WAVE; ++pp) {
         bool isv;
-        int ld;
-        const int slot = plan_load(pp, isv, ld);
+        const int n = load_index(pp, isv);
+        const int slot = 64 * n + lane;
         const int row = isv ? slot / L::VS : slot / L::KS;
         const int colx = min(slot - row * (isv ? L::VS : L::KS), L::DS - 1) * 8;
         goff[pp] = (uint32_t)(row * hd_k + colx) * 2u;
+        ldo[pp] = (isv ? L::K_ELEMS : 0) + 512 * n;
     }
+    const bool last_is_v = wave >= L::KR;
     const __bf16 *kbase = p.k + krow0 * hd_k + (int64_t)hk * D;
     const __bf16 *vbase = p.v + krow0 * hd_k + (int64_t)hk * D;
     auto issue = [&](int t) {
@@ -194,10 +197,8 @@ void attn_fwd_kernel(FwdParams p) {
         const __amdgpu_buffer_rsrc_t vr = buffer_rsrc(vbase + (int64_t)key0 * hd_k, nbytes);
 #pragma unroll
         for (int pp = 0; pp < L::PER_WAVE; ++pp) {
-            bool isv;
-            int ld;
-            plan_load(pp, isv, ld);
-            buffer_lds_dma16(isv ? vr : kr, goff[pp], dst + ld);
+            const bool isv = pp == L::PER_WAVE - 1 ? last_is_v : pp >= L::KW;
+            buffer_lds_dma16(isv ? vr : kr, goff[pp], dst + ldo[pp]);
         }
     };
 
@@ -273,48 +274,69 @@ void attn_fwd_kernel(FwdParams p) {
         }
     };
 
-    // Weights of one tile (branch-free, so it interleaves with the next
-    // tile's MFMAs): the row sum adds the fp32 weights (the LSE needs them
-    // unrounded); the second product takes them rounded to bf16.
-    auto weights = [&](f32x16 (&s)[BC / 32], bf16x8 (&pk)[BC / 16]) {
-        const float m_use = m == -__builtin_inff() ? 0.f : m;
-        float rs = 0.f;
-#pragma unroll
-        for (int kb = 0; kb < BC / 32; ++kb)
-#pragma unroll
-            for (int r = 0; r < 16; ++r) {
-                s[kb][r] = fast_exp2(__builtin_fmaf(s[kb][r], c, -m_use));
-                rs += s[kb][r];
-            }
-        lsum += rs;
-#pragma unroll
-        for (int kk = 0; kk < BC / 16; ++kk) pk[kk] = pack_p8(s[kk >> 1], 8 * (kk & 1));
-    };
-
     // lane coordinates for the transpose reads of V
     const int tr_e = (lane & 15) >> 2;       // row (key) within a 4-key group
     const int tr_s = lane & 3;               // 4-column slice
     const int tr_dh = (lane >> 4) & 1;       // which 16 columns of a 32-column block
 
     const int v_lane = L::K_ELEMS + (4 * g + tr_e) * L::VP + 16 * tr_dh + 4 * tr_s;
-    auto pv = [&](int t, const bf16x8 (&pk)[BC / 16]) {
+    // The fused part of a step is cut into groups separated by full
+    // scheduling barriers, so that every LDS read is issued one group ahead
+    // of the MFMAs that consume it (in-order issue would otherwise stall each
+    // MFMA on its own read).  Group g of the score product covers d-slices
+    // 2g, 2g+1 (FPG fragments); weight chunk g makes pk[] entries of the same
+    // rank.
+    constexpr int NG = D / 32;                   // score groups per tile
+    constexpr int FPG = 2 * (BC / 32);           // K fragments per group
+    constexpr int VPL = (BC / 2) / NG;           // weights per lane per chunk
+    constexpr int NV = 2 * (D / 32);             // V transpose reads per key slice
+    static_assert(VPL % 8 == 0, "a weight chunk must fill whole pk entries");
+    auto read_k = [&](int t, int grp, bf16x8 (&kf)[FPG]) {
+        const __bf16 *ks = lds + lane_base(t, k_lane);
+#pragma unroll
+        for (int u = 0; u < 2; ++u)
+#pragma unroll
+            for (int kb = 0; kb < BC / 32; ++kb)
+                kf[u * (BC / 32) + kb] = ld_lds_bf16x8(ks + 32 * kb * L::KP + 16 * (2 * grp + u));
+    };
+    auto mfma_k = [&](int grp, const bf16x8 (&kf)[FPG], f32x16 (&s)[BC / 32]) {
+#pragma unroll
+        for (int u = 0; u < 2; ++u)
+#pragma unroll
+            for (int kb = 0; kb < BC / 32; ++kb)
+                s[kb] = mfma32x32x16(kf[u * (BC / 32) + kb], qf[2 * grp + u], s[kb]);
+    };
+    auto weight_chunk = [&](int grp, f32x16 (&s)[BC / 32], bf16x8 (&pk)[BC / 16], float m_use,
+                            float &rs) {
+#pragma unroll
+        for (int f = grp * VPL; f < (grp + 1) * VPL; ++f) {
+            const int kb = f / 16, r = f % 16;
+            s[kb][r] = fast_exp2(__builtin_fmaf(s[kb][r], c, -m_use));
+            rs += s[kb][r];
+        }
+#pragma unroll
+        for (int kk = grp * VPL / 8; kk < (grp + 1) * VPL / 8; ++kk)
+            pk[kk] = pack_p8(s[kk >> 1], 8 * (kk & 1));
+    };
+    auto read_v = [&](int t, int kk, s16x4 (&vf)[NV]) {
         const __bf16 *vs = lds + lane_base(t, v_lane);
 #pragma unroll
-        for (int kk = 0; kk < BC / 16; ++kk) {
-#pragma unroll
-            for (int db = 0; db < D / 32; ++db) {
-                const s16x4 lo = lds_read_tr(vs + 16 * kk * L::VP + 32 * db);
-                const s16x4 hi = lds_read_tr(vs + (16 * kk + 8) * L::VP + 32 * db);
-                oacc[db] = mfma32x32x16(concat_tr(lo, hi), pk[kk], oacc[db]);
-            }
+        for (int db = 0; db < D / 32; ++db) {
+            vf[2 * db] = lds_read_tr(vs + 16 * kk * L::VP + 32 * db);
+            vf[2 * db + 1] = lds_read_tr(vs + (16 * kk + 8) * L::VP + 32 * db);
         }
+    };
+    auto mfma_v = [&](int kk, const s16x4 (&vf)[NV], const bf16x8 (&pk)[BC / 16]) {
+#pragma unroll
+        for (int db = 0; db < D / 32; ++db)
+            oacc[db] = mfma32x32x16(concat_tr(vf[2 * db], vf[2 * db + 1]), pk[kk], oacc[db]);
     };
 
     // One pipeline step: wait for tile j+1, refill the stage of tile j-1 with
-    // tile j+2, then S_{j+1} on the matrix cores interleaved with the softmax
+    // tile j+3, then S_{j+1} on the matrix cores interleaved with the softmax
     // of S_j, then O += P_j V_j.  scur holds S_j, snext receives S_{j+1}.
     auto step = [&](int j, f32x16 (&scur)[BC / 32], f32x16 (&snext)[BC / 32]) {
-        // tile j+1 complete (tile j+2 may still be in flight)
+        // tile j+1 complete (tiles j+2, j+3 may still be in flight)
         if (j + 2 < nt) wait_vmcnt<L::PER_WAVE>();
         else wait_vmcnt<0>();
         lds_barrier();
@@ -327,18 +349,36 @@ void attn_fwd_kernel(FwdParams p) {
                 snext[kb] = __builtin_nondeterministic_value(snext[kb]);
         }
         if (j < ntw) {
+            // the first K group of tile j+1 loads during the mask and row max
+            // (on a wave's last tile those scores are not used; the stage
+            // read is always in bounds)
+            bf16x8 kf[2][FPG];
+            read_k(j + 1, 0, kf[0]);
             mask(j, scur);
             row_max(scur);
-            bf16x8 pk[BC / 16];
-            // One basic block: the vector ALUs make this tile's weights while
-            // the matrix cores compute the next tile's scores (on a wave's
-            // last tile those scores are not used; the stage read is always in
-            // bounds), then the second product.
             __builtin_amdgcn_s_setprio(1);
-            weights(scur, pk);
-            scores(j + 1, snext);
-            __builtin_amdgcn_sched_barrier(0);   // keep the V reads out of the fused region
-            pv(j, pk);
+            const float m_use = m == -__builtin_inff() ? 0.f : m;
+            float rs = 0.f;
+            bf16x8 pk[BC / 16];
+            s16x4 vf[2][NV];
+#pragma unroll
+            for (int kb = 0; kb < BC / 32; ++kb) snext[kb] = f32x16{};
+#pragma unroll
+            for (int g = 0; g < NG; ++g) {
+                __builtin_amdgcn_sched_barrier(0);
+                if (g + 1 < NG) read_k(j + 1, g + 1, kf[(g + 1) & 1]);
+                else read_v(j, 0, vf[0]);
+                mfma_k(g, kf[g & 1], snext);
+                weight_chunk(g, scur, pk, m_use, rs);
+            }
+            lsum += rs;
+#pragma unroll
+            for (int kk = 0; kk < BC / 16; ++kk) {
+                __builtin_amdgcn_sched_barrier(0);
+                if (kk + 1 < BC / 16) read_v(j, kk + 1, vf[(kk + 1) & 1]);
+                mfma_v(kk, vf[kk & 1], pk);
+            }
+            __builtin_amdgcn_sched_barrier(0);
             __builtin_amdgcn_s_setprio(0);
         }
     };

@@ -70,8 +70,10 @@ __device__ __forceinline__ bf16x8 pack_p8(const f32x16 &s, int r0) {
 // LDS transpose read (ds_read_b64_tr_b16).  Within each group of 16 lanes,
 // lanes 4e..4e+3 each point at 4 consecutive bf16 of "row" e; lane i of the
 // group then receives element i of rows 0..3.  Used to fetch 4 keys of one
-// value column from a row-major V tile.
-__device__ __forceinline__ s16x4 lds_read_tr(const __bf16 *p) {
+// value column from a row-major V tile.  The restrict qualifier gives the
+// access alias information; without it the compiler must assume the read may
+// alias any buffer load still writing LDS and waits for all of them first.
+__device__ __forceinline__ s16x4 lds_read_tr(const __bf16 *__restrict__ p) {
     return __builtin_amdgcn_ds_read_tr16_b64_v4i16((lds_s16x4 *)(p));
 }
 
