@@ -132,6 +132,13 @@ DECODE = [  # B, Hq, Hkv, Skv, d, splits
     (2, 32, 8, 4096, 128, 0),       # library picks the split count
     (1, 40, 8, 513, 64, 2),
     (4, 16, 2, 129, 128, 1),
+    # 256 or more (sequence, KV head) groups: a workgroup merges all chunks of
+    # its groups itself (uneven last chunk; chunks shorter than the load
+    # ring; empty chunks; d = 64)
+    (64, 8, 4, 1000, 128, 7),
+    (64, 8, 4, 200, 128, 3),
+    (32, 16, 8, 100, 128, 64),
+    (128, 4, 2, 777, 64, 3),
 ]
 
 

@@ -21,10 +21,10 @@ constexpr int kFwdThreads = 64 * kFwdWaves;
 constexpr int kFwdBr = 32 * kFwdWaves;
 constexpr int kFwdBc = 64;
 
-// Decode tile shape: 4 waves, each takes 32 of the 128 keys of a tile; one
-// workgroup serves up to 32 query heads of one KV head.
+// Decode: 4 waves per workgroup, 64-key tiles; one work item serves up to
+// 32 query heads of one KV head.
 constexpr int kDecThreads = 256;
-constexpr int kDecBc = 128;
+constexpr int kDecBc = 64;
 constexpr int kDecCols = 32;
 
 struct FwdParams {
@@ -48,6 +48,8 @@ struct DecParams {
     int B, Hq, Hkv, group, Skv;
     int ncb;                 // blocks of <= 32 query heads per KV head
     int nsplit, chunk;       // key chunks and keys per chunk
+    int nti;                 // tiles per chunk (set by the launcher)
+    int own_groups;          // a workgroup merges all chunks of its groups (set by the launcher)
     float c;                 // scale * log2(e)
 };
 

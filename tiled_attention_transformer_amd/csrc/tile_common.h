@@ -23,6 +23,7 @@ typedef __bf16 bf16x4 __attribute__((ext_vector_type(4)));
 typedef __bf16 bf16x2 __attribute__((ext_vector_type(2)));
 typedef float f32x16 __attribute__((ext_vector_type(16)));
 typedef float f32x2 __attribute__((ext_vector_type(2)));
+typedef float f32x4 __attribute__((ext_vector_type(4)));
 typedef short s16x4 __attribute__((ext_vector_type(4)));
 typedef uint32_t u32x4 __attribute__((ext_vector_type(4)));
 typedef uint32_t u32x2 __attribute__((ext_vector_type(2)));
@@ -113,10 +114,16 @@ __device__ __forceinline__ void wait_vmcnt() {
     __builtin_amdgcn_s_waitcnt((N & 15) | ((N >> 4) << 14) | (7 << 4) | (15 << 8));
 }
 
+// s_waitcnt on the LDS counter only: every LDS read of this wave has landed.
+__device__ __forceinline__ void wait_lgkmcnt0() {
+    __builtin_amdgcn_s_waitcnt(0xF | (7 << 4) | (0 << 8) | (3 << 14));
+}
+
 // Workgroup barrier for LDS hand-off.  The waits it needs are issued
-// explicitly by the caller (wait_vmcnt for direct loads; reads are consumed
-// before the barrier); the signal fences only stop the compiler from moving
-// memory accesses across it.
+// explicitly by the caller: wait_vmcnt for direct loads, and for LDS reads
+// either their use before the barrier (an operand must have arrived) or
+// wait_lgkmcnt0; s_barrier itself waits for no memory access.  The signal
+// fences only stop the compiler from moving memory accesses across it.
 __device__ __forceinline__ void lds_barrier() {
     __atomic_signal_fence(__ATOMIC_SEQ_CST);
     __builtin_amdgcn_s_barrier();
