@@ -135,6 +135,67 @@ def write_traffic(fetch_dir: str, write_dir: str):
     print(json.dumps(out))
 
 
+def extra_workloads(api, dev, stream, calls=5):
+    """Context lines beside the headline: the long causal workload (B1 H32
+    S16384 d128) and the ragged causal batch (16 sequences, lengths drawn
+    U{128..8192} with seed 5, H32 d128).  Timing only: the inputs are seeded
+    N(0,1) bf16 draws made on the GPU (the lengths follow the same recipe as
+    the test inputs); K of the long workload is scaled per head by U(0.5, 2)
+    as in its test recipe."""
+    import torch
+    out = {}
+    gen = torch.Generator(device=dev)
+
+    def timed(fn):
+        for _ in range(2):
+            fn()
+        ev = [(torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True))
+              for _ in range(calls)]
+        for a, b in ev:
+            a.record(stream)
+            fn()
+            b.record(stream)
+        torch.cuda.synchronize()
+        return float(np.mean([a.elapsed_time(b) for a, b in ev]))
+
+    # long causal prefill
+    gen.manual_seed(3)
+    B, H, S, d = 1, 32, 16384, 128
+    q, k, v = (torch.randn((B, S, H, d), generator=gen, device=dev, dtype=torch.float32)
+               for _ in range(3))
+    k = k * (0.5 + 1.5 * torch.rand((1, 1, H, 1), generator=gen, device=dev))
+    q, k, v = (t.to(torch.bfloat16) for t in (q, k, v))
+    o = torch.empty_like(q)
+    lse = torch.empty((B, H, S), dtype=torch.float32, device=dev)
+    ms = timed(lambda: api.attn_fwd(q, k, v, o=o, lse=lse, causal=True, stream=stream))
+    fl = prefill_flops(B, H, S, S, d, True)
+    out["long_causal_B1_H32_S16384_d128"] = {
+        "ms": round(ms, 4), "TFLOP/s": round(fl / (ms * 1e-3) / 1e12, 1),
+        "frac_of_2500": round(fl / (ms * 1e-3) / 1e12 / PEAK_BF16_TFLOPS, 4)}
+    del q, k, v, o, lse
+
+    # ragged causal batch
+    lengths = np.random.default_rng(5).integers(128, 8192 + 1, 16)
+    cu = np.zeros(17, dtype=np.int32)
+    cu[1:] = np.cumsum(lengths)
+    total, H = int(cu[-1]), 32
+    gen.manual_seed(5)
+    q, k, v = (torch.randn((total, H, d), generator=gen, device=dev, dtype=torch.float32)
+               .to(torch.bfloat16) for _ in range(3))
+    cu_d = torch.from_numpy(cu).to(dev)
+    o = torch.empty_like(q)
+    lse = torch.empty((H, total), dtype=torch.float32, device=dev)
+    mx = int(lengths.max())
+    ms = timed(lambda: api.attn_fwd_varlen(q, k, v, cu_d, cu_d, mx, mx, o=o, lse=lse,
+                                           causal=True, stream=stream))
+    fl = float(sum(4.0 * d * H * L * (L + 1) / 2 for L in lengths))
+    out["ragged_causal_16seq_H32_d128"] = {
+        "ms": round(ms, 4), "TFLOP/s": round(fl / (ms * 1e-3) / 1e12, 1),
+        "frac_of_2500": round(fl / (ms * 1e-3) / 1e12 / PEAK_BF16_TFLOPS, 4),
+        "total_tokens": total, "algorithmic_flop": fl}
+    return out
+
+
 def cpu_baseline(spec, data, max_pairs):
     """The C oracle on a bounded sample of the prefill workload (rank 0 only)."""
     from oracle import cpu
@@ -158,9 +219,12 @@ def cpu_baseline(spec, data, max_pairs):
 def main():
     ap = argparse.ArgumentParser(description=__doc__.split("\n")[0])
     ap.add_argument("--gpus", type=int, default=1)
-    ap.add_argument("--steps", type=int, default=50)
-    ap.add_argument("--warmup", type=int, default=10)
+    ap.add_argument("--steps", type=int, default=100)
+    ap.add_argument("--warmup", type=int, default=200,
+                    help="untimed steps first (the clocks need some tens of ms to settle)")
     ap.add_argument("--no-cpu-baseline", action="store_true")
+    ap.add_argument("--no-extra", action="store_true",
+                    help="skip the long-causal and ragged-batch context lines")
     ap.add_argument("--cpu-pairs", type=float, default=2.0e8,
                     help="allowed query/key pairs in the CPU-baseline sample")
     ap.add_argument("--copy-calibration", action="store_true",
@@ -291,6 +355,8 @@ def main():
         },
         "kernel_hash": kernel_hash(),
     }
+    if not args.no_extra:
+        result["extra"] = extra_workloads(api, dev, stream)
     if not args.no_cpu_baseline:
         result["cpu_baseline"] = cpu_baseline(pspec, pdata, args.cpu_pairs)
     print(json.dumps(result), flush=True)
