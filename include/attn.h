@@ -112,11 +112,14 @@ attn_status_t attn_varlen_check(const int *cu_seqlens_host, int nseq, int total,
  *   q, o : [B, Hq, d] bf16      k_cache, v_cache : [B, Skv, Hkv, d] bf16
  *   lse  : [B, Hq] fp32 (or NULL)
  * The query is the newest position, so all Skv cached keys are attended.
- * The cache is cut into num_splits chunks of ceil(Skv / num_splits) keys;
- * one kernel computes a normalised partial output and its log-sum-exp per
- * (sequence, KV head, chunk) -- every query head of a KV group shares one
- * pass over that chunk of K and V -- and a second kernel merges the chunks:
+ * The cache is cut into num_splits chunks of ceil(Skv / num_splits) keys; a
+ * normalised partial output and its log-sum-exp are computed per (sequence,
+ * KV head, chunk) -- every query head of a KV group shares one pass over that
+ * chunk of K and V -- and the chunks are merged:
  * LSE = M + log(sum_s exp(lse_s - M)), O = sum_s exp(lse_s - LSE) * O_s.
+ * When the (sequence, KV head) groups spread evenly over the GPU's compute
+ * units the merge happens inside the chunk kernel and the workspace is not
+ * touched; otherwise a second kernel merges partials kept in the workspace.
  * num_splits <= 0 lets the library choose (attn_decode_pick_splits).
  * workspace: DEVICE scratch of at least attn_decode_workspace_bytes(...)
  * bytes, 16-byte aligned, owned by the caller, may be reused between calls
@@ -127,6 +130,23 @@ attn_status_t attn_decode(const void *q, const void *k_cache, const void *v_cach
                           float *lse, int B, int Hq, int Hkv, int Skv, int d, float scale,
                           int num_splits, void *workspace, size_t workspace_bytes,
                           hipStream_t stream);
+
+/*
+ * Decode against caches filled to different lengths: sequence b attends to
+ * keys 0 .. seqlens_k[b]-1 of its cache rows.  Same layouts, chunking,
+ * workspace and errors as attn_decode, with Skv_max the cache capacity
+ * (the row count of k_cache and v_cache).  seqlens_k: DEVICE int32 [B],
+ * 4-byte aligned, read by the kernels; values are clamped to
+ * [0, Skv_max] on the device (the host never reads them).  A sequence of
+ * length 0 gets O = 0 and LSE = -inf.  Chunks past a sequence's length read
+ * no memory.  Serving keeps one KV cache per sequence, each filled to its
+ * own length (lecompute.fr, "Flapping Airplanes, ThunderKittens and
+ * megakernels", section "A benchmark that could test the broader promise").
+ */
+attn_status_t attn_decode_varlen(const void *q, const void *k_cache, const void *v_cache,
+                                 void *o, float *lse, const int *seqlens_k, int B, int Hq,
+                                 int Hkv, int Skv_max, int d, float scale, int num_splits,
+                                 void *workspace, size_t workspace_bytes, hipStream_t stream);
 
 /* Bytes of decode workspace for these sizes (0 when num_splits resolves to
  * 1; num_splits <= 0 means the library's choice, as in attn_decode).  Returns

@@ -33,7 +33,7 @@ def lib():
 
 def test_library_exports_every_declared_symbol(lib):
     names = declared_functions()
-    assert len(names) == 7, names
+    assert len(names) == 8, names
     raw = ctypes.CDLL(_lib.LIB_PATH)
     for n in names:
         assert hasattr(raw, n), n
@@ -132,6 +132,23 @@ def test_decode_validation(lib):
     assert lib.attn_decode_workspace_bytes(2, 8, 2, 100, 128, 1) == 0
     assert lib.attn_decode_workspace_bytes(2, 8, 3, 100, 128, 4) == 0    # bad ratio
     assert lib.attn_decode_workspace_bytes(2, 8, 2, 100, 96, 4) == 0     # bad d
+
+
+def decode_varlen(lib, seqlens=P, B=2, Hq=8, Hkv=2, Skv=100, d=128, scale=0.1, splits=4, ws=P,
+                  wsb=1 << 30, q=P):
+    return lib.attn_decode_varlen(q, P, P, P, None, seqlens, B, Hq, Hkv, Skv, d, scale, splits,
+                                  ws, wsb, None)
+
+
+def test_decode_varlen_validation(lib):
+    assert decode_varlen(lib, seqlens=None) == NULLPTR
+    assert decode_varlen(lib, seqlens=P + 2) == ALIGN
+    assert decode_varlen(lib, q=None) == NULLPTR
+    assert decode_varlen(lib, Skv=0) == SHAPE
+    assert decode_varlen(lib, d=96) == BAD_D
+    assert decode_varlen(lib, Hq=6, Hkv=4) == GQA
+    assert decode_varlen(lib, scale=0.0) == SCALE
+    assert decode_varlen(lib, ws=None) == WS
 
 
 def test_decode_split_choice(lib):

@@ -155,6 +155,61 @@ def test_decode_matches_oracle(api, dev, case):
     assert_close(bf16_to_np(o), o_ref, f32_to_np(lse), lse_ref, str(case))
 
 
+DECODE_VARLEN = [  # B, Hq, Hkv, Skv_max, d, splits, lengths (None: random in [0, Skv_max])
+    (4, 8, 2, 1000, 128, 7, [1000, 1, 0, 513]),
+    (3, 4, 4, 300, 64, 1, [300, 17, 64]),
+    (5, 16, 4, 777, 128, 0, None),
+    (2, 64, 1, 200, 128, 3, [5, 200]),              # MQA, two column blocks
+    (64, 8, 4, 1000, 128, 8, None),                  # groups fill the GPU: in-kernel merge
+    (4, 8, 2, 256, 128, 4, [-5, 300, 256, 64]),      # out-of-range lengths are clamped
+]
+
+
+def _decode_varlen_ref(data, lengths, scale):
+    B, Hq, d = data["q"].shape
+    o = np.zeros((B, Hq, d))
+    lse = np.full((B, Hq), -np.inf)
+    for b, L in enumerate(lengths):
+        if L > 0:
+            ob, lb = cpu.decode_full(data["q"][b:b + 1], data["k"][b:b + 1, :L],
+                                     data["v"][b:b + 1, :L], scale)
+            o[b], lse[b] = ob[0], lb[0]
+    return o, lse
+
+
+@pytest.mark.parametrize("case", DECODE_VARLEN,
+                         ids=lambda c: "B%d_Hq%d_Hkv%d_Skv%d_d%d_s%d" % c[:6])
+def test_decode_varlen_matches_oracle(api, dev, case):
+    """Per-sequence cache lengths (0, 1, full, random; clamped when out of range)."""
+    import torch
+    B, Hq, Hkv, Skv, d, splits, lengths = case
+    data = si.make_decode(31 + Skv, B, Hq, Hkv, Skv, d)
+    if lengths is None:
+        lengths = np.random.default_rng(B + Skv).integers(0, Skv + 1, B)
+    lengths = np.asarray(lengths, dtype=np.int32)
+    scale = si.default_scale(d)
+    q, k, v = (to_dev(data[x], dev) for x in "qkv")
+    seq = torch.from_numpy(lengths).to(dev)
+    o, lse = api.attn_decode_varlen(q, k, v, seq, scale=scale, num_splits=splits)
+    torch.cuda.synchronize()
+    o_ref, lse_ref = _decode_varlen_ref(data, np.clip(lengths, 0, Skv), scale)
+    assert_close(bf16_to_np(o), o_ref, f32_to_np(lse), lse_ref, str(case[:6]))
+
+
+def test_decode_varlen_full_lengths_equal_decode(api, dev):
+    """Every sequence at full length: the same bits as attn_decode."""
+    import torch
+    for B, splits in ((4, 5), (64, 8)):
+        data = si.make_decode(41, B, 16, 4, 640, 128)
+        q, k, v = (to_dev(data[x], dev) for x in "qkv")
+        seq = torch.full((B,), 640, dtype=torch.int32, device=dev)
+        o1, l1 = api.attn_decode(q, k, v, num_splits=splits)
+        o2, l2 = api.attn_decode_varlen(q, k, v, seq, num_splits=splits)
+        torch.cuda.synchronize()
+        assert torch.equal(o1.view(torch.int16), o2.view(torch.int16))
+        assert torch.equal(l1, l2)
+
+
 def test_decode_split_counts_agree(api, dev):
     """1, 2, 8, 64 chunks and the library's choice agree closely (fp32 merge)."""
     import torch

@@ -159,6 +159,27 @@ def attn_decode(q, k_cache, v_cache, o=None, lse=None, scale=None, num_splits=0,
     ``[B,Hq]`` fp32.  workspace: a uint8 GPU tensor of at least
     :func:`attn_decode_workspace_bytes` bytes (allocated here if omitted).
     """
+    return _decode(q, k_cache, v_cache, None, o, lse, scale, num_splits, workspace, want_lse,
+                   stream)
+
+
+def attn_decode_varlen(q, k_cache, v_cache, seqlens_k, o=None, lse=None, scale=None,
+                       num_splits=0, workspace=None, want_lse=True, stream=None):
+    """Decode against caches of per-sequence lengths; returns ``(o, lse)``.
+
+    As :func:`attn_decode`, with ``seqlens_k`` an int32 GPU tensor ``[B]``:
+    sequence b attends to its first ``seqlens_k[b]`` cache rows (clamped to
+    the cache capacity on the device).
+    """
+    _need(seqlens_k, "seqlens_k", torch.int32, 1)
+    if seqlens_k.shape[0] != q.shape[0]:
+        raise ValueError("seqlens_k must have one entry per sequence")
+    return _decode(q, k_cache, v_cache, seqlens_k, o, lse, scale, num_splits, workspace,
+                   want_lse, stream)
+
+
+def _decode(q, k_cache, v_cache, seqlens_k, o, lse, scale, num_splits, workspace, want_lse,
+            stream):
     _need(q, "q", torch.bfloat16, 3)
     _need(k_cache, "k_cache", torch.bfloat16, 4)
     _need(v_cache, "v_cache", torch.bfloat16, 4)
@@ -178,8 +199,16 @@ def attn_decode(q, k_cache, v_cache, o=None, lse=None, scale=None, num_splits=0,
     if workspace is None and nbytes > 0:
         workspace = torch.empty(nbytes, dtype=torch.uint8, device=q.device)
     ws_bytes = 0 if workspace is None else workspace.numel() * workspace.element_size()
-    st = _lib.load().attn_decode(_ptr(q), _ptr(k_cache), _ptr(v_cache), _ptr(o), _ptr(lse), B,
-                                 Hq, Hkv, Skv, d, _scale(scale, d), int(num_splits),
-                                 _ptr(workspace), ws_bytes, _stream(stream))
-    _check(st, "attn_decode")
+    lib = _lib.load()
+    if seqlens_k is None:
+        st = lib.attn_decode(_ptr(q), _ptr(k_cache), _ptr(v_cache), _ptr(o), _ptr(lse), B, Hq,
+                             Hkv, Skv, d, _scale(scale, d), int(num_splits), _ptr(workspace),
+                             ws_bytes, _stream(stream))
+        _check(st, "attn_decode")
+    else:
+        st = lib.attn_decode_varlen(_ptr(q), _ptr(k_cache), _ptr(v_cache), _ptr(o), _ptr(lse),
+                                    _ptr(seqlens_k), B, Hq, Hkv, Skv, d, _scale(scale, d),
+                                    int(num_splits), _ptr(workspace), ws_bytes,
+                                    _stream(stream))
+        _check(st, "attn_decode_varlen")
     return o, lse

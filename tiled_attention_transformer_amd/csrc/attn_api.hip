@@ -170,9 +170,13 @@ size_t attn_decode_workspace_bytes(int B, int Hq, int Hkv, int Skv, int d, int n
     return decode_ws_bytes(B, Hq, d, sh.nsplit);
 }
 
-attn_status_t attn_decode(const void *q, const void *k_cache, const void *v_cache, void *o,
-                          float *lse, int B, int Hq, int Hkv, int Skv, int d, float scale,
-                          int num_splits, void *workspace, size_t workspace_bytes,
+}  // extern "C"
+
+namespace {
+
+attn_status_t decode_impl(const void *q, const void *k_cache, const void *v_cache, void *o,
+                          float *lse, const int *seqlens, int B, int Hq, int Hkv, int Skv, int d,
+                          float scale, int num_splits, void *workspace, size_t workspace_bytes,
                           hipStream_t stream) {
     if (!q || !k_cache || !v_cache || !o) return ATTN_ERR_NULLPTR;
     if (!decode_sizes_ok(B, Hq, Hkv, Skv, d)) return ATTN_ERR_SHAPE;
@@ -196,6 +200,7 @@ attn_status_t attn_decode(const void *q, const void *k_cache, const void *v_cach
     p.v = (const __bf16 *)v_cache;
     p.o = (__bf16 *)o;
     p.lse = lse;
+    p.seqlens = seqlens;
     if (need > 0) {
         p.ws_o = (float *)workspace;
         p.ws_lse = p.ws_o + (size_t)sh.nsplit * B * Hq * d;
@@ -210,6 +215,28 @@ attn_status_t attn_decode(const void *q, const void *k_cache, const void *v_cach
     p.chunk = sh.chunk;
     p.c = scale * attn::kLog2e;
     return from_hip(attn::launch_decode(p, d, stream));
+}
+
+}  // namespace
+
+extern "C" {
+
+attn_status_t attn_decode(const void *q, const void *k_cache, const void *v_cache, void *o,
+                          float *lse, int B, int Hq, int Hkv, int Skv, int d, float scale,
+                          int num_splits, void *workspace, size_t workspace_bytes,
+                          hipStream_t stream) {
+    return decode_impl(q, k_cache, v_cache, o, lse, nullptr, B, Hq, Hkv, Skv, d, scale,
+                       num_splits, workspace, workspace_bytes, stream);
+}
+
+attn_status_t attn_decode_varlen(const void *q, const void *k_cache, const void *v_cache,
+                                 void *o, float *lse, const int *seqlens_k, int B, int Hq,
+                                 int Hkv, int Skv_max, int d, float scale, int num_splits,
+                                 void *workspace, size_t workspace_bytes, hipStream_t stream) {
+    if (!seqlens_k) return ATTN_ERR_NULLPTR;
+    if (!aligned(seqlens_k, 4)) return ATTN_ERR_ALIGNMENT;
+    return decode_impl(q, k_cache, v_cache, o, lse, seqlens_k, B, Hq, Hkv, Skv_max, d, scale,
+                       num_splits, workspace, workspace_bytes, stream);
 }
 
 }  // extern "C"

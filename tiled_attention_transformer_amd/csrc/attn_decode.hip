@@ -114,7 +114,10 @@ void attn_decode_split_kernel(DecParams p) {
         r.hk = id % p.Hkv;
         r.b = id / p.Hkv;
         r.k_lo = r.sp * p.chunk;
-        r.nkeys = max(0, min(p.Skv, r.k_lo + p.chunk) - r.k_lo);
+        // the sequence's cache length (per sequence when given; tiles past it
+        // get empty load ranges, so they read no memory, and are masked)
+        const int len = p.seqlens ? min(max(p.seqlens[r.b], 0), p.Skv) : p.Skv;
+        r.nkeys = max(0, min(len, r.k_lo + p.chunk) - r.k_lo);
         r.ncols = min(NCOL, p.group - NCOL * cb);
         r.h0 = r.hk * p.group + NCOL * cb;
         return r;

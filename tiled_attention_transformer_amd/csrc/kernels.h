@@ -45,6 +45,7 @@ struct DecParams {
     __bf16 *o;
     float *lse;              // may be null
     float *ws_o, *ws_lse;    // split partials (null when nsplit == 1)
+    const int *seqlens;      // keys per sequence (device, clamped to [0, Skv]), or null: all Skv
     int B, Hq, Hkv, group, Skv;
     int ncb;                 // blocks of <= 32 query heads per KV head
     int nsplit, chunk;       // key chunks and keys per chunk
