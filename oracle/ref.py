@@ -65,7 +65,7 @@ def softmax_rows(s: np.ndarray, allowed: np.ndarray):
     with no allowed entry gets ``p = 0``, ``m = -inf``, ``l = 0``.
     """
     s = np.where(allowed, s, NEG_INF)
-    m = s.max(axis=-1)
+    m = s.max(axis=-1, initial=NEG_INF)         # also defined for zero keys
     any_ok = allowed.any(axis=-1)
     m_safe = np.where(any_ok, m, 0.0)
     e = np.where(allowed, np.exp(s - m_safe[..., None]), 0.0)

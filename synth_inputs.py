@@ -122,6 +122,31 @@ def make_varlen(seed, nseq, lo, hi, H, d, Hkv=None, lengths=None):
                 cu_seqlens=cu, lengths=lengths)
 
 
+def make_varlen_cross(seed, lengths_q, lengths_k, H, d, Hkv=None):
+    """Packed ragged batch whose query and key lengths differ per sequence.
+
+    The shape of chunked prefill: sequence s brings ``lengths_q[s]`` new
+    query rows and attends to ``lengths_k[s]`` keys (its earlier tokens and
+    the new ones).  Either length may be 0.  q is [total_q,H,d], k/v are
+    [total_k,Hkv,d], and cu_seqlens_q / cu_seqlens_k are int32 [nseq+1].
+    """
+    Hkv = H if Hkv is None else Hkv
+    lq = np.asarray(lengths_q, dtype=np.int64)
+    lk = np.asarray(lengths_k, dtype=np.int64)
+    if lq.shape != lk.shape:
+        raise ValueError("lengths_q and lengths_k must have one entry per sequence")
+    rng = np.random.default_rng(seed)
+    cu_q = np.zeros(len(lq) + 1, dtype=np.int32)
+    cu_k = np.zeros(len(lk) + 1, dtype=np.int32)
+    cu_q[1:] = np.cumsum(lq)
+    cu_k[1:] = np.cumsum(lk)
+    q = rng.standard_normal((int(cu_q[-1]), H, d), dtype=np.float32)
+    k = rng.standard_normal((int(cu_k[-1]), Hkv, d), dtype=np.float32)
+    v = rng.standard_normal((int(cu_k[-1]), Hkv, d), dtype=np.float32)
+    return dict(q=f32_to_bf16_bits(q), k=f32_to_bf16_bits(k), v=f32_to_bf16_bits(v),
+                cu_seqlens_q=cu_q, cu_seqlens_k=cu_k, lengths_q=lq, lengths_k=lk)
+
+
 def make_config(n: int):
     """Inputs and the spec for one of the five workloads."""
     spec = dict(CONFIGS[n])

@@ -359,6 +359,39 @@ def test_varlen_equals_separate_calls_and_c_rows():
             np.testing.assert_allclose(lc[n], lse[h, cu[s] + i], atol=1e-13)
 
 
+def test_varlen_cross_lengths_and_empty_sequences():
+    """Chunked-prefill shape: query and key lengths differ per sequence.
+
+    A sequence with no keys gives O = 0 and LSE = -inf on every row (the
+    no-allowed-key reading); a sequence with no queries writes nothing.  Each
+    non-empty sequence equals a separate call, under bottom-right causal
+    alignment, and the C oracle's rows agree with the numpy ones.
+    """
+    lq, lk = [2, 0, 5, 3, 1], [4, 3, 5, 0, 6]
+    data = si.make_varlen_cross(57, lq, lk, H=4, d=8, Hkv=2)
+    q, k, v = (si.bf16_to_f64(data[x]) for x in "qkv")
+    cq, ck = data["cu_seqlens_q"], data["cu_seqlens_k"]
+    for causal in (False, True):
+        o, lse = ref.attention_varlen(q, k, v, cq, ck, 0.5, causal)
+        # sequence 3 has three queries and no keys
+        assert np.all(o[cq[3]:cq[4]] == 0) and np.all(np.isneginf(lse[:, cq[3]:cq[4]]))
+        for s in (0, 2, 4):
+            a, b, c, e = cq[s], cq[s + 1], ck[s], ck[s + 1]
+            os_, ls_ = ref.attention(q[None, a:b], k[None, c:e], v[None, c:e], 0.5, causal)
+            np.testing.assert_array_equal(o[a:b], os_[0])
+            np.testing.assert_array_equal(lse[:, a:b], ls_[0])
+        if causal:
+            # sequence 0: 2 queries after 2 earlier keys; row 0 sees keys 0..2
+            s_ = 0.5 * (q[0, 0] @ k[0:3, 0].T)
+            w = np.exp(s_ - s_.max())
+            np.testing.assert_allclose(o[0, 0], (w / w.sum()) @ v[0:3, 0], atol=1e-14)
+        rows = np.array([(s, h, i) for s in range(5) for h in range(4) for i in range(lq[s])])
+        oc, lc = cpu.varlen_rows(data["q"], data["k"], data["v"], cq, ck, 0.5, causal, rows)
+        for n, (s, h, i) in enumerate(rows):
+            np.testing.assert_allclose(oc[n], o[cq[s] + i, h], atol=1e-13)
+            assert lc[n] == lse[h, cq[s] + i] or abs(lc[n] - lse[h, cq[s] + i]) < 1e-13
+
+
 # ---- the C oracle against the numpy oracle, and sampled rows ----
 
 @pytest.mark.parametrize("case", CASES)

@@ -324,6 +324,44 @@ def test_varlen_equals_separate_calls_bitwise(api, dev):
             assert np.array_equal(o[a:b], os_[0]) and np.array_equal(lse[:, a:b], ls_[0])
 
 
+VARLEN_CROSS = [  # d, Hq, Hkv, query lengths, key lengths (chunked prefill, empty sides)
+    (128, 4, 2, [5, 0, 300, 64, 1, 200], [100, 7, 300, 0, 400, 77]),
+    (64, 6, 3, [129, 3, 0, 130], [1000, 3, 1, 129]),
+]
+
+
+@pytest.mark.parametrize("case", VARLEN_CROSS, ids=["d128", "d64"])
+@pytest.mark.parametrize("causal", [False, True], ids=["full", "causal"])
+def test_varlen_cross_lengths_match_oracle(api, dev, case, causal):
+    """Query and key lengths differ per sequence, either may be 0.
+
+    Every query row is compared with the oracle; rows of a sequence with no
+    keys (and, under the bottom-right causal mask, leading rows of a sequence
+    with more queries than keys) must be exactly O = 0, LSE = -inf.
+    """
+    import torch
+    d, Hq, Hkv, lq, lk = case
+    data = si.make_varlen_cross(21 + d, lq, lk, H=Hq, d=d, Hkv=Hkv)
+    cq, ck = data["cu_seqlens_q"], data["cu_seqlens_k"]
+    q, k, v = (to_dev(data[x], dev) for x in "qkv")
+    cq_d, ck_d = torch.from_numpy(cq).to(dev), torch.from_numpy(ck).to(dev)
+    scale = si.default_scale(d)
+    print("varlen cross d=%d causal=%d lq=%s lk=%s" % (d, causal, lq, lk), flush=True)
+    o, lse = api.attn_fwd_varlen(q, k, v, cq_d, ck_d, max(lq), max(lk), scale=scale,
+                                 causal=causal)
+    torch.cuda.synchronize()
+    o, lse = bf16_to_np(o), f32_to_np(lse)
+    rows = np.array([(s, h, i) for s in range(len(lq)) for h in range(Hq) for i in range(lq[s])],
+                    dtype=np.int64)
+    o_ref, lse_ref = cpu.varlen_rows(data["q"], data["k"], data["v"], cq, ck, scale, causal, rows)
+    tok = cq[rows[:, 0]] + rows[:, 2]
+    assert_close(o[tok, rows[:, 1]], o_ref, lse[rows[:, 1], tok], lse_ref, str(case))
+    for s in range(len(lq)):
+        dead = lq[s] if lk[s] == 0 else (max(0, lq[s] - lk[s]) if causal else 0)
+        a = cq[s]
+        assert np.all(o[a:a + dead] == 0) and np.all(np.isneginf(lse[:, a:a + dead]))
+
+
 def test_lse_optional(api, dev):
     import torch
     data = si.make_prefill(19, 1, 2, 2, 200, 200, 64)
