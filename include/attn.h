@@ -69,7 +69,7 @@ typedef enum {
  *   q, o : [B, Sq, Hq, d]  bf16        k, v : [B, Skv, Hkv, d]  bf16
  *   lse  : [B, Hq, Sq]     fp32 (or NULL)
  *   causal: 0 = every key, nonzero = bottom-right causal mask.
- * Query tiles of 128 rows, key tiles of 64 keys; under the causal mask the
+ * Query tiles of 256 rows, key tiles of 64 keys; under the causal mask the
  * key tiles above a query tile's diagonal are never loaded.
  */
 attn_status_t attn_fwd(const void *q, const void *k, const void *v, void *o, float *lse,

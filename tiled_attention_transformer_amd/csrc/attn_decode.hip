@@ -422,9 +422,8 @@ hipError_t launch_t(DecParams p, hipStream_t s) {
     constexpr int BC = DEC_BC;
     const int64_t items = (int64_t)p.B * p.Hkv * p.ncb * p.nsplit;
     if (items > 0x7fffffff) return hipErrorInvalidConfiguration;
-    int dev = 0, cus = 0;
-    hipError_t e = hipGetDevice(&dev);
-    if (e == hipSuccess) e = hipDeviceGetAttribute(&cus, hipDeviceAttributeMultiprocessorCount, dev);
+    int cus = 0;
+    hipError_t e = current_cu_count(&cus);
     if (e != hipSuccess) return e;
     p.nti = (p.chunk + BC - 1) / BC;
     const int64_t want = (int64_t)cus * DEC_WPC;

@@ -15,9 +15,10 @@
 // one wave interleaves both streams).
 //
 // gfx950 mapping:
-//  * one workgroup = 8 waves = 256 query rows of one (batch, head), one
-//    workgroup per CU (two waves per SIMD); each wave owns 32 rows and keeps
-//    its Q fragment, running max/sum and fp32 output accumulator in registers;
+//  * one work item = 256 query rows of one (batch, head); a workgroup of 8
+//    waves runs one item at a time, one workgroup per CU (two waves per
+//    SIMD); each wave owns 32 rows and keeps its Q fragment, running max/sum
+//    and fp32 output accumulator in registers;
 //  * K and V tiles of 64 keys move HBM -> LDS with buffer loads that write
 //    straight to LDS (buffer_load_dwordx4 ... lds, no register staging) into
 //    a 4-stage ring: while tile j is consumed, tile j+1 is ready and tiles
@@ -28,6 +29,14 @@
 //    d+8, V: d+32 elements) so the MFMA operand reads are free of bank
 //    conflicts; the padding slots are filled by harmless duplicate loads so
 //    every load instruction covers a whole 1 KB run of LDS;
+//  * persistent workgroups (fixed-size batches): the grid has one workgroup
+//    per CU and each walks a static list of items.  The tile loads form one
+//    stream across items, so the first tiles of the next item, and its query
+//    rows, load while the current item finishes; the output of an item is
+//    written while the scores of the next one are computed.  This is the
+//    scheduling of the same page, section "Prepare the next operation
+//    without overwriting the current one" (start the next piece of work
+//    before the current one has fully drained), applied inside one kernel;
 //  * S^T = K*Q^T and O^T += V^T*P^T on v_mfma_f32_32x32x16_bf16.  In the S^T
 //    layout each lane owns one query row, so the row max/sum are in-lane plus
 //    one v_permlane32_swap, the rescale factor is a per-lane scalar, and P goes
@@ -44,10 +53,14 @@
 //  * under the causal mask, key tiles above a query tile's diagonal are never
 //    loaded, waves skip tiles above their own rows, and only tiles that cross
 //    the diagonal or the sequence end evaluate the mask;
-//  * the grid is 1-D, ordered (tile rank, batch*head) so that every head's
-//    longest tile is dispatched first under the causal mask, and all tiles of
-//    one head land on the same XCD (workgroups go round-robin over the 8 XCDs)
-//    when batch*heads is a multiple of 8, so they share that XCD's L2 for K/V.
+//  * item order: (tile rank, batch*head), so under the causal mask the
+//    longest items come first.  A persistent workgroup w takes positions w,
+//    then the mirror position of the next row of the list, and so on
+//    (boustrophedon), which pairs long items with short ones; the mirror is
+//    taken in steps of 8 so an item's head keeps the XCD of workgroup w
+//    (workgroups go round-robin over the 8 XCDs) and its K/V stays in one L2.
+//    Ragged batches launch one workgroup per item instead: their item sizes
+//    are known only on the device, and the hardware dispatcher balances them.
 #include "kernels.h"
 #include "tile_common.h"
 
@@ -85,6 +98,62 @@ struct FwdLay {
     static_assert(KR + VR <= NW && KW >= 1 && VW >= 1, "load plan");
 };
 
+// One work item: query rows q0 .. q0+BR-1 of one (batch or sequence, head).
+struct FwdItem {
+    int b, h;
+    int Sq, Skv;            // query rows and keys of the sequence
+    int q0;                 // first query row of the item
+    int nt;                 // key tiles any row of the item may see (0: none)
+    int64_t qrow0, krow0;   // first query / key row of the sequence
+};
+
+template <bool CAUSAL, bool VARLEN>
+__device__ __forceinline__ FwdItem fwd_item(const FwdParams &p, int it) {
+    FwdItem x;
+    const int BH = p.nbatch * p.Hq;
+    const int rank = it / BH;
+    const int bh = it - rank * BH;
+    x.b = bh / p.Hq;
+    x.h = bh - x.b * p.Hq;
+    if constexpr (VARLEN) {
+        // the offsets are never written by the kernel: read them through the
+        // constant address space, so they are scalar loads into SGPRs (and
+        // take no part in the vector-load counter the tile waits rely on)
+        typedef const __attribute__((address_space(4))) int cint;
+        cint *cq = (cint *)p.cu_q, *ck = (cint *)p.cu_k;
+        const int qs = cq[x.b], qe = cq[x.b + 1];
+        const int ks = ck[x.b], ke = ck[x.b + 1];
+        const bool ok = qs >= 0 && qe >= qs && qe <= p.total_q && ks >= 0 && ke >= ks &&
+                        ke <= p.total_k;
+        x.Sq = ok ? qe - qs : 0;
+        x.Skv = ok ? ke - ks : 0;
+        x.qrow0 = qs;
+        x.krow0 = ks;
+    } else {
+        x.Sq = p.Sq;
+        x.Skv = p.Skv;
+        x.qrow0 = (int64_t)x.b * p.Sq;
+        x.krow0 = (int64_t)x.b * p.Skv;
+    }
+    const int tile = CAUSAL ? (p.ntiles - 1 - rank) : rank;
+    x.q0 = tile * BR;
+    int kend = x.Skv;
+    // one past the last key any row of the item may see (bottom-right causal)
+    if (CAUSAL) kend = min(x.Skv, x.q0 + BR + (x.Skv - x.Sq));
+    x.nt = (x.q0 < x.Sq && kend > 0) ? (kend + BC - 1) / BC : 0;
+    return x;
+}
+
+// The r-th item of this workgroup (boustrophedon over rows of gridDim.x
+// items, mirrored in steps of 8 so the item's head stays on this XCD), or -1.
+__device__ __forceinline__ int fwd_item_at(const FwdParams &p, int r) {
+    const int G = gridDim.x, w = blockIdx.x;
+    int pos = w;
+    if (r & 1) pos = (G % 8 == 0) ? (G / 8 - 1 - w / 8) * 8 + (w % 8) : G - 1 - w;
+    const int64_t it = (int64_t)r * G + pos;
+    return it < p.nitems ? (int)it : -1;
+}
+
 template <int D, bool CAUSAL, bool VARLEN>
 __global__ __launch_bounds__(NT) __attribute__((amdgpu_waves_per_eu(2, 2)))
 void attn_fwd_kernel(FwdParams p) {
@@ -96,68 +165,18 @@ void attn_fwd_kernel(FwdParams p) {
     const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
     const int g = lane >> 5;            // which half of the wave
     const int col = lane & 31;          // query row within the wave
-
-    const int BH = p.nbatch * p.Hq;
-    const int id = blockIdx.x;
-    const int tile_rank = id / BH;
-    const int bh = id - tile_rank * BH;
-    const int b = bh / p.Hq;
-    const int h = bh - b * p.Hq;
-    const int hk = h / p.group;
-
-    int64_t qrow0, krow0;
-    int Sq, Skv;
-    int64_t lse_base, lse_hstride;
-    if constexpr (VARLEN) {
-        const int qs = p.cu_q[b], qe = p.cu_q[b + 1];
-        const int ks = p.cu_k[b], ke = p.cu_k[b + 1];
-        const bool ok = qs >= 0 && qe >= qs && qe <= p.total_q && ks >= 0 && ke >= ks &&
-                        ke <= p.total_k;
-        Sq = ok ? qe - qs : 0;
-        Skv = ok ? ke - ks : 0;
-        qrow0 = qs;
-        krow0 = ks;
-        lse_base = qs;
-        lse_hstride = p.total_q;
-    } else {
-        Sq = p.Sq;
-        Skv = p.Skv;
-        qrow0 = (int64_t)b * Sq;
-        krow0 = (int64_t)b * Skv;
-        lse_base = (int64_t)b * p.Hq * Sq;
-        lse_hstride = Sq;
-    }
-    const int tile = CAUSAL ? (p.ntiles - 1 - tile_rank) : tile_rank;
-    const int q0 = tile * BR;
-    if (q0 >= Sq) return;                        // whole workgroup: uniform exit
-
-    const int off = Skv - Sq;                    // bottom-right causal offset
-    int kend = Skv;
-    if (CAUSAL) kend = min(Skv, q0 + BR + off);  // one past the last key any row may see
-    const int nt = kend > 0 ? (kend + BC - 1) / BC : 0;
-
-    const int wrow0 = q0 + 32 * wave;            // first row of this wave
-    const int qr = wrow0 + col;                  // this lane's query row
-    // key tiles this wave computes (its rows' causal reach; none past Sq)
-    int ntw = 0;
-    if (wrow0 < Sq) {
-        int wk = Skv;
-        if (CAUSAL) wk = min(Skv, min(wrow0 + 32, Sq) + off);
-        ntw = wk > 0 ? min(nt, (wk + BC - 1) / BC) : 0;
-    }
     const int64_t hd_q = (int64_t)p.Hq * D;
     const int64_t hd_k = (int64_t)p.Hkv * D;
 
-    // Q fragments (B operand of S^T = K Q^T), resident for the whole loop.
-    bf16x8 qf[D / 16];
-    {
-        const __bf16 *qp = p.q + (qrow0 + qr) * hd_q + (int64_t)h * D + 8 * g;
-#pragma unroll
-        for (int t = 0; t < D / 16; ++t) {
-            if (qr < Sq) qf[t] = ld_global_bf16x8(qp + 16 * t);
-            else qf[t] = bf16x8{};
+    auto item = [&](int r) { return fwd_item<CAUSAL, VARLEN>(p, fwd_item_at(p, r)); };
+    // next item after position r that has key tiles, or -1
+    auto next_tiled = [&](int r) -> int {
+        for (int s = r + 1;; ++s) {
+            const int it = fwd_item_at(p, s);
+            if (it < 0) return -1;
+            if (fwd_item<CAUSAL, VARLEN>(p, it).nt > 0) return s;
         }
-    }
+    };
 
     // Direct-load plan: a tile's K rows (KS 16-byte slots each, the last one
     // padding that re-reads the row's last chunk) and V rows (VS slots, the
@@ -184,37 +203,81 @@ void attn_fwd_kernel(FwdParams p) {
         ldo[pp] = (isv ? L::K_ELEMS : 0) + 512 * n;
     }
     const bool last_is_v = wave >= L::KR;
-    const __bf16 *kbase = p.k + krow0 * hd_k + (int64_t)hk * D;
-    const __bf16 *vbase = p.v + krow0 * hd_k + (int64_t)hk * D;
-    auto issue = [&](int t) {
-        const int key0 = t * BC;
-        __bf16 *dst = lds + (t % NS) * L::STAGE;
-        // the descriptors end at the last valid key, so rows past the sequence
-        // end read as zeros
-        const int rows = min(BC, Skv - key0);
-        const int nbytes = (int)(((int64_t)(rows - 1) * hd_k + D) * 2);
-        const __amdgpu_buffer_rsrc_t kr = buffer_rsrc(kbase + (int64_t)key0 * hd_k, nbytes);
-        const __amdgpu_buffer_rsrc_t vr = buffer_rsrc(vbase + (int64_t)key0 * hd_k, nbytes);
+
+    // The load stream: every tile of every item of this workgroup, in order,
+    // numbered 0, 1, 2, ...; tile n goes to stage n % NS.  Once the stream
+    // is exhausted each issue is a load over an empty range (it only writes
+    // zeros to a free stage), so every issue adds the same number of loads
+    // to the wave's counter and the waits below are fixed counts.
+    int l_r = -1;            // item of the next tile (-1: stream exhausted)
+    int l_tiles = 0;         // tiles of that item still to issue
+    int l_keys = 0;          // valid keys from the next tile on
+    int64_t l_off = 0;       // element offset of the next tile (K and V alike)
+    int l_stage = 0;         // LDS element offset of the next tile's stage
+    auto load_item = [&](int r) {
+        l_r = r;
+        if (r >= 0) {
+            const FwdItem x = item(r);
+            l_tiles = x.nt;
+            l_keys = x.Skv;
+            l_off = x.krow0 * hd_k + (int64_t)(x.h / p.group) * D;
+        }
+    };
+    auto issue_next = [&]() {
+        __bf16 *dst = lds + l_stage;
+        const __bf16 *kb = p.k, *vb = p.v;
+        int nbytes = 0;
+        if (l_r >= 0) {
+            // the descriptors end at the last valid key, so rows past the
+            // sequence end read as zeros
+            const int rows = min(BC, l_keys);
+            nbytes = (int)(((int64_t)(rows - 1) * hd_k + D) * 2);
+            kb = p.k + l_off;
+            vb = p.v + l_off;
+            l_off += BC * hd_k;
+            l_keys -= BC;
+            if (--l_tiles == 0) load_item(next_tiled(l_r));
+        }
+        const __amdgpu_buffer_rsrc_t kr = buffer_rsrc(kb, nbytes);
+        const __amdgpu_buffer_rsrc_t vr = buffer_rsrc(vb, nbytes);
 #pragma unroll
         for (int pp = 0; pp < L::PER_WAVE; ++pp) {
             const bool isv = pp == L::PER_WAVE - 1 ? last_is_v : pp >= L::KW;
             buffer_lds_dma16(isv ? vr : kr, goff[pp], dst + ldo[pp]);
         }
+        l_stage = l_stage == (NS - 1) * L::STAGE ? 0 : l_stage + L::STAGE;
     };
 
-    // LDS element offset of this lane's first operand in stage t.  Kept
-    // opaque so that each read is one address register plus an immediate
-    // offset (otherwise the optimizer keeps one register per read).
-    auto lane_base = [&](int t, int lane_off) -> int {
-        int o = (t % NS) * L::STAGE + lane_off;
+    // Q fragments (B operand of S^T = K Q^T), resident while an item runs.
+    // The buffer descriptor covers this wave's valid rows only, so rows past
+    // the sequence end load as zeros.
+    bf16x8 qf[D / 16];
+    auto load_q = [&](const FwdItem &x) {
+        const int wr0 = x.q0 + 32 * wave;
+        const int rows = min(32, x.Sq - wr0);
+        const __bf16 *qb = p.q + (x.qrow0 + wr0) * hd_q + (int64_t)x.h * D;
+        const int nbytes = rows > 0 ? (int)(((int64_t)(rows - 1) * hd_q + D) * 2) : 0;
+        const __amdgpu_buffer_rsrc_t rq = buffer_rsrc(rows > 0 ? qb : p.q, nbytes);
+        const uint32_t off0 = (uint32_t)((col * hd_q + 8 * g) * 2);
+#pragma unroll
+        for (int t = 0; t < D / 16; ++t)
+            qf[t] = __builtin_bit_cast(bf16x8,
+                                       __builtin_amdgcn_raw_buffer_load_b128(rq, off0 + 32 * t, 0, 0));
+    };
+
+    // LDS element offset of this lane's first operand in the stage of tile n.
+    // Kept opaque so that each read is one address register plus an
+    // immediate offset (otherwise the optimizer keeps one register per read).
+    auto lane_base = [&](int n, int lane_off) -> int {
+        int o = (n % NS) * L::STAGE + lane_off;
         asm volatile("" : "+v"(o));
         return o;
     };
     const int k_lane = col * L::KP + 8 * g;
 
     // S^T = K Q^T for one tile: two 32-key blocks, chains interleaved.
-    auto scores = [&](int t, f32x16 (&s)[BC / 32]) {
-        const __bf16 *ks = lds + lane_base(t, k_lane);
+    auto scores = [&](int n, f32x16 (&s)[BC / 32]) {
+        const __bf16 *ks = lds + lane_base(n, k_lane);
 #pragma unroll
         for (int kb = 0; kb < BC / 32; ++kb) s[kb] = f32x16{};
 #pragma unroll
@@ -225,11 +288,12 @@ void attn_fwd_kernel(FwdParams p) {
     };
 
     f32x16 oacc[D / 32];
-#pragma unroll
-    for (int db = 0; db < D / 32; ++db) oacc[db] = f32x16{};
     float m = -__builtin_inff();     // reference max, scaled base-2 units
     float lsum = 0.f;                // this lane's share of the running sum
     const float c = p.c;
+
+    // geometry of the item being computed (wave-uniform, except qr)
+    int Skv = 0, off = 0, wrow0 = 0, qr = 0, ntw = 0;
 
     // Mask keys past each row's causal limit or past the sequence end; only
     // tiles that cross the diagonal or the end need it.
@@ -242,11 +306,22 @@ void attn_fwd_kernel(FwdParams p) {
             // opaque to the optimizer: otherwise it folds 4g into the 32
             // constants below and keeps them live (32 registers) across the loop
             asm volatile("" : "+v"(lim));
+            // each score: compare into VCC, then select -inf.  Written as one
+            // asm pair per score so the masks never pile up: left to itself
+            // the compiler hoists all 32 compares and holds 32 lane masks in
+            // scalar registers, which pushes other scalars out to memory
+            const float ninf = -__builtin_inff();
 #pragma unroll
             for (int kb = 0; kb < BC / 32; ++kb)
 #pragma unroll
-                for (int r = 0; r < 16; ++r)
-                    if (32 * kb + 8 * (r >> 2) + (r & 3) > lim) s[kb][r] = -__builtin_inff();
+                for (int r = 0; r < 16; ++r) {
+                    float x = s[kb][r];
+                    asm volatile("v_cmp_gt_i32_e32 vcc, %2, %1\n\tv_cndmask_b32_e32 %0, %0, %3, vcc"
+                                 : "+v"(x)
+                                 : "v"(lim), "i"(32 * kb + 8 * (r >> 2) + (r & 3)), "v"(ninf)
+                                 : "vcc");
+                    s[kb][r] = x;
+                }
         }
     };
 
@@ -291,8 +366,8 @@ void attn_fwd_kernel(FwdParams p) {
     constexpr int VPL = (BC / 2) / NG;           // weights per lane per chunk
     constexpr int NV = 2 * (D / 32);             // V transpose reads per key slice
     static_assert(VPL % 8 == 0, "a weight chunk must fill whole pk entries");
-    auto read_k = [&](int t, int grp, bf16x8 (&kf)[FPG]) {
-        const __bf16 *ks = lds + lane_base(t, k_lane);
+    auto read_k = [&](int n, int grp, bf16x8 (&kf)[FPG]) {
+        const __bf16 *ks = lds + lane_base(n, k_lane);
 #pragma unroll
         for (int u = 0; u < 2; ++u)
 #pragma unroll
@@ -318,8 +393,8 @@ void attn_fwd_kernel(FwdParams p) {
         for (int kk = grp * VPL / 8; kk < (grp + 1) * VPL / 8; ++kk)
             pk[kk] = pack_p8(s[kk >> 1], 8 * (kk & 1));
     };
-    auto read_v = [&](int t, int kk, s16x4 (&vf)[NV]) {
-        const __bf16 *vs = lds + lane_base(t, v_lane);
+    auto read_v = [&](int n, int kk, s16x4 (&vf)[NV]) {
+        const __bf16 *vs = lds + lane_base(n, v_lane);
 #pragma unroll
         for (int db = 0; db < D / 32; ++db) {
             vf[2 * db] = lds_read_tr(vs + 16 * kk * L::VP + 32 * db);
@@ -331,29 +406,62 @@ void attn_fwd_kernel(FwdParams p) {
         for (int db = 0; db < D / 32; ++db)
             oacc[db] = mfma32x32x16(concat_tr(vf[2 * db], vf[2 * db + 1]), pk[kk], oacc[db]);
     };
-
-    // One pipeline step: wait for tile j+1, refill the stage of tile j-1 with
-    // tile j+3, then S_{j+1} on the matrix cores interleaved with the softmax
-    // of S_j, then O += P_j V_j.  scur holds S_j, snext receives S_{j+1}.
-    auto step = [&](int j, f32x16 (&scur)[BC / 32], f32x16 (&snext)[BC / 32]) {
-        // tile j+1 complete (tiles j+2, j+3 may still be in flight)
-        if (j + 2 < nt) wait_vmcnt<L::PER_WAVE>();
-        else wait_vmcnt<0>();
-        lds_barrier();
-        if (j + 3 < nt) issue(j + 3);
-        if (j >= ntw) {
-            // no tile for this wave: snext gets a placeholder, so that no score
-            // buffer has to stay live across steps
+    // O += P_j V_j, V fragments read one key slice ahead
+    auto pv = [&](int n, s16x4 (&vf)[2][NV], const bf16x8 (&pk)[BC / 16]) {
 #pragma unroll
-            for (int kb = 0; kb < BC / 32; ++kb)
-                snext[kb] = __builtin_nondeterministic_value(snext[kb]);
+        for (int kk = 0; kk < BC / 16; ++kk) {
+            __builtin_amdgcn_sched_barrier(0);
+            if (kk + 1 < BC / 16) read_v(n, kk + 1, vf[(kk + 1) & 1]);
+            mfma_v(kk, vf[kk & 1], pk);
         }
+        __builtin_amdgcn_sched_barrier(0);
+    };
+
+    int cn = 0;              // stream number of the tile being computed
+    bool stores = false;     // output stores issued since the last full wait
+    bool q_pend = false;     // query rows loaded during the previous step
+    int nt = 0;              // key tiles of the current item
+    int rA = -1, rB = -1;    // current item and the next one with key tiles
+    int ntB = 0, ntwB = 0;   // key tiles of item rB, and this wave's share
+
+    // Query rows are loaded one step ahead: at the end of a step whose next
+    // step is the last one of its item Y (that last step computes the first
+    // scores of the item after Y; this step's score MFMAs are done with qf).
+    auto prefetch_q = [&](int rY) {
+        const int rn = next_tiled(rY);
+        if (rn >= 0) {
+            load_q(item(rn));
+            q_pend = true;
+        }
+    };
+
+    // One pipeline step of item-local tile j (stream tile cn): wait for tile
+    // cn+1, refill the stage of tile cn-1 with the next tile of the stream,
+    // then the scores of tile cn+1 on the matrix cores interleaved with the
+    // softmax of S_j, then O += P_j V_j.  scur holds S_j, snext receives the
+    // scores of tile cn+1, which on the item's last tile is the first tile of
+    // the next item (computed with that item's query rows).  j >= nt is a
+    // no-op (the loop below is unrolled by two).
+    auto step = [&](int j, f32x16 (&scur)[BC / 32], f32x16 (&snext)[BC / 32]) {
+        if (j >= nt) return;
+        // tile cn+1 complete (cn+2 and any later query rows may still be in
+        // flight; loads complete in order); after output stores wait for
+        // everything, since stores and loads share the counter
+        if (stores) wait_vmcnt<0>();
+        else if (q_pend) wait_vmcnt<L::PER_WAVE + D / 16>();
+        else wait_vmcnt<L::PER_WAVE>();
+        stores = false;
+        q_pend = false;
+        lds_barrier();
+        const bool last = j == nt - 1;
+        // the item whose last step comes next, if any (-2: none)
+        const int r_last = j + 1 == nt - 1 ? rA : (last && ntB == 1 ? rB : -2);
         if (j < ntw) {
-            // the first K group of tile j+1 loads during the mask and row max
-            // (on a wave's last tile those scores are not used; the stage
-            // read is always in bounds)
+            // the first K group of tile cn+1 loads during the mask and row max
+            // (scores nobody needs are computed anyway; the stage read is
+            // always in bounds)
             bf16x8 kf[2][FPG];
-            read_k(j + 1, 0, kf[0]);
+            read_k(cn + 1, 0, kf[0]);
             mask(j, scur);
             row_max(scur);
             __builtin_amdgcn_s_setprio(1);
@@ -364,70 +472,182 @@ void attn_fwd_kernel(FwdParams p) {
 #pragma unroll
             for (int kb = 0; kb < BC / 32; ++kb) snext[kb] = f32x16{};
 #pragma unroll
-            for (int g = 0; g < NG; ++g) {
+            for (int gr = 0; gr < NG; ++gr) {
                 __builtin_amdgcn_sched_barrier(0);
-                if (g + 1 < NG) read_k(j + 1, g + 1, kf[(g + 1) & 1]);
-                else read_v(j, 0, vf[0]);
-                mfma_k(g, kf[g & 1], snext);
-                weight_chunk(g, scur, pk, m_use, rs);
+                if (gr + 1 < NG) read_k(cn + 1, gr + 1, kf[(gr + 1) & 1]);
+                else read_v(cn, 0, vf[0]);
+                mfma_k(gr, kf[gr & 1], snext);
+                weight_chunk(gr, scur, pk, m_use, rs);
             }
             lsum += rs;
-#pragma unroll
-            for (int kk = 0; kk < BC / 16; ++kk) {
-                __builtin_amdgcn_sched_barrier(0);
-                if (kk + 1 < BC / 16) read_v(j, kk + 1, vf[(kk + 1) & 1]);
-                mfma_v(kk, vf[kk & 1], pk);
-            }
-            __builtin_amdgcn_sched_barrier(0);
+            pv(cn, vf, pk);
             __builtin_amdgcn_s_setprio(0);
+        } else {
+            // no tile of this item for this wave; it may still owe the first
+            // scores of the next item
+            if (last && ntwB > 0) {
+                scores(cn + 1, snext);
+            } else {
+                // a placeholder, so that no score buffer stays live across steps
+#pragma unroll
+                for (int kb = 0; kb < BC / 32; ++kb)
+                    snext[kb] = __builtin_nondeterministic_value(snext[kb]);
+            }
+        }
+        // the next tile of the stream goes into the stage of tile cn-1 (every
+        // wave is past its last read, at the barrier above); issued after
+        // the compute so that the MFMAs start right after the barrier
+        issue_next();
+        // one load point for both paths (a load in each branch would be
+        // merged by register copies that wait for the load at once)
+        if (r_last != -2) prefetch_q(r_last);
+        ++cn;
+    };
+
+    // Output of an item: O = acc / l (bf16), LSE = (m + log2 l) * ln 2.  With
+    // zero set, the item has no keys: O = 0 and LSE = -inf.  The stores go
+    // through buffer descriptors that end at this wave's last valid row, so
+    // rows past the sequence end are dropped by the range check instead of a
+    // per-lane branch (a divergent branch here would make the compiler treat
+    // the item loop's state as per-lane).
+    auto write_out = [&](const FwdItem &x, bool zero) {
+        const int wr0 = x.q0 + 32 * wave;
+        if (wr0 >= x.Sq) return;
+        const int rows = min(32, x.Sq - wr0);
+        const float lt = zero ? 0.f : half_swap_sum(lsum);
+        const float inv = lt > 0.f ? 1.f / lt : 0.f;
+        const __bf16 *ob = p.o + (x.qrow0 + wr0) * hd_q + (int64_t)x.h * D;
+        const __amdgpu_buffer_rsrc_t ro = buffer_rsrc(ob, (int)(((int64_t)(rows - 1) * hd_q + D) * 2));
+        const uint32_t oo = (uint32_t)((col * hd_q + 4 * g) * 2);
+#pragma unroll
+        for (int db = 0; db < D / 32; ++db)
+#pragma unroll
+            for (int rq = 0; rq < 4; ++rq) {
+                const bf16x4 v4 = zero ? bf16x4{} :
+                    to_bf16x4(oacc[db][4 * rq] * inv, oacc[db][4 * rq + 1] * inv,
+                              oacc[db][4 * rq + 2] * inv, oacc[db][4 * rq + 3] * inv);
+                __builtin_amdgcn_raw_buffer_store_b64(__builtin_bit_cast(u32x2, v4), ro,
+                                                      oo + (32 * db + 8 * rq) * 2, 0, 0);
+            }
+        if (p.lse != nullptr) {
+            int64_t l0;
+            if constexpr (VARLEN) l0 = (int64_t)x.h * p.total_q + x.qrow0 + wr0;
+            else l0 = ((int64_t)x.b * p.Hq + x.h) * x.Sq + wr0;
+            const __amdgpu_buffer_rsrc_t rl = buffer_rsrc(p.lse + l0, rows * 4);
+            const float v = lt > 0.f ? (m + fast_log2(lt)) * kLn2 : -__builtin_inff();
+            // one lane per row stores; the other half's offset is out of range
+            __builtin_amdgcn_raw_buffer_store_b32(__builtin_bit_cast(uint32_t, v), rl,
+                                                  g == 0 ? (uint32_t)(col * 4) : 0x80000000u, 0, 0);
+        }
+    };
+
+    // key tiles of item x that this wave computes (its rows' causal reach)
+    auto wave_tiles = [&](const FwdItem &x) -> int {
+        const int w0 = x.q0 + 32 * wave;
+        if (w0 >= x.Sq || x.nt == 0) return 0;
+        int wk = x.Skv;
+        if (CAUSAL) wk = min(x.Skv, min(w0 + 32, x.Sq) + (x.Skv - x.Sq));
+        return wk > 0 ? min(x.nt, (wk + BC - 1) / BC) : 0;
+    };
+    // items after position r0 and before r1 (-1: to the end) that have rows
+    // but no keys: O = 0, LSE = -inf
+    auto write_empty = [&](int r0, int r1) {
+        for (int r = r0 + 1; r1 < 0 || r < r1; ++r) {
+            const int it = fwd_item_at(p, r);
+            if (it < 0) break;
+            const FwdItem x = fwd_item<CAUSAL, VARLEN>(p, it);
+            if (x.q0 < x.Sq && x.nt == 0) {
+                write_out(x, true);
+                stores = true;
+            }
+        }
+    };
+    // make item r current: its geometry, and the next item with key tiles
+    auto enter = [&](int r) {
+        rA = r;
+        const FwdItem x = item(r);
+        nt = x.nt;
+        Skv = x.Skv;
+        off = x.Skv - x.Sq;                       // bottom-right causal offset
+        wrow0 = x.q0 + 32 * wave;                 // first row of this wave
+        qr = wrow0 + col;                         // this lane's query row
+        ntw = wave_tiles(x);
+        rB = next_tiled(r);
+        ntB = 0;
+        ntwB = 0;
+        if (rB >= 0) {
+            const FwdItem y = item(rB);
+            ntB = y.nt;
+            ntwB = wave_tiles(y);
         }
     };
 
     // score buffers: a step reads scur only for tiles whose scores it wrote
     f32x16 sa[BC / 32], sb[BC / 32];
-    if (nt > 0) {
-        issue(0);
-        if (nt > 1) issue(1);
-        if (nt > 2) issue(2);
-        // tile 0 complete (tiles 1, 2 may still be in flight), visible to all waves
-        if (nt > 2) wait_vmcnt<2 * L::PER_WAVE>();
-        else if (nt > 1) wait_vmcnt<L::PER_WAVE>();
-        else wait_vmcnt<0>();
+    const int r0 = next_tiled(-1);
+    write_empty(-1, r0);
+    if (r0 >= 0) {
+        enter(r0);
+        load_q(item(r0));
+        load_item(r0);
+        issue_next();
+        issue_next();
+        issue_next();
+        // the first item's query rows and first tile have landed (its next
+        // tiles may be in flight), visible to all waves
+        if (stores) wait_vmcnt<0>();
+        else wait_vmcnt<2 * L::PER_WAVE>();
+        stores = false;
         lds_barrier();
-        if (ntw > 0) scores(0, sa);
-    }
-    // unrolled by two so the score buffers alternate without copies; the
-    // second step always runs (past the end it only waits at the barrier)
-    for (int j = 0; j < nt; j += 2) {
-        step(j, sa, sb);
-        step(j + 1, sb, sa);
-    }
-
-    // Epilogue: O = acc / l (bf16), LSE = (m + log2 l) * ln 2.
-    if (wrow0 >= Sq) return;
-    const float lt = half_swap_sum(lsum);
-    if (qr >= Sq) return;
-    const float inv = lt > 0.f ? 1.f / lt : 0.f;
-    __bf16 *op = p.o + (qrow0 + qr) * hd_q + (int64_t)h * D + 4 * g;
+        if (ntw > 0) {
+            scores(cn, sa);
+        } else {
 #pragma unroll
-    for (int db = 0; db < D / 32; ++db)
-#pragma unroll
-        for (int rq = 0; rq < 4; ++rq) {
-            const bf16x4 v4 = to_bf16x4(oacc[db][4 * rq] * inv, oacc[db][4 * rq + 1] * inv,
-                                        oacc[db][4 * rq + 2] * inv, oacc[db][4 * rq + 3] * inv);
-            *reinterpret_cast<bf16x4 *>(op + 32 * db + 8 * rq) = v4;
+            for (int kb = 0; kb < BC / 32; ++kb) sa[kb] = __builtin_nondeterministic_value(sa[kb]);
         }
-    if (p.lse != nullptr && g == 0)
-        p.lse[lse_base + (int64_t)h * lse_hstride + qr] =
-            lt > 0.f ? (m + fast_log2(lt)) * kLn2 : -__builtin_inff();
+        if (nt == 1) prefetch_q(rA);
+    }
+    while (rA >= 0) {
+#pragma unroll
+        for (int db = 0; db < D / 32; ++db) oacc[db] = f32x16{};
+        m = -__builtin_inff();
+        lsum = 0.f;
+        // unrolled by two so the score buffers alternate without copies
+        for (int j = 0; j < nt; j += 2) {
+            step(j, sa, sb);
+            step(j + 1, sb, sa);
+        }
+        // the next item's first scores are in sb after an odd tile count
+        if (nt & 1) {
+#pragma unroll
+            for (int kb = 0; kb < BC / 32; ++kb) sa[kb] = sb[kb];
+        }
+        write_out(item(rA), false);
+        stores = true;
+        write_empty(rA, rB);
+        if (rB < 0) break;
+        enter(rB);
+    }
+    wait_vmcnt<0>();                 // no load may outlive the workgroup
 }
 
 template <int D, bool CAUSAL, bool VARLEN>
-hipError_t launch_t(const FwdParams &p, hipStream_t s) {
-    const int64_t blocks = (int64_t)p.ntiles * p.nbatch * p.Hq;
-    if (blocks <= 0) return hipSuccess;
-    if (blocks > 0x7fffffff) return hipErrorInvalidConfiguration;
-    hipLaunchKernelGGL((attn_fwd_kernel<D, CAUSAL, VARLEN>), dim3((unsigned)blocks), dim3(NT), 0,
+hipError_t launch_t(const FwdParams &p_in, hipStream_t s) {
+    FwdParams p = p_in;
+    const int64_t items = (int64_t)p.ntiles * p.nbatch * p.Hq;
+    if (items <= 0) return hipSuccess;
+    if (items > 0x7fffffff) return hipErrorInvalidConfiguration;
+    p.nitems = (int)items;
+    int grid = p.nitems;
+    if (!VARLEN) {
+        // one workgroup per CU (the LDS ring allows no more), each walking
+        // its share of the items
+        int cus = 0;
+        const hipError_t e = current_cu_count(&cus);
+        if (e != hipSuccess) return e;
+        if (cus > 0 && grid > cus) grid = cus;
+    }
+    hipLaunchKernelGGL((attn_fwd_kernel<D, CAUSAL, VARLEN>), dim3((unsigned)grid), dim3(NT), 0,
                        s, p);
     return hipGetLastError();
 }

@@ -6,6 +6,8 @@
 #include <hip/hip_runtime.h>
 #include <stdint.h>
 
+#include <atomic>
+
 namespace attn {
 
 constexpr float kLn2 = 0.69314718055994530942f;
@@ -27,6 +29,30 @@ constexpr int kDecThreads = 256;
 constexpr int kDecBc = 64;
 constexpr int kDecCols = 32;
 
+// Compute units of the current device.  Cached per device after the first
+// query: the attribute query costs host time on every launch otherwise,
+// which shows up as idle GPU time between back-to-back calls.
+inline hipError_t current_cu_count(int *cus) {
+    static std::atomic<int> cache[64];
+    int dev = 0;
+    hipError_t e = hipGetDevice(&dev);
+    if (e != hipSuccess) return e;
+    const bool cached = dev >= 0 && dev < 64;
+    if (cached) {
+        const int c = cache[dev].load(std::memory_order_relaxed);
+        if (c > 0) {
+            *cus = c;
+            return hipSuccess;
+        }
+    }
+    int n = 0;
+    e = hipDeviceGetAttribute(&n, hipDeviceAttributeMultiprocessorCount, dev);
+    if (e != hipSuccess) return e;
+    if (cached) cache[dev].store(n, std::memory_order_relaxed);
+    *cus = n;
+    return hipSuccess;
+}
+
 struct FwdParams {
     const __bf16 *q, *k, *v;
     __bf16 *o;
@@ -36,7 +62,8 @@ struct FwdParams {
     int Hq, Hkv, group;      // group = Hq / Hkv
     int Sq, Skv;             // fixed batch only
     int total_q, total_k;    // varlen only
-    int ntiles;              // query tiles per (batch, head) in the grid
+    int ntiles;              // query tiles per (batch, head)
+    int nitems;              // ntiles * nbatch * Hq (set by the launcher)
     float c;                 // scale * log2(e)
 };
 
