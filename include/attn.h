@@ -118,8 +118,12 @@ attn_status_t attn_varlen_check(const int *cu_seqlens_host, int nseq, int total,
  * chunk of K and V -- and the chunks are merged:
  * LSE = M + log(sum_s exp(lse_s - M)), O = sum_s exp(lse_s - LSE) * O_s.
  * When the (sequence, KV head) groups spread evenly over the GPU's compute
- * units the merge happens inside the chunk kernel and the workspace is not
- * touched; otherwise a second kernel merges partials kept in the workspace.
+ * units, each workgroup takes whole sequences instead: its four waves split
+ * the keys and their results are merged the same way inside the kernel, and
+ * the workspace is not touched; otherwise the chunks spread over the
+ * workgroups and a second kernel merges partials kept in the workspace.
+ * Either way the result is the same log-sum-exp merge (up to fp32 rounding
+ * order), and it is deterministic for given sizes and num_splits.
  * num_splits <= 0 lets the library choose (attn_decode_pick_splits).
  * workspace: DEVICE scratch of at least attn_decode_workspace_bytes(...)
  * bytes, 16-byte aligned, owned by the caller, may be reused between calls

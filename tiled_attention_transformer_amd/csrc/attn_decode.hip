@@ -1,37 +1,42 @@
 // Split-KV decode for gfx950: one new query token per sequence against a KV
-// cache, followed by a log-sum-exp merge of the key chunks.
+// cache, with a log-sum-exp merge of the key ranges.
 //
-// The per-chunk work is the attention of the FlashAttention-4 page
+// The per-range work is the attention of the FlashAttention-4 page
 // (lecompute.fr, "FlashAttention-4 : limites du calcul matriciel", section
-// "Entre deux multiplications il faut fabriquer les poids"); the merge uses
+// "Entre deux multiplications il faut fabriquer les poids"); the merges use
 // the same common-scale bookkeeping as the tiled softmax (section "Déplacer
-// une partie des exponentielles"), applied across chunks.  Decode rereads the
-// whole context state for every generated token, so it is bound by memory
-// bandwidth (lecompute.fr, "Flapping Airplanes, ThunderKittens and
+// une partie des exponentielles"), applied across key ranges.  Decode rereads
+// the whole context state for every generated token, so it is bound by
+// memory bandwidth (lecompute.fr, "Flapping Airplanes, ThunderKittens and
 // megakernels", section "Follow the request instead of one utilization
 // number", and the KV-cache note in "A benchmark that could test the broader
 // promise").
 //
 // gfx950 mapping (the split kernel streams; it is bound by HBM bandwidth):
 //  * a persistent grid, one 4-wave workgroup per CU: workgroup w takes the
-//    work items (sequence, KV head, block of <= 32 query heads, key chunk)
-//    w, w + grid, ... and streams their 64-key K/V tiles back to back, so the
-//    load pipeline never drains between items;
-//  * tiles move HBM -> LDS with buffer loads that write straight to LDS into
-//    a 4-stage ring (3 tiles, 96 KB, in flight per CU); rows are unpadded
-//    and their 16-byte chunks are XOR-swizzled by row so that both operand
-//    reads below are free of bank conflicts;
-//  * every wave computes the scores of all 64 keys against all query heads
-//    of the block (S^T = K Q^T, v_mfma_f32_32x32x16_bf16; cheap next to the
-//    memory time) and keeps identical softmax state; wave w then owns output
-//    columns 32w .. 32w+31 of O^T += V^T P^T (V read with ds_read_b64_tr_b16),
-//    so no cross-wave merge is needed;
-//  * the next item's query rows load into LDS the same way while the
-//    current item streams (a load into registers would make every wait on
-//    the in-order load counter also wait for all older tile loads);
-//  * each item's result is written normalised, in fp32, with its natural-log
-//    LSE, and a second small kernel merges the chunks; with a single chunk
-//    the result goes out directly as bf16.
+//    work items w, w + grid, ...; an item is (sequence, KV head, block of
+//    <= 32 query heads, key range), and all query heads of a GQA group share
+//    one pass over that range of K and V;
+//  * the four waves split an item's keys: wave v takes 32-key tiles v, v+4,
+//    v+8, ... (so together they read 128 consecutive keys at a time) and
+//    streams them through a private 2-stage LDS ring with buffer loads that
+//    write straight to LDS.  No wave waits for another while streaming:
+//    a ring shared by the workgroup needs a barrier per tile, and that
+//    barrier alone held a plain load stream of this shape to ~5.35 TB/s
+//    where private rings reach ~5.9 TB/s;
+//  * each wave keeps its own online softmax (running max, sum, fp32
+//    output) for its keys: S^T = K Q^T and O^T += V^T P^T on
+//    v_mfma_f32_32x32x16_bf16, V read with ds_read_b64_tr_b16; rows are
+//    unpadded and their 16-byte chunks XOR-swizzled by row so both operand
+//    reads are free of bank conflicts;
+//  * at the end of an item the four waves merge their states through LDS
+//    (log-sum-exp weights, then a fixed-order sum, so results are
+//    deterministic) and the result goes out: bf16 O and LSE when the item is
+//    the whole sequence, else a normalised fp32 partial with its natural-log
+//    LSE for a second small kernel that merges the key ranges;
+//  * the next item's query rows are loaded into spare registers at the end
+//    of each wave's last tile, ahead of that wave's next tile load, so the
+//    stream does not drain between items.
 #include "kernels.h"
 #include "tile_common.h"
 
@@ -42,21 +47,21 @@ namespace {
 constexpr int NT = kDecThreads;          // 4 waves
 constexpr int NWV = NT / 64;
 constexpr int NCOL = kDecCols;           // query heads per block (MFMA columns)
+constexpr int TK = 32;                   // keys per wave tile
 
-template <int D, int BC, int NSD>
+template <int D>
 struct DecLay {
     static constexpr int CPR = D / 8;                  // 16-byte chunks per row
-    static constexpr int T_ELEMS = BC * D;             // one K or V tile
+    static constexpr int T_ELEMS = TK * D;             // one K or V tile
     static constexpr int STAGE = 2 * T_ELEMS;          // K, then V
-    static constexpr int LOADS = 2 * BC * CPR / 64;    // wave-wide loads per tile
-    static constexpr int PER_WAVE = LOADS / NWV;
-    static constexpr int Q_ELEMS = NCOL * D;           // query rows of one item
-    static constexpr int Q_LOADS = Q_ELEMS / 512;      // wave-wide loads for them
-    static constexpr int Q_PER_WAVE = (Q_LOADS + NWV - 1) / NWV;
-    static constexpr int Q_BASE = NSD * STAGE;
-    static constexpr int TOTAL = Q_BASE + Q_ELEMS;
-    static_assert(LOADS % (2 * NWV) == 0, "K and V loads must split evenly over the waves");
+    static constexpr int LOADS = T_ELEMS / 512;        // wave-wide loads per K (or V) tile
+    static constexpr int RING = 2 * STAGE;             // two stages per wave
+    static constexpr int MERGE = NCOL * D;             // fp32 output block for the merge
+    static constexpr int LSE = NWV * NCOL;             // per-wave LSEs (fp32)
+    // LDS in bf16 elements: the rings, then the fp32 merge areas
+    static constexpr int TOTAL = NWV * RING + 2 * (MERGE + LSE);
     static_assert((CPR & (CPR - 1)) == 0 && 32 % CPR == 0, "chunk swizzle needs a power of two");
+    static_assert(T_ELEMS % 512 == 0, "a tile must be whole wave loads");
 };
 
 // Chunk swizzles (physical chunk = logical chunk ^ f(row)).  K is read by
@@ -68,11 +73,10 @@ __device__ __forceinline__ int swz_k(int row) { return row & (D / 8 - 1); }
 template <int D>
 __device__ __forceinline__ int swz_v(int row) { return (4 * (row & 3)) & (D / 8 - 1); }
 
-// BC keys per tile, NSD ring stages
-template <int D, int BC, int NSD>
+template <int D>
 __global__ __launch_bounds__(NT)
 void attn_decode_split_kernel(DecParams p) {
-    using L = DecLay<D, BC, NSD>;
+    using L = DecLay<D>;
     __shared__ __attribute__((aligned(16))) __bf16 lds[L::TOTAL];
 
     const int tid = threadIdx.x;
@@ -81,303 +85,292 @@ void attn_decode_split_kernel(DecParams p) {
     const int g = lane >> 5;
     const int col = lane & 31;
     const int64_t hd_k = (int64_t)p.Hkv * D;
+    __bf16 *ring = lds + wave * L::RING;
+    float *merge_o = reinterpret_cast<float *>(lds + NWV * L::RING);
+    float *merge_l = merge_o + L::MERGE;
 
-    // Work items are (group, chunk) with group = (sequence, KV head, block of
-    // query heads).  Without own_groups, workgroup w takes items w, w + grid,
-    // ... (chunks of one group spread over workgroups; a second kernel merges
-    // them).  With own_groups, it takes whole groups w, w + grid, ..., their
-    // chunks in order, and merges the chunks itself.
+    // Work items are (group, key range), range fastest, with group =
+    // (sequence, KV head, block of query heads); workgroup w takes items
+    // w, w + grid, ...
     const int G = gridDim.x;
-    const int ngroups = p.B * p.Hkv * p.ncb;
-    const int my_items = p.own_groups
-                             ? (ngroups - (int)blockIdx.x + G - 1) / G * p.nsplit
-                             : (ngroups * p.nsplit - (int)blockIdx.x + G - 1) / G;
-    const int ntot = my_items * p.nti;           // tiles this workgroup streams
+    const int nitems = p.B * p.Hkv * p.ncb * p.nsplit;
+    const int my_items = ((int)blockIdx.x < nitems) ? (nitems - (int)blockIdx.x + G - 1) / G : 0;
 
     struct Item {
-        int b, hk, h0, ncols, sp, k_lo, nkeys;
+        int b, hk, h0, ncols, sp, k_lo, nkeys, ntiles;
     };
-    // work item `it` of this workgroup (it < my_items)
     auto get_item = [&](int it) {
         Item r;
-        int id;                                  // group index
-        if (p.own_groups) {
-            r.sp = it % p.nsplit;
-            id = (int)blockIdx.x + G * (it / p.nsplit);
-        } else {
-            const int item = (int)blockIdx.x + G * it;   // (group, chunk), chunk fastest
-            r.sp = item % p.nsplit;
-            id = item / p.nsplit;
-        }
+        const int item = (int)blockIdx.x + G * it;
+        r.sp = item % p.nsplit;
+        int id = item / p.nsplit;
         const int cb = id % p.ncb;
         id /= p.ncb;
         r.hk = id % p.Hkv;
         r.b = id / p.Hkv;
         r.k_lo = r.sp * p.chunk;
-        // the sequence's cache length (per sequence when given; tiles past it
-        // get empty load ranges, so they read no memory, and are masked)
-        const int len = p.seqlens ? min(max(p.seqlens[r.b], 0), p.Skv) : p.Skv;
+        // the sequence's cache length (per sequence when given)
+        // (read through the constant address space: a scalar load, outside
+        // the vector-load counter the tile waits rely on)
+        typedef const __attribute__((address_space(4))) int cint;
+        const int len = p.seqlens ? min(max(((cint *)p.seqlens)[r.b], 0), p.Skv) : p.Skv;
         r.nkeys = max(0, min(len, r.k_lo + p.chunk) - r.k_lo);
+        r.ntiles = (r.nkeys + TK - 1) / TK;
         r.ncols = min(NCOL, p.group - NCOL * cb);
         r.h0 = r.hk * p.group + NCOL * cb;
         return r;
     };
+    // this wave's tiles of an item: w, w + NWV, ...
+    auto wave_tiles = [&](const Item &it) { return wave < it.ntiles ? (it.ntiles - wave + NWV - 1) / NWV : 0; };
 
-    // Load plan: wave w issues loads w, w+4, ... of a tile (K loads first);
-    // lane L of load m of a tensor fills slot 64m + L = (row, physical chunk).
-    uint32_t goff[L::PER_WAVE];
-    int ldo[L::PER_WAVE];
+    // Load plan: load m of a tensor (m < LOADS) fills slots 64m .. 64m+63 of
+    // the tile; lane L's slot is (row, physical chunk).
+    uint32_t goff[2 * L::LOADS];
 #pragma unroll
-    for (int pp = 0; pp < L::PER_WAVE; ++pp) {
-        const int n = wave + NWV * pp;
-        const bool isv = pp >= L::PER_WAVE / 2;
-        const int m = isv ? n - L::LOADS / 2 : n;
+    for (int pp = 0; pp < 2 * L::LOADS; ++pp) {
+        const bool isv = pp >= L::LOADS;
+        const int m = isv ? pp - L::LOADS : pp;
         const int slot = 64 * m + lane;
         const int row = slot / L::CPR;
         const int lc = (slot % L::CPR) ^ (isv ? swz_v<D>(row) : swz_k<D>(row));
         goff[pp] = (uint32_t)(row * hd_k + 8 * lc) * 2u;
-        ldo[pp] = (isv ? L::T_ELEMS : 0) + 512 * m;
     }
 
-    // Load stream: tile `lt` of item `li`; `lbase` is that item's first key row.
+    // This wave's load stream: its tiles of every item, in order.  `li` is
+    // the item of the next tile, `lt` the wave's tile index within it.
     int li = 0, lt = 0, lstage = 0;
+    int lcnt = 0;                                // tiles issued so far
     Item litem = get_item(0);
-    auto issue_next = [&]() {
-        int rows = 0;
-        int64_t row0 = 0;
-        if (li < my_items) {
-            rows = min(BC, litem.nkeys - BC * lt);
-            row0 = ((int64_t)litem.b * p.Skv + litem.k_lo + BC * lt) * hd_k + (int64_t)litem.hk * D;
-        }
-        const int nbytes = rows > 0 ? (int)(((int64_t)(rows - 1) * hd_k + D) * 2) : 0;
-        const __amdgpu_buffer_rsrc_t kr = buffer_rsrc(p.k + (rows > 0 ? row0 : 0), nbytes);
-        const __amdgpu_buffer_rsrc_t vr = buffer_rsrc(p.v + (rows > 0 ? row0 : 0), nbytes);
-        __bf16 *dst = lds + lstage * L::STAGE;
-#pragma unroll
-        for (int pp = 0; pp < L::PER_WAVE; ++pp)
-            buffer_lds_dma16(pp >= L::PER_WAVE / 2 ? vr : kr, goff[pp], dst + ldo[pp]);
-        lstage = lstage == NSD - 1 ? 0 : lstage + 1;
-        if (++lt == p.nti) {
+    int lcount = my_items > 0 ? wave_tiles(litem) : 0;
+    // skip items where this wave has no tile
+    auto lskip = [&]() {
+        while (li < my_items && lt >= lcount) {
             lt = 0;
-            if (++li < my_items) litem = get_item(li);
+            if (++li < my_items) {
+                litem = get_item(li);
+                lcount = wave_tiles(litem);
+            }
         }
+    };
+    lskip();
+    auto issue_next = [&]() {
+        if (li >= my_items) return;
+        const int key0 = litem.k_lo + TK * (wave + NWV * lt);
+        const int rows = min(TK, litem.k_lo + litem.nkeys - key0);
+        const int64_t row0 = ((int64_t)litem.b * p.Skv + key0) * hd_k + (int64_t)litem.hk * D;
+        // the descriptors end at the last valid key: rows past it read zeros
+        const int nbytes = (int)(((int64_t)(rows - 1) * hd_k + D) * 2);
+        const __amdgpu_buffer_rsrc_t kr = buffer_rsrc(p.k + row0, nbytes);
+        const __amdgpu_buffer_rsrc_t vr = buffer_rsrc(p.v + row0, nbytes);
+        __bf16 *dst = ring + lstage * L::STAGE;
+#pragma unroll
+        for (int pp = 0; pp < 2 * L::LOADS; ++pp)
+            buffer_lds_dma16(pp >= L::LOADS ? vr : kr, goff[pp],
+                             dst + (pp >= L::LOADS ? L::T_ELEMS : 0) + 512 * (pp % L::LOADS));
+        lstage ^= 1;
+        ++lt;
+        ++lcnt;
+        lskip();
     };
 
-    // Query rows of an item (heads h0 .. h0+ncols-1, contiguous in memory)
-    // into the LDS query buffer; rows past ncols read as zeros.
-    auto issue_q = [&](const Item &it) {
-        const int nbytes = it.ncols * D * 2;
+    // Query rows of an item (heads h0 .. h0+ncols-1, contiguous in memory),
+    // as the B operand of S^T = K Q^T: column `col` is query head h0 + col.
+    // The descriptor covers the item's heads only, so other columns are 0.
+    auto load_q = [&](const Item &it, bf16x8 (&q)[D / 16]) {
         const __amdgpu_buffer_rsrc_t qr =
-            buffer_rsrc(p.q + ((int64_t)it.b * p.Hq + it.h0) * D, nbytes);
-#pragma unroll
-        for (int pp = 0; pp < L::Q_PER_WAVE; ++pp) {
-            const int n = min(wave + NWV * pp, L::Q_LOADS - 1);
-            buffer_lds_dma16(qr, (uint32_t)(1024 * n + 16 * lane), lds + L::Q_BASE + 512 * n);
-        }
-    };
-    // Query fragments (B operand of S^T = K Q^T) from the LDS buffer: column
-    // `col` is query head h0 + col.
-    auto read_q = [&](bf16x8 (&qf)[D / 16]) {
+            buffer_rsrc(p.q + ((int64_t)it.b * p.Hq + it.h0) * D, it.ncols * D * 2);
+        const uint32_t o0 = (uint32_t)((col * D + 8 * g) * 2);
 #pragma unroll
         for (int t = 0; t < D / 16; ++t)
-            qf[t] = ld_lds_bf16x8(lds + L::Q_BASE + col * D + 8 * g + 16 * t);
+            q[t] = __builtin_bit_cast(bf16x8, __builtin_amdgcn_raw_buffer_load_b128(qr, o0 + 32 * t, 0, 0));
     };
 
-    // Per-lane operand offsets (elements, within a stage).  K: row col (+32kb),
+    // Per-lane operand offsets (elements, within a stage).  K: row col,
     // logical chunk 2t + g.  V: the transposing read of keys 4g + e (+16kk,
-    // +8) and columns 32*wave + 16*dh + 4*s.
+    // +8) and columns 32*db + 16*dh + 4*s.
     int kof[D / 16];
 #pragma unroll
     for (int t = 0; t < D / 16; ++t) kof[t] = col * D + 8 * ((2 * t + g) ^ swz_k<D>(col));
     const int tr_e = (lane & 15) >> 2, tr_s = lane & 3, tr_dh = (lane >> 4) & 1;
-    const bool pv_wave = wave < D / 32;
-    const int vlc = 4 * (pv_wave ? wave : 0) + 2 * tr_dh + (tr_s >> 1);
-    const int vof = L::T_ELEMS + (4 * g + tr_e) * D + 8 * (vlc ^ swz_v<D>(tr_e)) + 4 * (tr_s & 1);
+    int vof[D / 32];
+#pragma unroll
+    for (int db = 0; db < D / 32; ++db) {
+        const int vlc = 4 * db + 2 * tr_dh + (tr_s >> 1);
+        vof[db] = L::T_ELEMS + (4 * g + tr_e) * D + 8 * (vlc ^ swz_v<D>(tr_e)) + 4 * (tr_s & 1);
+    }
 
-    f32x16 oacc = f32x16{};
+    f32x16 oacc[D / 32];
     float m = -__builtin_inff();
     float lsum = 0.f;
     const float c = p.c;
-    // running merge of a group's chunks (own_groups): the log-sum-exp
-    // combine, in log2 units, on normalised chunk outputs
-    f32x16 macc = f32x16{};
-    float mm = -__builtin_inff(), ml = 0.f;
+    bf16x8 qf[D / 16], qn[D / 16];
 
-    int ci = 0, ct = 0, cstage = 0;              // compute stream: item, tile, stage
-    Item citem = get_item(0);
-    bf16x8 qf[D / 16];
-    issue_q(citem);
+    // The first item's query rows, then the first two tiles of the stream:
+    // the rows are older than both tiles, so the first tile wait covers them.
+    if (my_items > 0) load_q(get_item(0), qf);
+    issue_next();
+    issue_next();
+
+    int cstage = 0;                              // stage of the tile being computed
+    int ccnt = 0;                                // tiles computed so far
+    bool stores = false;                         // output stores since the last full wait
+    for (int ci = 0; ci < my_items; ++ci) {
+        const Item it = get_item(ci);
+        const int nmine = wave_tiles(it);
+        if (ci > 0) {
 #pragma unroll
-    for (int i = 0; i < NSD - 1; ++i) issue_next();
-    // The next item's query rows are loaded at its predecessor's second tile
-    // (after the barrier that follows every wave's read of the buffer), so
-    // nti - 2 tile batches follow that load before the item starts; with
-    // fewer than NSD - 2 of them the per-step wait does not cover it, and
-    // item starts wait for every load.
-    const bool short_items = p.nti < NSD;
-
-    for (int tau = 0; tau < ntot; ++tau) {
-        // tile tau complete (the next NSD-2 may still be in flight), visible
-        // to every wave; its stage's previous tile has been consumed
-        if (ct == 0 && short_items) wait_vmcnt<0>();
-        else wait_vmcnt<(NSD - 2) * L::PER_WAVE>();
-        lds_barrier();
-        issue_next();
-        if (ct == 0) {
-            read_q(qf);
-            if (p.nti == 1 && ci + 1 < my_items) {
-                wait_lgkmcnt0();                 // this wave's copy has landed ...
-                lds_barrier();                   // ... and every other wave's
-                issue_q(get_item(ci + 1));
-            }
-        } else if (ct == 1 && ci + 1 < my_items) {
-            issue_q(get_item(ci + 1));
+            for (int t = 0; t < D / 16; ++t) qf[t] = qn[t];
         }
-        const __bf16 *st = lds + cstage * L::STAGE;
+#pragma unroll
+        for (int db = 0; db < D / 32; ++db) oacc[db] = f32x16{};
+        m = -__builtin_inff();
+        lsum = 0.f;
 
-        // S^T for the tile's two 32-key blocks
-        f32x16 s[BC / 32];
+        for (int tw = 0; tw < nmine; ++tw) {
+            // this tile complete.  Loads complete in order, so when the next
+            // tile of the stream has been issued, everything but its loads
+            // (and anything issued after it) must be done; otherwise, and
+            // after output stores (which share the counter), wait for all.
+            if (lcnt >= ccnt + 2 && !stores) wait_vmcnt<2 * L::LOADS>();
+            else wait_vmcnt<0>();
+            stores = false;
+            const __bf16 *st = ring + cstage * L::STAGE;
+
+            // S^T for the tile's 32 keys
+            f32x16 s = f32x16{};
 #pragma unroll
-        for (int kb = 0; kb < BC / 32; ++kb) s[kb] = f32x16{};
-#pragma unroll
-        for (int t = 0; t < D / 16; ++t)
-#pragma unroll
-            for (int kb = 0; kb < BC / 32; ++kb)
-                s[kb] = mfma32x32x16(ld_lds_bf16x8(st + kof[t] + 32 * kb * D), qf[t], s[kb]);
-        const int key0 = BC * ct;
-        if (key0 + BC > citem.nkeys) {
-#pragma unroll
-            for (int kb = 0; kb < BC / 32; ++kb)
+            for (int t = 0; t < D / 16; ++t) s = mfma32x32x16(ld_lds_bf16x8(st + kof[t]), qf[t], s);
+            const int kt = TK * (wave + NWV * tw);  // first key of the tile, within the item
+            if (kt + TK > it.nkeys) {
 #pragma unroll
                 for (int r = 0; r < 16; ++r)
-                    if (key0 + 32 * kb + 8 * (r >> 2) + 4 * g + (r & 3) >= citem.nkeys)
-                        s[kb][r] = -__builtin_inff();
-        }
-        // online softmax, lazy rescale (reference max moves by > kRescaleSlack)
-        float mx = -__builtin_inff();
+                    if (kt + 8 * (r >> 2) + 4 * g + (r & 3) >= it.nkeys) s[r] = -__builtin_inff();
+            }
+            // online softmax, lazy rescale (reference max moves by > kRescaleSlack)
+            float mx = -__builtin_inff();
 #pragma unroll
-        for (int kb = 0; kb < BC / 32; ++kb)
+            for (int r = 0; r < 16; ++r) mx = fmaxf(mx, s[r]);
+            const float mt = half_swap_max(mx) * c;
+            const bool raise = mt > m + kRescaleSlack;
+            if (__builtin_amdgcn_ballot_w64(raise)) {
+                const float m_new = raise ? mt : m;
+                const float alpha = m_new == -__builtin_inff() ? 1.f : fast_exp2(m - m_new);
+                lsum *= alpha;
 #pragma unroll
-            for (int r = 0; r < 16; ++r) mx = fmaxf(mx, s[kb][r]);
-        const float mt = half_swap_max(mx) * c;
-        const bool raise = mt > m + kRescaleSlack;
-        if (__builtin_amdgcn_ballot_w64(raise)) {
-            const float m_new = raise ? mt : m;
-            const float alpha = m_new == -__builtin_inff() ? 1.f : fast_exp2(m - m_new);
-            lsum *= alpha;
+                for (int db = 0; db < D / 32; ++db)
 #pragma unroll
-            for (int r = 0; r < 16; ++r) oacc[r] *= alpha;
-            m = m_new;
-        }
-        const float m_use = m == -__builtin_inff() ? 0.f : m;
-        float rs = 0.f;
-#pragma unroll
-        for (int kb = 0; kb < BC / 32; ++kb)
+                    for (int r = 0; r < 16; ++r) oacc[db][r] *= alpha;
+                m = m_new;
+            }
+            const float m_use = m == -__builtin_inff() ? 0.f : m;
+            float rs = 0.f;
 #pragma unroll
             for (int r = 0; r < 16; ++r) {
-                s[kb][r] = fast_exp2(__builtin_fmaf(s[kb][r], c, -m_use));
-                rs += s[kb][r];
+                s[r] = fast_exp2(__builtin_fmaf(s[r], c, -m_use));
+                rs += s[r];
             }
-        lsum += rs;
-        if (pv_wave) {
+            lsum += rs;
+            // O^T += V^T P^T, 16 keys at a time, all D columns
 #pragma unroll
-            for (int kk = 0; kk < BC / 16; ++kk) {
-                const bf16x8 pk = pack_p8(s[kk >> 1], 8 * (kk & 1));
-                const s16x4 lo = lds_read_tr(st + vof + 16 * kk * D);
-                const s16x4 hi = lds_read_tr(st + vof + (16 * kk + 8) * D);
-                oacc = mfma32x32x16(concat_tr(lo, hi), pk, oacc);
+            for (int kk = 0; kk < TK / 16; ++kk) {
+                const bf16x8 pk = pack_p8(s, 8 * kk);
+#pragma unroll
+                for (int db = 0; db < D / 32; ++db) {
+                    const s16x4 lo = lds_read_tr(st + vof[db] + 16 * kk * D);
+                    const s16x4 hi = lds_read_tr(st + vof[db] + (16 * kk + 8) * D);
+                    oacc[db] = mfma32x32x16(concat_tr(lo, hi), pk, oacc[db]);
+                }
             }
+            // the next item's query rows, ahead of this wave's next tile load
+            if (tw == nmine - 1 && ci + 1 < my_items) load_q(get_item(ci + 1), qn);
+            // this stage is consumed: refill it with the tile after next
+            issue_next();
+            cstage ^= 1;
+            ++ccnt;
         }
+        if (nmine == 0 && ci + 1 < my_items) load_q(get_item(ci + 1), qn);
 
-        if (ct == p.nti - 1 && p.own_groups) {
-            // chunk done: fold (O_s = acc / l, lse_s = m + log2 l) into the
-            // group's merge; the last chunk writes the result
-            const float lt2 = half_swap_sum(lsum);
-            const float inv = lt2 > 0.f ? 1.f / lt2 : 0.f;
-            const float ls2 = lt2 > 0.f ? m + fast_log2(lt2) : -__builtin_inff();
-            if (ls2 != -__builtin_inff()) {
-                const float mn = fmaxf(mm, ls2);
-                const float a = mm == -__builtin_inff() ? 0.f : fast_exp2(mm - mn);
-                const float w = fast_exp2(ls2 - mn) * inv;
+        // Merge of the four waves' states: per query column, the waves'
+        // log-sum-exp values give each wave's weight; the weighted outputs
+        // are then summed in a fixed wave order through LDS.
+        const float lt2 = half_swap_sum(lsum);
+        const float lse2 = lt2 > 0.f ? m + fast_log2(lt2) : -__builtin_inff();   // log2 units
+        if (g == 0) merge_l[wave * NCOL + col] = lse2;
+        wait_lgkmcnt0();
+        lds_barrier();
+        float M = -__builtin_inff();
 #pragma unroll
-                for (int r = 0; r < 16; ++r) macc[r] = macc[r] * a + oacc[r] * w;
-                ml = ml * a + fast_exp2(ls2 - mn);
-                mm = mn;
-            }
-            if (citem.sp == p.nsplit - 1) {
-                const float inv2 = ml > 0.f ? 1.f / ml : 0.f;
-                const int h = citem.h0 + col;
-                if (col < citem.ncols) {
-                    if (pv_wave) {
-                        __bf16 *op = p.o + ((int64_t)citem.b * p.Hq + h) * D + 32 * wave + 4 * g;
+        for (int w = 0; w < NWV; ++w) M = fmaxf(M, merge_l[w * NCOL + col]);
+        float wsum = 0.f;
 #pragma unroll
-                        for (int rq = 0; rq < 4; ++rq)
-                            *reinterpret_cast<bf16x4 *>(op + 8 * rq) =
-                                to_bf16x4(macc[4 * rq] * inv2, macc[4 * rq + 1] * inv2,
-                                          macc[4 * rq + 2] * inv2, macc[4 * rq + 3] * inv2);
-                    }
-                    if (wave == 0 && g == 0 && p.lse != nullptr)
-                        p.lse[(int64_t)citem.b * p.Hq + h] =
-                            ml > 0.f ? (mm + fast_log2(ml)) * kLn2 : -__builtin_inff();
-                }
-                macc = f32x16{};
-                mm = -__builtin_inff();
-                ml = 0.f;
-            }
-            oacc = f32x16{};
-            m = -__builtin_inff();
-            lsum = 0.f;
-            ct = 0;
-            if (++ci < my_items) citem = get_item(ci);
-        } else if (ct == p.nti - 1) {
-            // item done: O = acc / l, LSE = (m + log2 l) ln 2
-            const float lt2 = half_swap_sum(lsum);
-            const float inv = lt2 > 0.f ? 1.f / lt2 : 0.f;
-            const float lse_nat = lt2 > 0.f ? (m + fast_log2(lt2)) * kLn2 : -__builtin_inff();
-            const int h = citem.h0 + col;
-            if (col < citem.ncols) {
-                if (pv_wave) {
-                    const int dbase = 32 * wave + 4 * g;
-                    if (p.nsplit == 1) {
-                        __bf16 *op = p.o + ((int64_t)citem.b * p.Hq + h) * D + dbase;
-#pragma unroll
-                        for (int rq = 0; rq < 4; ++rq)
-                            *reinterpret_cast<bf16x4 *>(op + 8 * rq) =
-                                to_bf16x4(oacc[4 * rq] * inv, oacc[4 * rq + 1] * inv,
-                                          oacc[4 * rq + 2] * inv, oacc[4 * rq + 3] * inv);
-                    } else {
-                        float *op = p.ws_o + (((int64_t)citem.sp * p.B + citem.b) * p.Hq + h) * D + dbase;
-#pragma unroll
-                        for (int rq = 0; rq < 4; ++rq) {
-                            f32x4 v4 = {oacc[4 * rq] * inv, oacc[4 * rq + 1] * inv,
-                                        oacc[4 * rq + 2] * inv, oacc[4 * rq + 3] * inv};
-                            *reinterpret_cast<f32x4 *>(op + 8 * rq) = v4;
-                        }
-                    }
-                }
-                if (wave == 0 && g == 0) {
-                    if (p.nsplit == 1) {
-                        if (p.lse != nullptr) p.lse[(int64_t)citem.b * p.Hq + h] = lse_nat;
-                    } else {
-                        p.ws_lse[((int64_t)citem.sp * p.B + citem.b) * p.Hq + h] = lse_nat;
-                    }
-                }
-            }
-            oacc = f32x16{};
-            m = -__builtin_inff();
-            lsum = 0.f;
-            ct = 0;
-            if (++ci < my_items) citem = get_item(ci);
-        } else {
-            ++ct;
+        for (int w = 0; w < NWV; ++w) {
+            const float lw = merge_l[w * NCOL + col];
+            wsum += lw == -__builtin_inff() ? 0.f : fast_exp2(lw - M);
         }
-        cstage = cstage == NSD - 1 ? 0 : cstage + 1;
+        // weight of this wave's normalised output, times 1 / l for the
+        // normalisation: exp2(lse2 - M) / wsum / l = exp2(m - M) / wsum
+        const float f = lt2 > 0.f ? fast_exp2(m - M) / wsum : 0.f;
+#pragma unroll
+        for (int db = 0; db < D / 32; ++db)
+#pragma unroll
+            for (int r = 0; r < 16; ++r) oacc[db][r] *= f;
+        // merge_o holds O^T in the accumulator layout: element (db, r) of
+        // lane L at index ((db * 16 + r) * 64 + L), so reads and writes are
+        // contiguous per register
+#pragma unroll
+        for (int w = 0; w < NWV; ++w) {
+            if (wave == w) {
+                if (w > 0) {
+#pragma unroll
+                    for (int db = 0; db < D / 32; ++db)
+#pragma unroll
+                        for (int r = 0; r < 16; ++r) oacc[db][r] += merge_o[(db * 16 + r) * 64 + lane];
+                }
+                if (w < NWV - 1) {
+#pragma unroll
+                    for (int db = 0; db < D / 32; ++db)
+#pragma unroll
+                        for (int r = 0; r < 16; ++r) merge_o[(db * 16 + r) * 64 + lane] = oacc[db][r];
+                }
+            }
+            if (w < NWV - 1) {
+                wait_lgkmcnt0();
+                lds_barrier();
+            }
+        }
+        if (wave == NWV - 1) stores = true;
+        if (wave == NWV - 1 && col < it.ncols) {
+            const int h = it.h0 + col;
+            const float lse_nat = M == -__builtin_inff() ? -__builtin_inff() : (M + fast_log2(wsum)) * kLn2;
+            if (p.nsplit == 1) {
+                __bf16 *op = p.o + ((int64_t)it.b * p.Hq + h) * D + 4 * g;
+#pragma unroll
+                for (int db = 0; db < D / 32; ++db)
+#pragma unroll
+                    for (int rq = 0; rq < 4; ++rq)
+                        *reinterpret_cast<bf16x4 *>(op + 32 * db + 8 * rq) =
+                            to_bf16x4(oacc[db][4 * rq], oacc[db][4 * rq + 1], oacc[db][4 * rq + 2],
+                                      oacc[db][4 * rq + 3]);
+                if (g == 0 && p.lse != nullptr) p.lse[(int64_t)it.b * p.Hq + h] = lse_nat;
+            } else {
+                float *op = p.ws_o + (((int64_t)it.sp * p.B + it.b) * p.Hq + h) * D + 4 * g;
+#pragma unroll
+                for (int db = 0; db < D / 32; ++db)
+#pragma unroll
+                    for (int rq = 0; rq < 4; ++rq) {
+                        const f32x4 v4 = {oacc[db][4 * rq], oacc[db][4 * rq + 1], oacc[db][4 * rq + 2],
+                                          oacc[db][4 * rq + 3]};
+                        *reinterpret_cast<f32x4 *>(op + 32 * db + 8 * rq) = v4;
+                    }
+                if (g == 0) p.ws_lse[((int64_t)it.sp * p.B + it.b) * p.Hq + h] = lse_nat;
+            }
+        }
     }
     wait_vmcnt<0>();                 // no load may outlive the workgroup
 }
 
-// Merge of the chunk partials: one 64-thread workgroup per (sequence, query
-// head); LSE = M + log(sum_s exp(lse_s - M)), O = sum_s exp(lse_s - LSE) O_s.
+// Merge of the key-range partials: one 64-thread workgroup per (sequence,
+// query head); LSE = M + log(sum_s exp(lse_s - M)), O = sum_s exp(lse_s - LSE) O_s.
 template <int D>
 __global__ __launch_bounds__(64) void attn_decode_combine_kernel(DecParams p) {
     const int bh = blockIdx.x;                      // b * Hq + h
@@ -406,37 +399,29 @@ __global__ __launch_bounds__(64) void attn_decode_combine_kernel(DecParams p) {
     if (p.lse != nullptr && t == 0) p.lse[bh] = lse;
 }
 
-// Tile size, ring depth and workgroups per CU of the split kernel.
-#ifndef DEC_BC
-#define DEC_BC 64
-#endif
-#ifndef DEC_NS
-#define DEC_NS 4
-#endif
-#ifndef DEC_WPC
-#define DEC_WPC 1
-#endif
-
 template <int D>
 hipError_t launch_t(DecParams p, hipStream_t s) {
-    constexpr int BC = DEC_BC;
-    const int64_t items = (int64_t)p.B * p.Hkv * p.ncb * p.nsplit;
-    if (items > 0x7fffffff) return hipErrorInvalidConfiguration;
     int cus = 0;
     hipError_t e = current_cu_count(&cus);
     if (e != hipSuccess) return e;
-    p.nti = (p.chunk + BC - 1) / BC;
-    const int64_t want = (int64_t)cus * DEC_WPC;
-    // whole groups per workgroup when they spread evenly (at most 10 % idle)
+    // When the (sequence, KV head, head block) groups spread evenly over the
+    // CUs (at most 10 % idle), each workgroup takes whole sequences: its
+    // four waves split the keys and merge them, and the result goes out
+    // directly.  Otherwise the key ranges of a sequence spread over the
+    // workgroups and a second kernel merges their partials.
     const int64_t groups = (int64_t)p.B * p.Hkv * p.ncb;
-    const int64_t rounds = (groups + want - 1) / want;
-    p.own_groups = p.nsplit > 1 && groups >= want && rounds * want * 10 <= groups * 11;
-    const int64_t units = p.own_groups ? groups : items;
-    const int blocks = (int)(units < want ? units : want);
-    hipLaunchKernelGGL((attn_decode_split_kernel<D, BC, DEC_NS>), dim3((unsigned)blocks), dim3(NT), 0,
-                       s, p);
+    const int64_t rounds = (groups + cus - 1) / cus;
+    if (p.nsplit > 1 && groups >= cus && rounds * cus * 10 <= groups * 11) {
+        p.nsplit = 1;
+        p.chunk = p.Skv;
+    }
+    const int64_t items = groups * p.nsplit;
+    if (items > 0x7fffffff) return hipErrorInvalidConfiguration;
+    const int blocks = (int)(items < cus ? items : cus);
+    if (blocks <= 0) return hipSuccess;
+    hipLaunchKernelGGL((attn_decode_split_kernel<D>), dim3((unsigned)blocks), dim3(NT), 0, s, p);
     e = hipGetLastError();
-    if (e != hipSuccess || p.nsplit == 1 || p.own_groups) return e;
+    if (e != hipSuccess || p.nsplit == 1) return e;
     hipLaunchKernelGGL(attn_decode_combine_kernel<D>, dim3((unsigned)(p.B * p.Hq)), dim3(64), 0,
                        s, p);
     return hipGetLastError();

@@ -76,8 +76,6 @@ struct DecParams {
     int B, Hq, Hkv, group, Skv;
     int ncb;                 // blocks of <= 32 query heads per KV head
     int nsplit, chunk;       // key chunks and keys per chunk
-    int nti;                 // tiles per chunk (set by the launcher)
-    int own_groups;          // a workgroup merges all chunks of its groups (set by the launcher)
     float c;                 // scale * log2(e)
 };
 
