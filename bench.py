@@ -349,9 +349,9 @@ def main():
             "roofline": {"bound": "hbm", "achieved": round(gbs, 1), "peak": PEAK_HBM_GBS,
                          "unit": "GB/s", "frac": round(gbs / PEAK_HBM_GBS, 4),
                          "traffic": load_traffic("decode"),
-                         "kernel": "attn_decode_split_kernel<128, 64, 4> (chunks merged in the "
-                                   "kernel; the separate combine kernel runs only when the "
-                                   "groups do not fill the GPU)"},
+                         "kernel": "attn_decode_split_kernel<128> (whole sequences per "
+                                   "workgroup, waves merged in the kernel; the combine kernel "
+                                   "runs only when the groups do not fill the GPU)"},
         },
         "kernel_hash": kernel_hash(),
     }
