@@ -444,9 +444,9 @@ void attn_fwd_kernel(FwdParams p) {
     // no-op (the loop below is unrolled by two).
     auto step = [&](int j, f32x16 (&scur)[BC / 32], f32x16 (&snext)[BC / 32]) {
         if (j >= nt) return;
-        // tile cn+1 complete (cn+2 and any later query rows may still be in
-        // flight; loads complete in order); after output stores wait for
-        // everything, since stores and loads share the counter
+        // tile cn+1 complete (the query rows and tile cn+2 issued after it
+        // may still be in flight; loads complete in order); after output
+        // stores wait for everything, since stores and loads share the counter
         if (stores) wait_vmcnt<0>();
         else if (q_pend) wait_vmcnt<L::PER_WAVE + D / 16>();
         else wait_vmcnt<L::PER_WAVE>();
@@ -494,13 +494,16 @@ void attn_fwd_kernel(FwdParams p) {
                     snext[kb] = __builtin_nondeterministic_value(snext[kb]);
             }
         }
+        // one load point for both paths (a load in each branch would be
+        // merged by register copies that wait for the load at once).  It
+        // comes before the tile load below: the compiler's wait for qf in the
+        // next step then counts the tile loads as younger and lets them fly
+        // (issued after them, it made every step wait for the newest tile).
+        if (r_last != -2) prefetch_q(r_last);
         // the next tile of the stream goes into the stage of tile cn-1 (every
         // wave is past its last read, at the barrier above); issued after
         // the compute so that the MFMAs start right after the barrier
         issue_next();
-        // one load point for both paths (a load in each branch would be
-        // merged by register copies that wait for the load at once)
-        if (r_last != -2) prefetch_q(r_last);
         ++cn;
     };
 
@@ -605,7 +608,14 @@ void attn_fwd_kernel(FwdParams p) {
 #pragma unroll
             for (int kb = 0; kb < BC / 32; ++kb) sa[kb] = __builtin_nondeterministic_value(sa[kb]);
         }
-        if (nt == 1) prefetch_q(rA);
+        if (nt == 1) {
+            // the first step is already the item's last: it needs the next
+            // item's rows.  Here no tile load follows them, so wait for them
+            // at once (this path only; elsewhere tile loads follow the rows,
+            // and the compiler's waits for qf then let those tiles fly)
+            prefetch_q(rA);
+            wait_vmcnt<0>();
+        }
     }
     while (rA >= 0) {
 #pragma unroll
