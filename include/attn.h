@@ -112,7 +112,8 @@ attn_status_t attn_varlen_check(const int *cu_seqlens_host, int nseq, int total,
  *   q, o : [B, Hq, d] bf16      k_cache, v_cache : [B, Skv, Hkv, d] bf16
  *   lse  : [B, Hq] fp32 (or NULL)
  * The query is the newest position, so all Skv cached keys are attended.
- * The cache is cut into num_splits chunks of ceil(Skv / num_splits) keys; a
+ * The cache is cut into num_splits chunks of ceil(Skv / num_splits) keys,
+ * rounded up to a multiple of 32 (trailing chunks may then be empty); a
  * normalised partial output and its log-sum-exp are computed per (sequence,
  * KV head, chunk) -- every query head of a KV group shares one pass over that
  * chunk of K and V -- and the chunks are merged:
@@ -151,6 +152,37 @@ attn_status_t attn_decode_varlen(const void *q, const void *k_cache, const void 
                                  void *o, float *lse, const int *seqlens_k, int B, int Hq,
                                  int Hkv, int Skv_max, int d, float scale, int num_splits,
                                  void *workspace, size_t workspace_bytes, hipStream_t stream);
+
+/*
+ * Decode against a paged KV cache (blocks of page_size keys drawn from a
+ * shared pool, as a serving system allocates them).
+ *   k_pages, v_pages : [num_pages, page_size, Hkv, d] bf16 (DEVICE)
+ *   block_table      : DEVICE int32 [B, max_pages_per_seq]; key j of sequence
+ *                      b is row j % page_size of page
+ *                      block_table[b * max_pages_per_seq + j / page_size]
+ *   seqlens_k        : DEVICE int32 [B], keys per sequence, clamped on the
+ *                      device to [0, max_pages_per_seq * page_size]
+ *   q, o, lse, scale, num_splits, workspace: as attn_decode, with the cache
+ *   capacity Skv = max_pages_per_seq * page_size (use that value for
+ *   attn_decode_workspace_bytes / attn_decode_pick_splits).
+ * page_size must be a positive multiple of 16.  Only table entries that
+ * hold keys below a sequence's length are read; a page id outside
+ * [0, num_pages) is read as zeros (no memory outside the pool is touched)
+ * and the result for that sequence is then meaningless.  block_table and
+ * seqlens_k are read by the kernels only (the host never reads them).
+ * Returns ATTN_ERR_NULLPTR for a NULL table or lengths, ATTN_ERR_SHAPE for a
+ * page size that is not a multiple of 16 or non-positive counts, and the
+ * errors of attn_decode otherwise.  The per-sequence cache of the serving
+ * note in lecompute.fr, "Flapping Airplanes, ThunderKittens and
+ * megakernels", section "A benchmark that could test the broader promise",
+ * stored in fixed-size pages.
+ */
+attn_status_t attn_decode_paged(const void *q, const void *k_pages, const void *v_pages,
+                                void *o, float *lse, const int *block_table,
+                                const int *seqlens_k, int B, int Hq, int Hkv, int d,
+                                int page_size, int max_pages_per_seq, int num_pages, float scale,
+                                int num_splits, void *workspace, size_t workspace_bytes,
+                                hipStream_t stream);
 
 /* Bytes of decode workspace for these sizes (0 when num_splits resolves to
  * 1; num_splits <= 0 means the library's choice, as in attn_decode).  Returns

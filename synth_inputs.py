@@ -101,6 +101,30 @@ def make_decode(seed, B, Hq, Hkv, Skv, d):
     return dict(q=f32_to_bf16_bits(q), k=f32_to_bf16_bits(k), v=f32_to_bf16_bits(v))
 
 
+def make_paged(seed, B, Hq, Hkv, d, page_size, max_pages, num_pages):
+    """A paged KV cache: q [B,Hq,d], k/v pages [num_pages,page_size,Hkv,d]
+    (bf16 bit patterns) and an int32 block table [B,max_pages] of distinct
+    page ids in random order (needs num_pages >= B*max_pages).  ``gather``
+    turns it back into a dense [B, max_pages*page_size, Hkv, d] cache.
+    """
+    if num_pages < B * max_pages:
+        raise ValueError("the pool must hold every table entry")
+    rng = np.random.default_rng(seed)
+    q = rng.standard_normal((B, Hq, d), dtype=np.float32)
+    k = rng.standard_normal((num_pages, page_size, Hkv, d), dtype=np.float32)
+    v = rng.standard_normal((num_pages, page_size, Hkv, d), dtype=np.float32)
+    table = rng.permutation(num_pages)[:B * max_pages].reshape(B, max_pages).astype(np.int32)
+    return dict(q=f32_to_bf16_bits(q), k_pages=f32_to_bf16_bits(k),
+                v_pages=f32_to_bf16_bits(v), block_table=table)
+
+
+def gather_pages(pages, table):
+    """Dense [B, max_pages*page_size, H, d] view of paged storage (indexing only)."""
+    B, max_pages = table.shape
+    out = pages[table.reshape(-1)]                       # [B*max_pages, page, H, d]
+    return out.reshape(B, max_pages * pages.shape[1], pages.shape[2], pages.shape[3])
+
+
 def make_varlen(seed, nseq, lo, hi, H, d, Hkv=None, lengths=None):
     """Packed ragged batch: q/k/v [total,H,d] and int32 cu_seqlens [nseq+1].
 

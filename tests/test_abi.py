@@ -33,7 +33,7 @@ def lib():
 
 def test_library_exports_every_declared_symbol(lib):
     names = declared_functions()
-    assert len(names) == 8, names
+    assert len(names) == 9, names
     raw = ctypes.CDLL(_lib.LIB_PATH)
     for n in names:
         assert hasattr(raw, n), n
@@ -149,6 +149,28 @@ def test_decode_varlen_validation(lib):
     assert decode_varlen(lib, Hq=6, Hkv=4) == GQA
     assert decode_varlen(lib, scale=0.0) == SCALE
     assert decode_varlen(lib, ws=None) == WS
+
+
+def decode_paged(lib, table=P, seqlens=P, B=2, Hq=8, Hkv=2, d=128, page=16, maxp=8, npages=32,
+                 scale=0.1, splits=4, ws=P, wsb=1 << 30, q=P):
+    return lib.attn_decode_paged(q, P, P, P, None, table, seqlens, B, Hq, Hkv, d, page, maxp,
+                                 npages, scale, splits, ws, wsb, None)
+
+
+def test_decode_paged_validation(lib):
+    assert decode_paged(lib, table=None) == NULLPTR
+    assert decode_paged(lib, seqlens=None) == NULLPTR
+    assert decode_paged(lib, q=None) == NULLPTR
+    assert decode_paged(lib, table=P + 2) == ALIGN
+    assert decode_paged(lib, seqlens=P + 1) == ALIGN
+    for page in (0, 8, 24, -16):                 # not a positive multiple of 16
+        assert decode_paged(lib, page=page) == SHAPE
+    assert decode_paged(lib, maxp=0) == SHAPE
+    assert decode_paged(lib, npages=0) == SHAPE
+    assert decode_paged(lib, d=96) == BAD_D
+    assert decode_paged(lib, Hq=6, Hkv=4) == GQA
+    assert decode_paged(lib, scale=float("inf")) == SCALE
+    assert decode_paged(lib, ws=None) == WS
 
 
 def test_decode_split_choice(lib):

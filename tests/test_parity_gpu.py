@@ -210,6 +210,60 @@ def test_decode_varlen_full_lengths_equal_decode(api, dev):
         assert torch.equal(l1, l2)
 
 
+DECODE_PAGED = [  # B, Hq, Hkv, d, page_size, max_pages, splits, lengths (None: random)
+    (4, 8, 2, 128, 16, 40, 4, [640, 1, 0, 333]),     # 16-key pages: a tile spans two pages
+    (3, 16, 4, 128, 32, 10, 1, [320, 31, 200]),
+    (5, 8, 8, 64, 64, 6, 0, None),
+    (2, 32, 4, 128, 256, 4, 3, [1024, 700]),
+    (64, 8, 2, 128, 128, 4, 8, None),                 # groups fill the GPU: whole sequences
+    (3, 4, 1, 128, 48, 7, 2, [336, 47, 100]),         # page size a multiple of 16, not of 32
+]
+
+
+@pytest.mark.parametrize("case", DECODE_PAGED,
+                         ids=lambda c: "B%d_Hq%d_Hkv%d_d%d_page%d_x%d_s%d" % c[:7])
+def test_decode_paged_matches_oracle(api, dev, case):
+    """Paged cache with shuffled pages: same as the oracle on the gathered cache."""
+    import torch
+    B, Hq, Hkv, d, page, maxp, splits, lengths = case
+    cap = page * maxp
+    data = si.make_paged(77 + page + B, B, Hq, Hkv, d, page, maxp, B * maxp + 3)
+    if lengths is None:
+        lengths = np.random.default_rng(B + page).integers(0, cap + 1, B)
+    lengths = np.asarray(lengths, dtype=np.int32)
+    scale = si.default_scale(d)
+    q = to_dev(data["q"], dev)
+    kp, vp = to_dev(data["k_pages"], dev), to_dev(data["v_pages"], dev)
+    table = torch.from_numpy(data["block_table"]).to(dev)
+    seq = torch.from_numpy(lengths).to(dev)
+    print("paged decode case", case[:7], flush=True)
+    o, lse = api.attn_decode_paged(q, kp, vp, table, seq, scale=scale, num_splits=splits)
+    torch.cuda.synchronize()
+    dense = dict(q=data["q"], k=si.gather_pages(data["k_pages"], data["block_table"]),
+                 v=si.gather_pages(data["v_pages"], data["block_table"]))
+    o_ref, lse_ref = _decode_varlen_ref(dense, np.clip(lengths, 0, cap), scale)
+    assert_close(bf16_to_np(o), o_ref, f32_to_np(lse), lse_ref, str(case[:7]))
+
+
+def test_decode_paged_identity_table_equals_varlen(api, dev):
+    """Pages laid out in order (page id = b * max_pages + i): the same bits as
+    decode over the equivalent dense cache."""
+    import torch
+    B, Hq, Hkv, d, page, maxp = 6, 16, 4, 128, 64, 8
+    data = si.make_decode(43, B, Hq, Hkv, page * maxp, d)
+    lengths = torch.tensor([512, 1, 0, 300, 64, 129], dtype=torch.int32, device=dev)
+    q, k, v = (to_dev(data[x], dev) for x in "qkv")
+    kp = k.reshape(B * maxp, page, Hkv, d)
+    vp = v.reshape(B * maxp, page, Hkv, d)
+    table = torch.arange(B * maxp, dtype=torch.int32, device=dev).reshape(B, maxp)
+    for splits in (1, 4):
+        o1, l1 = api.attn_decode_varlen(q, k, v, lengths, num_splits=splits)
+        o2, l2 = api.attn_decode_paged(q, kp, vp, table, lengths, num_splits=splits)
+        torch.cuda.synchronize()
+        assert torch.equal(o1.view(torch.int16), o2.view(torch.int16))
+        assert torch.equal(l1, l2)
+
+
 def test_decode_split_counts_agree(api, dev):
     """1, 2, 8, 64 chunks and the library's choice agree closely (fp32 merge)."""
     import torch

@@ -178,6 +178,47 @@ def attn_decode_varlen(q, k_cache, v_cache, seqlens_k, o=None, lse=None, scale=N
                    want_lse, stream)
 
 
+def attn_decode_paged(q, k_pages, v_pages, block_table, seqlens_k, o=None, lse=None, scale=None,
+                      num_splits=0, workspace=None, want_lse=True, stream=None):
+    """Decode against a paged KV cache; returns ``(o, lse)``.
+
+    q ``[B,Hq,d]`` bf16; k_pages/v_pages ``[num_pages,page_size,Hkv,d]`` bf16;
+    block_table int32 GPU ``[B,max_pages_per_seq]`` (page ids); seqlens_k
+    int32 GPU ``[B]``.  Key j of sequence b is row ``j % page_size`` of page
+    ``block_table[b, j // page_size]``.
+    """
+    _need(q, "q", torch.bfloat16, 3)
+    _need(k_pages, "k_pages", torch.bfloat16, 4)
+    _need(v_pages, "v_pages", torch.bfloat16, 4)
+    _need(block_table, "block_table", torch.int32, 2)
+    _need(seqlens_k, "seqlens_k", torch.int32, 1)
+    B, Hq, d = q.shape
+    num_pages, page_size, Hkv = k_pages.shape[0], k_pages.shape[1], k_pages.shape[2]
+    if tuple(v_pages.shape) != tuple(k_pages.shape) or k_pages.shape[3] != d:
+        raise ValueError("shape mismatch")
+    if block_table.shape[0] != B or seqlens_k.shape[0] != B:
+        raise ValueError("block_table and seqlens_k must have one row per sequence")
+    max_pages = block_table.shape[1]
+    if o is None:
+        o = torch.empty_like(q)
+    _need(o, "o", torch.bfloat16, 3)
+    if lse is None and want_lse:
+        lse = torch.empty((B, Hq), dtype=torch.float32, device=q.device)
+    if lse is not None:
+        _need(lse, "lse", torch.float32, 2)
+    nbytes = attn_decode_workspace_bytes(B, Hq, Hkv, max_pages * page_size, d, num_splits)
+    if workspace is None and nbytes > 0:
+        workspace = torch.empty(nbytes, dtype=torch.uint8, device=q.device)
+    ws_bytes = 0 if workspace is None else workspace.numel() * workspace.element_size()
+    st = _lib.load().attn_decode_paged(_ptr(q), _ptr(k_pages), _ptr(v_pages), _ptr(o), _ptr(lse),
+                                       _ptr(block_table), _ptr(seqlens_k), B, Hq, Hkv, d,
+                                       page_size, max_pages, num_pages, _scale(scale, d),
+                                       int(num_splits), _ptr(workspace), ws_bytes,
+                                       _stream(stream))
+    _check(st, "attn_decode_paged")
+    return o, lse
+
+
 def _decode(q, k_cache, v_cache, seqlens_k, o, lse, scale, num_splits, workspace, want_lse,
             stream):
     _need(q, "q", torch.bfloat16, 3)

@@ -39,7 +39,10 @@ int pick_splits(int B, int Hq, int Hkv, int Skv) {
 DecodeShape decode_shape(int B, int Hq, int Hkv, int Skv, int num_splits) {
     DecodeShape sh;
     sh.nsplit = num_splits > 0 ? num_splits : pick_splits(B, Hq, Hkv, Skv);
-    sh.chunk = ceil_div(Skv, sh.nsplit);
+    // chunks start on 32-key boundaries, so a kernel tile (32 keys, read as
+    // two 16-key halves) never straddles a 16-key boundary -- in a paged
+    // cache, never a page boundary; trailing chunks may be empty
+    sh.chunk = ceil_div(ceil_div(Skv, sh.nsplit), 32) * 32;
     sh.ncb = ceil_div(Hq / Hkv, attn::kDecCols);
     return sh;
 }
@@ -174,10 +177,15 @@ size_t attn_decode_workspace_bytes(int B, int Hq, int Hkv, int Skv, int d, int n
 
 namespace {
 
+struct PagedCache {
+    const int *block_table;
+    int page_size, max_pages, num_pages;
+};
+
 attn_status_t decode_impl(const void *q, const void *k_cache, const void *v_cache, void *o,
                           float *lse, const int *seqlens, int B, int Hq, int Hkv, int Skv, int d,
                           float scale, int num_splits, void *workspace, size_t workspace_bytes,
-                          hipStream_t stream) {
+                          hipStream_t stream, const PagedCache *paged = nullptr) {
     if (!q || !k_cache || !v_cache || !o) return ATTN_ERR_NULLPTR;
     if (!decode_sizes_ok(B, Hq, Hkv, Skv, d)) return ATTN_ERR_SHAPE;
     if (!d_ok(d)) return ATTN_ERR_UNSUPPORTED_D;
@@ -201,6 +209,12 @@ attn_status_t decode_impl(const void *q, const void *k_cache, const void *v_cach
     p.o = (__bf16 *)o;
     p.lse = lse;
     p.seqlens = seqlens;
+    if (paged != nullptr) {
+        p.block_table = paged->block_table;
+        p.page_size = paged->page_size;
+        p.max_pages = paged->max_pages;
+        p.num_pages = paged->num_pages;
+    }
     if (need > 0) {
         p.ws_o = (float *)workspace;
         p.ws_lse = p.ws_o + (size_t)sh.nsplit * B * Hq * d;
@@ -237,6 +251,28 @@ attn_status_t attn_decode_varlen(const void *q, const void *k_cache, const void 
     if (!aligned(seqlens_k, 4)) return ATTN_ERR_ALIGNMENT;
     return decode_impl(q, k_cache, v_cache, o, lse, seqlens_k, B, Hq, Hkv, Skv_max, d, scale,
                        num_splits, workspace, workspace_bytes, stream);
+}
+
+attn_status_t attn_decode_paged(const void *q, const void *k_pages, const void *v_pages,
+                                void *o, float *lse, const int *block_table,
+                                const int *seqlens_k, int B, int Hq, int Hkv, int d,
+                                int page_size, int max_pages_per_seq, int num_pages, float scale,
+                                int num_splits, void *workspace, size_t workspace_bytes,
+                                hipStream_t stream) {
+    if (!block_table || !seqlens_k) return ATTN_ERR_NULLPTR;
+    if (page_size < 16 || page_size % 16 || max_pages_per_seq < 1 || num_pages < 1)
+        return ATTN_ERR_SHAPE;
+    if ((int64_t)max_pages_per_seq * page_size > 0x7fffffff ||
+        (int64_t)num_pages * page_size * Hkv * d > kMaxElems ||
+        (int64_t)B * max_pages_per_seq > 0x7fffffff)
+        return ATTN_ERR_SHAPE;
+    if (!aligned(block_table, 4) || !aligned(seqlens_k, 4)) return ATTN_ERR_ALIGNMENT;
+    const PagedCache pc{block_table, page_size, max_pages_per_seq, num_pages};
+    // each sequence can hold max_pages_per_seq * page_size keys; the
+    // checks and key chunking below treat that as the cache capacity
+    return decode_impl(q, k_pages, v_pages, o, lse, seqlens_k, B, Hq, Hkv,
+                       max_pages_per_seq * page_size, d, scale, num_splits, workspace,
+                       workspace_bytes, stream, &pc);
 }
 
 }  // extern "C"

@@ -124,7 +124,11 @@ void attn_decode_split_kernel(DecParams p) {
     auto wave_tiles = [&](const Item &it) { return wave < it.ntiles ? (it.ntiles - wave + NWV - 1) / NWV : 0; };
 
     // Load plan: load m of a tensor (m < LOADS) fills slots 64m .. 64m+63 of
-    // the tile; lane L's slot is (row, physical chunk).
+    // the tile; lane L's slot is (row, physical chunk).  A tile is read as
+    // two halves of 16 keys, each through its own buffer descriptor (in a
+    // paged cache the halves may sit in different pages); a load never
+    // straddles the halves, and its offset is relative to its half.
+    static_assert((TK / 2) % (512 / D) == 0, "a load must stay within a half tile");
     uint32_t goff[2 * L::LOADS];
 #pragma unroll
     for (int pp = 0; pp < 2 * L::LOADS; ++pp) {
@@ -133,7 +137,7 @@ void attn_decode_split_kernel(DecParams p) {
         const int slot = 64 * m + lane;
         const int row = slot / L::CPR;
         const int lc = (slot % L::CPR) ^ (isv ? swz_v<D>(row) : swz_k<D>(row));
-        goff[pp] = (uint32_t)(row * hd_k + 8 * lc) * 2u;
+        goff[pp] = (uint32_t)((row % (TK / 2)) * hd_k + 8 * lc) * 2u;
     }
 
     // This wave's load stream: its tiles of every item, in order.  `li` is
@@ -157,16 +161,37 @@ void attn_decode_split_kernel(DecParams p) {
         if (li >= my_items) return;
         const int key0 = litem.k_lo + TK * (wave + NWV * lt);
         const int rows = min(TK, litem.k_lo + litem.nkeys - key0);
-        const int64_t row0 = ((int64_t)litem.b * p.Skv + key0) * hd_k + (int64_t)litem.hk * D;
-        // the descriptors end at the last valid key: rows past it read zeros
-        const int nbytes = (int)(((int64_t)(rows - 1) * hd_k + D) * 2);
-        const __amdgpu_buffer_rsrc_t kr = buffer_rsrc(p.k + row0, nbytes);
-        const __amdgpu_buffer_rsrc_t vr = buffer_rsrc(p.v + row0, nbytes);
+        __amdgpu_buffer_rsrc_t kr[2], vr[2];
+#pragma unroll
+        for (int h = 0; h < 2; ++h) {
+            const int rh = min(max(rows - h * (TK / 2), 0), TK / 2);   // valid rows of the half
+            const int kh = key0 + h * (TK / 2);
+            int64_t row0 = 0;
+            bool ok = rh > 0;
+            if (p.block_table != nullptr) {
+                // the page holding these 16 keys (16 divides the page size);
+                // a page id outside the pool reads as zeros, no memory access
+                typedef const __attribute__((address_space(4))) int cint;
+                const int pid = ok ? ((cint *)p.block_table)[(int64_t)litem.b * p.max_pages + kh / p.page_size] : 0;
+                ok = ok && pid >= 0 && pid < p.num_pages;
+                row0 = ((int64_t)(ok ? pid : 0) * p.page_size + kh % p.page_size) * hd_k;
+            } else {
+                row0 = ((int64_t)litem.b * p.Skv + kh) * hd_k;
+            }
+            row0 += (int64_t)litem.hk * D;
+            // the descriptors end at the last valid key: rows past it read zeros
+            const int nbytes = ok ? (int)(((int64_t)(rh - 1) * hd_k + D) * 2) : 0;
+            kr[h] = buffer_rsrc(ok ? p.k + row0 : p.k, nbytes);
+            vr[h] = buffer_rsrc(ok ? p.v + row0 : p.v, nbytes);
+        }
         __bf16 *dst = ring + lstage * L::STAGE;
 #pragma unroll
-        for (int pp = 0; pp < 2 * L::LOADS; ++pp)
-            buffer_lds_dma16(pp >= L::LOADS ? vr : kr, goff[pp],
-                             dst + (pp >= L::LOADS ? L::T_ELEMS : 0) + 512 * (pp % L::LOADS));
+        for (int pp = 0; pp < 2 * L::LOADS; ++pp) {
+            const int m = pp % L::LOADS;
+            const int h = (m * (512 / D)) / (TK / 2);          // rows of load m: m * 512/D ..
+            buffer_lds_dma16(pp >= L::LOADS ? vr[h] : kr[h], goff[pp],
+                             dst + (pp >= L::LOADS ? L::T_ELEMS : 0) + 512 * m);
+        }
         lstage ^= 1;
         ++lt;
         ++lcnt;

@@ -73,6 +73,11 @@ struct DecParams {
     float *lse;              // may be null
     float *ws_o, *ws_lse;    // split partials (null when nsplit == 1)
     const int *seqlens;      // keys per sequence (device, clamped to [0, Skv]), or null: all Skv
+    // paged caches (block_table non-null): k, v are [num_pages, page_size,
+    // Hkv, d]; key j of sequence b is row j % page_size of page
+    // block_table[b * max_pages + j / page_size]; Skv = max_pages * page_size
+    const int *block_table;
+    int page_size, max_pages, num_pages;
     int B, Hq, Hkv, group, Skv;
     int ncb;                 // blocks of <= 32 query heads per KV head
     int nsplit, chunk;       // key chunks and keys per chunk
