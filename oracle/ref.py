@@ -240,6 +240,59 @@ def decode_split(q, k, v, scale, num_splits):
     return o, lse
 
 
+def e4m3fn_to_f64(codes):
+    """FP8 E4M3 codes (uint8) -> float64, from the format's definition.
+
+    The pages name FP8 among the formats each generation of matrix units
+    adds (lecompute.fr, "Flapping Airplanes, ThunderKittens and megakernels",
+    section "ThunderKittens starts with tiles, not whole applications",
+    glossary note on Tensor Cores) but do not define it; this is the E4M3
+    variant of the OCP 8-bit floating point specification (the "e4m3fn"
+    layout): bit 7 is the sign, bits 6..3 the exponent field ``E`` with bias
+    7, bits 2..0 the mantissa ``M``.
+
+    * ``E == 0``: subnormal, ``(-1)^s * (M / 8) * 2^-6`` (so ``M == 0`` is a
+      signed zero);
+    * ``E == 15`` and ``M == 7``: NaN (the format has no infinities);
+    * otherwise: normal, ``(-1)^s * (1 + M / 8) * 2^(E - 7)``; the largest
+      magnitude is ``1.75 * 2^8 = 448``.
+    """
+    c = np.asarray(codes, dtype=np.uint8).astype(np.int64)
+    sign = np.where(c >> 7, -1.0, 1.0)
+    e = (c >> 3) & 0xF
+    m = (c & 0x7).astype(np.float64)
+    val = np.where(e == 0, (m / 8.0) * 2.0 ** -6, (1.0 + m / 8.0) * np.exp2((e - 7).astype(np.float64)))
+    val = np.where((e == 15) & (c & 0x7 == 7), np.nan, val)
+    return sign * val
+
+
+def decode_fp8(q, k_codes, v_codes, scale, k_scale, v_scale, seqlens=None):
+    """Decode against an FP8 (e4m3fn) KV cache.
+
+    The cache stores codes and one scale per tensor: key ``j`` is
+    ``k_scale * e4m3fn(k_codes[..., j, ...])`` and likewise for the values.
+    The result is :func:`decode` over those dequantised values, sequence
+    ``b`` seeing its first ``seqlens[b]`` keys (clamped to ``[0, Skv]``; all
+    of them when ``seqlens`` is None).  A sequence with no key gets
+    ``O = 0`` and ``LSE = -inf``.
+    """
+    k = e4m3fn_to_f64(k_codes) * float(k_scale)
+    v = e4m3fn_to_f64(v_codes) * float(v_scale)
+    q = np.asarray(q, dtype=np.float64)
+    if seqlens is None:
+        return decode(q, k, v, scale)
+    B, Hq, d = q.shape
+    Skv = k.shape[1]
+    o = np.zeros((B, Hq, d))
+    lse = np.full((B, Hq), NEG_INF)
+    for b in range(B):
+        n = min(max(int(seqlens[b]), 0), Skv)
+        if n > 0:
+            ob, lb = decode(q[b:b + 1], k[b:b + 1, :n], v[b:b + 1, :n], scale)
+            o[b], lse[b] = ob[0], lb[0]
+    return o, lse
+
+
 def attention_rows(q, k, v, scale, causal, rows):
     """Selected output rows of :func:`attention`.
 

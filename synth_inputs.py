@@ -12,6 +12,11 @@ Recipe (one ``numpy.random.default_rng(seed)`` stream per workload):
 * long causal prefill: after v, one factor per head ``uniform(0.5, 2.0)``
   (float32) multiplies that head of K in float32 before the single bf16
   rounding, which varies how sharp the softmax is per head.
+* fp8 KV cache: q as for decode; K and V drawn as float32 standard normals
+  (order q, k, v), each tensor given one scale ``max|x| / 448`` (float32) and
+  stored as the FP8 E4M3 ("e4m3fn") codes of ``x / scale`` clipped to
+  [-448, 448], rounded to nearest by torch's float8_e4m3fn conversion (a
+  per-tensor quantiser of the usual kind; the codes span the format's range).
 * ragged batch: the 16 lengths are drawn first with
   ``integers(lo, hi + 1, nseq)`` (inclusive bounds), then q, k, v over the
   packed ``[total, H, d]`` layout.
@@ -25,7 +30,7 @@ import numpy as np
 
 __all__ = [
     "f32_to_bf16_bits", "bf16_to_f32", "bf16_to_f64", "CONFIGS",
-    "make_prefill", "make_decode", "make_varlen", "make_config",
+    "make_prefill", "make_decode", "make_decode_fp8", "make_varlen", "make_config",
 ]
 
 
@@ -99,6 +104,23 @@ def make_decode(seed, B, Hq, Hkv, Skv, d):
     k = rng.standard_normal((B, Skv, Hkv, d), dtype=np.float32)
     v = rng.standard_normal((B, Skv, Hkv, d), dtype=np.float32)
     return dict(q=f32_to_bf16_bits(q), k=f32_to_bf16_bits(k), v=f32_to_bf16_bits(v))
+
+
+def make_decode_fp8(seed, B, Hq, Hkv, Skv, d):
+    """q [B,Hq,d] (bf16 bits); k/v caches [B,Skv,Hkv,d] as uint8 e4m3fn
+    codes with float32 per-tensor scales ``k_scale`` and ``v_scale``."""
+    import torch
+    rng = np.random.default_rng(seed)
+    q = rng.standard_normal((B, Hq, d), dtype=np.float32)
+    out = dict(q=f32_to_bf16_bits(q))
+    for name in ("k", "v"):
+        x = rng.standard_normal((B, Skv, Hkv, d), dtype=np.float32)
+        sc = np.float32(np.abs(x).max() / np.float32(448.0))
+        y = np.clip(x / sc, np.float32(-448.0), np.float32(448.0)).astype(np.float32)
+        codes = torch.from_numpy(y).to(torch.float8_e4m3fn).view(torch.uint8).numpy()
+        out[name] = codes
+        out[name + "_scale"] = float(sc)
+    return out
 
 
 def make_paged(seed, B, Hq, Hkv, d, page_size, max_pages, num_pages):

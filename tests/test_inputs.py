@@ -51,3 +51,19 @@ def test_varlen_lengths_drawn_first_inclusive():
     assert small["cu_seqlens"][0] == 0 and np.all(np.diff(small["cu_seqlens"]) >= 2)
     assert small["q"].shape[0] == small["cu_seqlens"][-1]
     assert small["cu_seqlens"].dtype == np.int32
+
+
+def test_fp8_cache_generator():
+    a = si.make_decode_fp8(11, 2, 4, 2, 50, 16)
+    b = si.make_decode_fp8(11, 2, 4, 2, 50, 16)
+    for n in ("q", "k", "v"):
+        assert np.array_equal(a[n], b[n])
+    assert a["k"].dtype == np.uint8 and a["k"].shape == (2, 50, 2, 16)
+    assert a["q"].dtype == np.uint16 and a["q"].shape == (2, 4, 16)
+    for n in ("k", "v"):
+        c = a[n]
+        assert not np.any((c & 0x7F) == 0x7F), "no NaN codes"
+        assert np.any((c & 0x7F) == 0x7E), "the largest magnitude (448) is used"
+        assert a[n + "_scale"] > 0 and np.isfinite(a[n + "_scale"])
+        # the scale is float32: max|x| / 448
+        assert np.float32(a[n + "_scale"]) == a[n + "_scale"]

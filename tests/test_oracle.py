@@ -422,3 +422,108 @@ def test_c_oracle_rejects_bad_arguments():
     qb, _ = bf16_arr((1, 2, 2, 4), 56)
     with pytest.raises(ValueError):            # row out of range
         cpu.attn_rows(qb, kb, kb, 1.0, False, [[0, 2, 0]])
+
+
+# ----------------------------------------------------------- fp8 KV cache
+
+def test_e4m3fn_closed_form_values():
+    """Codes whose values the E4M3 definition fixes by hand."""
+    cases = {
+        0x00: 0.0, 0x80: -0.0, 0x01: 2.0 ** -9, 0x07: 7 * 2.0 ** -9, 0x08: 2.0 ** -6,
+        0x38: 1.0, 0x39: 1.125, 0x3F: 1.875, 0x40: 2.0, 0x30: 0.5, 0xB8: -1.0, 0xC0: -2.0,
+        0x77: 240.0, 0x78: 256.0, 0x7E: 448.0, 0xFE: -448.0,
+    }
+    codes = np.array(sorted(cases), dtype=np.uint8)
+    got = ref.e4m3fn_to_f64(codes)
+    want = np.array([cases[c] for c in sorted(cases)])
+    assert np.array_equal(got, want)
+    assert np.signbit(ref.e4m3fn_to_f64(np.array([0x80], dtype=np.uint8)))[0]
+    nan = ref.e4m3fn_to_f64(np.array([0x7F, 0xFF], dtype=np.uint8))
+    assert np.all(np.isnan(nan))
+
+
+def test_e4m3fn_matches_torch_on_every_code():
+    """All 256 codes against torch's own float8_e4m3fn -> float64 widening."""
+    import torch
+    codes = np.arange(256, dtype=np.uint8)
+    ours = ref.e4m3fn_to_f64(codes)
+    theirs = torch.from_numpy(codes).view(torch.float8_e4m3fn).to(torch.float64).numpy()
+    nan = np.isnan(theirs)
+    assert np.array_equal(np.isnan(ours), nan) and nan.sum() == 2
+    assert np.array_equal(ours[~nan], theirs[~nan])
+    assert np.array_equal(np.signbit(ours[~nan]), np.signbit(theirs[~nan]))
+
+
+def test_e4m3fn_order_and_symmetry():
+    """Codes 0..0x7E increase strictly; the sign bit only flips the sign."""
+    pos = ref.e4m3fn_to_f64(np.arange(0x7F, dtype=np.uint8))
+    assert np.all(np.diff(pos) > 0)
+    neg = ref.e4m3fn_to_f64(np.arange(0x80, 0xFF, dtype=np.uint8))
+    assert np.array_equal(neg, -pos)
+
+
+def _fp8_case(seed=5, B=3, Hq=4, Hkv=2, Skv=37, d=16):
+    data = si.make_decode_fp8(seed, B, Hq, Hkv, Skv, d)
+    return data, si.bf16_to_f64(data["q"])
+
+
+def test_decode_fp8_scales_enter_where_stated():
+    """O is linear in v_scale with LSE unchanged; only scale * k_scale matters."""
+    data, q = _fp8_case()
+    o1, l1 = ref.decode_fp8(q, data["k"], data["v"], 0.25, 0.5, 0.75)
+    o2, l2 = ref.decode_fp8(q, data["k"], data["v"], 0.25, 0.5, 1.5)
+    assert np.allclose(o2, 2 * o1, rtol=1e-13, atol=0) and np.array_equal(l1, l2)
+    o3, l3 = ref.decode_fp8(q, data["k"], data["v"], 0.5, 0.25, 0.75)
+    assert np.allclose(o3, o1, rtol=1e-12, atol=1e-14) and np.allclose(l3, l1, rtol=1e-13)
+
+
+def test_decode_fp8_uniform_keys_give_value_mean():
+    """Every key code 1.0: all scores equal q.1 * scale * k_scale, so O is the mean
+    dequantised value row and LSE = log(n) + that score (closed form)."""
+    data, q = _fp8_case()
+    k = np.full_like(data["k"], 0x38)
+    scale, ks, vs = 0.3, 0.125, 0.0625
+    o, lse = ref.decode_fp8(q, k, data["v"], scale, ks, vs)
+    B, Hq, d = q.shape
+    Skv, Hkv = k.shape[1], k.shape[2]
+    g = Hq // Hkv
+    vd = ref.e4m3fn_to_f64(data["v"]) * vs
+    for b in range(B):
+        for h in range(Hq):
+            want_o = vd[b, :, h // g, :].mean(axis=0)
+            want_l = math.log(Skv) + scale * ks * q[b, h].sum()
+            assert np.allclose(o[b, h], want_o, rtol=1e-12, atol=1e-15)
+            assert abs(lse[b, h] - want_l) < 1e-12
+
+
+def test_decode_fp8_lengths_are_prefixes_and_clamped():
+    """A length picks a prefix of the cache; 0 gives O = 0, LSE = -inf; out-of-range
+    lengths clamp to [0, Skv]."""
+    data, q = _fp8_case(B=4)
+    lens = np.array([0, 5, 37, 99])
+    o, lse = ref.decode_fp8(q, data["k"], data["v"], 0.2, 1.0, 1.0, seqlens=lens)
+    assert np.all(o[0] == 0) and np.all(np.isneginf(lse[0]))
+    o5, l5 = ref.decode_fp8(q[1:2], data["k"][1:2, :5], data["v"][1:2, :5], 0.2, 1.0, 1.0)
+    assert np.array_equal(o[1], o5[0]) and np.array_equal(lse[1], l5[0])
+    full, lf = ref.decode_fp8(q, data["k"], data["v"], 0.2, 1.0, 1.0)
+    assert np.array_equal(o[2:], full[2:]) and np.array_equal(lse[2:], lf[2:])
+    neg, ln = ref.decode_fp8(q, data["k"], data["v"], 0.2, 1.0, 1.0, seqlens=[-3, 0, 0, 0])
+    assert np.all(neg == 0) and np.all(np.isneginf(ln))
+
+
+def test_decode_fp8_brute_force_one_row():
+    """One output row by plain Python loops from the code values."""
+    data, q = _fp8_case(B=1, Hq=2, Hkv=1, Skv=6, d=4)
+    scale, ks, vs = 0.7, 0.05, 0.02
+    o, lse = ref.decode_fp8(q, data["k"], data["v"], scale, ks, vs)
+    kd = ref.e4m3fn_to_f64(data["k"])
+    vd = ref.e4m3fn_to_f64(data["v"])
+    for h in range(2):
+        s = [scale * sum(q[0, h, t] * ks * kd[0, j, 0, t] for t in range(4)) for j in range(6)]
+        m = max(s)
+        w = [math.exp(x - m) for x in s]
+        tot = sum(w)
+        for t in range(4):
+            want = sum(w[j] * vs * vd[0, j, 0, t] for j in range(6)) / tot
+            assert abs(o[0, h, t] - want) < 1e-12
+        assert abs(lse[0, h] - (m + math.log(tot))) < 1e-12
