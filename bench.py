@@ -57,15 +57,20 @@ def prefill_flops(B, H, Sq, Skv, d, causal):
     return 4.0 * d * pairs * B * H
 
 
-def decode_bytes(B, Hq, Hkv, Skv, d):
-    kv = 2 * B * Skv * Hkv * d * 2
+def decode_bytes(B, Hq, Hkv, Skv, d, kv_elem_bytes=2):
+    """K and V read once (bf16, or 1-byte fp8 codes), Q read, O and LSE written."""
+    kv = 2 * B * Skv * Hkv * d * kv_elem_bytes
     return kv + B * Hq * d * 2 + B * Hq * d * 2 + B * Hq * 4
 
 
 TRAFFIC_PATH = os.path.join(ROOT, "profiles", "traffic.json")
 # which kernels make up each reported path (substrings of the rocprofv3 names)
 TRAFFIC_KERNELS = {"prefill": ["attn_fwd_kernel<128, true, false>"],
-                   "decode": ["attn_decode_split_kernel<128", "attn_decode_combine_kernel<128>"]}
+                   "decode": ["attn_decode_split_kernel<128, false>",
+                              "attn_decode_combine_kernel<128>"],
+                   "decode_fp8": ["attn_decode_split_kernel<128, true>"]}
+# paths whose kernels only run with the fp8 extra (absent from a run without it)
+TRAFFIC_OPTIONAL = {"decode_fp8"}
 
 
 def load_traffic(kind: str):
@@ -104,7 +109,11 @@ def write_traffic(fetch_dir: str, write_dir: str):
     copy_kib = float(1 << 20)
 
     def copy_value(d):
-        vals = [v for k, v in d.items() if "copyBuffer" in k or "copy" in k.lower()]
+        # the runtime's device-to-device copy kernel; dtype conversions made
+        # while preparing inputs are elementwise "copy" kernels of torch
+        vals = [v for k, v in d.items() if "copyBuffer" in k]
+        if not vals:
+            vals = [v for k, v in d.items() if "copy" in k.lower()]
         if len(vals) != 1:
             sys.exit("expected exactly one copy kernel in the counter run")
         return vals[0]
@@ -126,6 +135,8 @@ def write_traffic(fetch_dir: str, write_dir: str):
                 wr += write[kw[0]] * w_scale * 1024
                 seen.append(kf[0])
         if not seen:
+            if kind in TRAFFIC_OPTIONAL:
+                continue
             sys.exit("no %s kernel in the counter run" % kind)
         out[kind] = {"bytes": int(round(rd + wr)), "read_bytes": int(round(rd)),
                      "write_bytes": int(round(wr)), "kernels": seen}
@@ -135,16 +146,20 @@ def write_traffic(fetch_dir: str, write_dir: str):
     print(json.dumps(out))
 
 
-def extra_workloads(api, dev, stream, calls=5):
+def extra_workloads(api, dev, stream, which="all", calls=5, dec_ms=None):
     """Context lines beside the headline: the long causal workload (B1 H32
-    S16384 d128) and the ragged causal batch (16 sequences, lengths drawn
-    U{128..8192} with seed 5, H32 d128).  Timing only: the inputs are seeded
-    N(0,1) bf16 draws made on the GPU (the lengths follow the same recipe as
-    the test inputs); K of the long workload is scaled per head by U(0.5, 2)
-    as in its test recipe."""
+    S16384 d128), the ragged causal batch (16 sequences, lengths drawn
+    U{128..8192} with seed 5, H32 d128) and the decode workload's sizes with
+    an fp8 (e4m3fn) KV cache.  Timing only: the inputs are seeded N(0,1)
+    draws made on the GPU (the lengths follow the same recipe as the test
+    inputs); K of the long workload is scaled per head by U(0.5, 2) as in its
+    test recipe; the fp8 cache holds the codes of x / (max|x| / 448) per
+    tensor, as the test recipe does.  ``which`` = "fp8" runs the fp8 decode
+    only."""
     import torch
     out = {}
     gen = torch.Generator(device=dev)
+    d = 128
 
     def timed(fn):
         for _ in range(2):
@@ -158,9 +173,37 @@ def extra_workloads(api, dev, stream, calls=5):
         torch.cuda.synchronize()
         return float(np.mean([a.elapsed_time(b) for a, b in ev]))
 
+    # decode with an fp8 KV cache (the decode workload's sizes)
+    gen.manual_seed(4)
+    B, Hq, Hkv, Skv = 64, 32, 8, 4096
+    q = torch.randn((B, Hq, d), generator=gen, device=dev, dtype=torch.float32).to(torch.bfloat16)
+    codes, scales = [], []
+    for _ in range(2):
+        x = torch.randn((B, Skv, Hkv, d), generator=gen, device=dev, dtype=torch.float32)
+        sc = float(x.abs().max()) / 448.0
+        codes.append((x / sc).clamp(-448.0, 448.0).to(torch.float8_e4m3fn).view(torch.uint8))
+        scales.append(sc)
+        del x
+    o = torch.empty_like(q)
+    lse = torch.empty((B, Hq), dtype=torch.float32, device=dev)
+    ws = torch.empty(max(1, api.attn_decode_workspace_bytes(B, Hq, Hkv, Skv, d, 8)),
+                     dtype=torch.uint8, device=dev)
+    ms = timed(lambda: api.attn_decode_fp8(q, codes[0], codes[1], scales[0], scales[1], o=o,
+                                           lse=lse, num_splits=8, workspace=ws, stream=stream))
+    nb = decode_bytes(B, Hq, Hkv, Skv, d, kv_elem_bytes=1)
+    gbs = nb / (ms * 1e-3) / 1e9
+    out["decode_fp8_kv_B64_Hq32_Hkv8_Skv4096_d128"] = {
+        "ms": round(ms, 5), "GB/s": round(gbs, 1), "frac_of_8000": round(gbs / PEAK_HBM_GBS, 4),
+        "algorithmic_bytes": nb, "traffic": load_traffic("decode_fp8"),
+        "kernel": "attn_decode_split_kernel<128, true>",
+        "speedup_vs_bf16_cache": None if dec_ms is None else round(dec_ms / ms, 3)}
+    del q, codes, o, lse, ws
+    if which == "fp8":
+        return out
+
     # long causal prefill
     gen.manual_seed(3)
-    B, H, S, d = 1, 32, 16384, 128
+    B, H, S = 1, 32, 16384
     q, k, v = (torch.randn((B, S, H, d), generator=gen, device=dev, dtype=torch.float32)
                for _ in range(3))
     k = k * (0.5 + 1.5 * torch.rand((1, 1, H, 1), generator=gen, device=dev))
@@ -223,8 +266,10 @@ def main():
     ap.add_argument("--warmup", type=int, default=200,
                     help="untimed steps first (the clocks need some tens of ms to settle)")
     ap.add_argument("--no-cpu-baseline", action="store_true")
+    ap.add_argument("--extra", choices=["all", "none", "fp8"], default="all",
+                    help="context workloads beside the headline (fp8: the fp8-cache decode only)")
     ap.add_argument("--no-extra", action="store_true",
-                    help="skip the long-causal and ragged-batch context lines")
+                    help="skip every context line (same as --extra none)")
     ap.add_argument("--cpu-pairs", type=float, default=2.0e8,
                     help="allowed query/key pairs in the CPU-baseline sample")
     ap.add_argument("--copy-calibration", action="store_true",
@@ -355,8 +400,9 @@ def main():
         },
         "kernel_hash": kernel_hash(),
     }
-    if not args.no_extra:
-        result["extra"] = extra_workloads(api, dev, stream)
+    which = "none" if args.no_extra else args.extra
+    if which != "none":
+        result["extra"] = extra_workloads(api, dev, stream, which=which, dec_ms=dec_avg)
     if not args.no_cpu_baseline:
         result["cpu_baseline"] = cpu_baseline(pspec, pdata, args.cpu_pairs)
     print(json.dumps(result), flush=True)

@@ -184,6 +184,36 @@ attn_status_t attn_decode_paged(const void *q, const void *k_pages, const void *
                                 int num_splits, void *workspace, size_t workspace_bytes,
                                 hipStream_t stream);
 
+/*
+ * Decode against an 8-bit floating-point KV cache: every cached element is
+ * an OCP FP8 E4M3 ("e4m3fn": 1 sign, 4 exponent bits with bias 7, 3 mantissa
+ * bits, subnormals, no infinities, codes 0x7F / 0xFF are NaN) code, one byte,
+ * and the cache holds k = k_scale * code(K), v = v_scale * code(V) with one
+ * positive fp32 scale per tensor.
+ *   q, o : [B, Hq, d] bf16      k_cache, v_cache : [B, Skv, Hkv, d] uint8 codes
+ *   lse  : [B, Hq] fp32 (or NULL)
+ *   seqlens_k : DEVICE int32 [B] (4-byte aligned) as in attn_decode_varlen, or
+ *   NULL to attend to all Skv keys of every sequence.
+ * The result is the attention of attn_decode over the dequantised cache:
+ * scores scale * k_scale * (q . code(k_j)), O = v_scale * sum_j p_j code(v_j).
+ * Codes are widened to bf16 exactly (every E4M3 value is a bf16 value); the
+ * scales are applied in fp32 to the scores and to the output.  Chunking,
+ * workspace (attn_decode_workspace_bytes with the same sizes) and errors as
+ * attn_decode; ATTN_ERR_SCALE also for a k_scale or v_scale that is not
+ * finite and > 0.  Cache pointers must be 16-byte aligned.  Halving the
+ * bytes per cached element halves the memory traffic that bounds decode
+ * (lecompute.fr, "Flapping Airplanes, ThunderKittens and megakernels",
+ * section "Follow the request instead of one utilization number"); each
+ * generation of matrix units takes narrower formats, FP8 among them (same
+ * page, section "ThunderKittens starts with tiles, not whole applications", glossary note
+ * on Tensor Cores).
+ */
+attn_status_t attn_decode_fp8(const void *q, const void *k_cache, const void *v_cache, void *o,
+                              float *lse, const int *seqlens_k, int B, int Hq, int Hkv,
+                              int Skv, int d, float scale, float k_scale, float v_scale,
+                              int num_splits, void *workspace, size_t workspace_bytes,
+                              hipStream_t stream);
+
 /* Bytes of decode workspace for these sizes (0 when num_splits resolves to
  * 1; num_splits <= 0 means the library's choice, as in attn_decode).  Returns
  * 0 for invalid sizes. */

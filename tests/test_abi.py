@@ -33,7 +33,7 @@ def lib():
 
 def test_library_exports_every_declared_symbol(lib):
     names = declared_functions()
-    assert len(names) == 9, names
+    assert len(names) == 10, names
     raw = ctypes.CDLL(_lib.LIB_PATH)
     for n in names:
         assert hasattr(raw, n), n
@@ -171,6 +171,30 @@ def test_decode_paged_validation(lib):
     assert decode_paged(lib, Hq=6, Hkv=4) == GQA
     assert decode_paged(lib, scale=float("inf")) == SCALE
     assert decode_paged(lib, ws=None) == WS
+
+
+def decode_fp8(lib, seqlens=None, B=2, Hq=8, Hkv=2, Skv=64, d=128, scale=0.1, ks=0.01, vs=0.01,
+               splits=4, ws=P, wsb=1 << 30, q=P, k=P, v=P):
+    return lib.attn_decode_fp8(q, k, v, P, None, seqlens, B, Hq, Hkv, Skv, d, scale, ks, vs,
+                               splits, ws, wsb, None)
+
+
+def test_decode_fp8_validation(lib):
+    assert decode_fp8(lib, q=None) == NULLPTR
+    assert decode_fp8(lib, k=None) == NULLPTR
+    assert decode_fp8(lib, v=None) == NULLPTR
+    assert decode_fp8(lib, k=P + 8) == ALIGN
+    assert decode_fp8(lib, seqlens=P + 2) == ALIGN
+    assert decode_fp8(lib, Skv=0) == SHAPE
+    assert decode_fp8(lib, d=96) == BAD_D
+    assert decode_fp8(lib, Hq=6, Hkv=4) == GQA
+    assert decode_fp8(lib, scale=0.0) == SCALE
+    for bad in (0.0, -1.0, float("inf"), float("nan")):
+        assert decode_fp8(lib, ks=bad) == SCALE
+        assert decode_fp8(lib, vs=bad) == SCALE
+    assert decode_fp8(lib, scale=1e-30, ks=1e-30) == SCALE    # product underflows to 0
+    assert decode_fp8(lib, ws=None) == WS
+    assert decode_fp8(lib, wsb=16) == WS
 
 
 def test_decode_split_choice(lib):

@@ -264,6 +264,83 @@ def test_decode_paged_identity_table_equals_varlen(api, dev):
         assert torch.equal(l1, l2)
 
 
+DECODE_FP8 = [  # B, Hq, Hkv, Skv, d, splits, lengths (None: every key; "rand": random)
+    (2, 8, 2, 1000, 128, 7, None),
+    (3, 4, 4, 1, 64, 1, None),
+    (3, 4, 4, 1, 64, 4, None),                 # more chunks than keys: empty chunks
+    (1, 64, 1, 300, 128, 3, None),             # MQA group of 64 query heads
+    (2, 32, 8, 4096, 128, 0, None),            # library picks the split count
+    (1, 40, 8, 513, 64, 2, None),
+    (4, 16, 2, 129, 128, 1, None),             # one chunk, ragged last 64-key tile
+    (64, 8, 4, 1000, 128, 7, None),            # groups fill the GPU: in-kernel merge
+    (128, 4, 2, 777, 64, 3, None),
+    (4, 8, 2, 1000, 128, 7, [1000, 1, 0, 513]),
+    (5, 16, 4, 777, 128, 0, "rand"),
+    (64, 8, 4, 1000, 128, 8, "rand"),
+    (4, 8, 2, 256, 128, 4, [-5, 300, 256, 64]),   # out-of-range lengths are clamped
+]
+
+
+def _run_decode_fp8(api, dev, data, scale, splits, lengths=None):
+    import torch
+    q = to_dev(data["q"], dev)
+    k = torch.from_numpy(data["k"]).to(dev)
+    v = torch.from_numpy(data["v"]).to(dev)
+    seq = None if lengths is None else torch.from_numpy(np.asarray(lengths, np.int32)).to(dev)
+    o, lse = api.attn_decode_fp8(q, k, v, data["k_scale"], data["v_scale"], seqlens_k=seq,
+                                 scale=scale, num_splits=splits)
+    torch.cuda.synchronize()
+    return bf16_to_np(o), f32_to_np(lse)
+
+
+@pytest.mark.parametrize("case", DECODE_FP8, ids=lambda c: "B%d_Hq%d_Hkv%d_Skv%d_d%d_s%d" % c[:6])
+def test_decode_fp8_matches_oracle(api, dev, case):
+    """fp8 (e4m3fn) caches with per-tensor scales against the oracle's dequantised decode."""
+    B, Hq, Hkv, Skv, d, splits, lengths = case
+    data = si.make_decode_fp8(41 + Skv, B, Hq, Hkv, Skv, d)
+    if isinstance(lengths, str):
+        lengths = np.random.default_rng(B + Skv).integers(0, Skv + 1, B)
+    scale = si.default_scale(d)
+    o, lse = _run_decode_fp8(api, dev, data, scale, splits, lengths)
+    o_ref, lse_ref = ref.decode_fp8(si.bf16_to_f64(data["q"]), data["k"], data["v"], scale,
+                                    data["k_scale"], data["v_scale"], seqlens=lengths)
+    assert_close(o, o_ref, lse, lse_ref, str(case[:6]))
+
+
+def test_decode_fp8_workload_sampled_sequences(api, dev):
+    """The decode workload's sizes (B64 Hq32 Hkv8 Skv4096 d128, 8 chunks) with an fp8
+    cache, in the launch configuration the benchmark times; the oracle checks
+    eight whole sequences."""
+    spec = si.CONFIGS[4]
+    B, Hq, Hkv, Skv, d = (spec[x] for x in ("B", "Hq", "Hkv", "Skv", "d"))
+    data = si.make_decode_fp8(spec["seed"], B, Hq, Hkv, Skv, d)
+    scale = si.default_scale(d)
+    o, lse = _run_decode_fp8(api, dev, data, scale, spec["num_splits"])
+    bs = np.array([0, 1, 17, 31, 32, 50, 62, 63])
+    o_ref, lse_ref = ref.decode_fp8(si.bf16_to_f64(data["q"][bs]), data["k"][bs], data["v"][bs],
+                                    scale, data["k_scale"], data["v_scale"])
+    assert_close(o[bs], o_ref, lse[bs], lse_ref, "fp8 decode workload")
+    assert np.all(np.isfinite(o)) and np.all(np.isfinite(lse))
+
+
+def test_decode_fp8_power_of_two_scales_equal_bf16_cache(api, dev):
+    """Codes times a power-of-two scale are exact bf16 values, so the bf16 decode of
+    that cache computes the same attention; the two paths agree to rounding."""
+    import torch
+    B, Hq, Hkv, Skv, d = 4, 16, 4, 900, 128
+    data = si.make_decode_fp8(77, B, Hq, Hkv, Skv, d)
+    data["k_scale"], data["v_scale"] = 2.0 ** -6, 2.0 ** -7
+    o8, l8 = _run_decode_fp8(api, dev, data, 0.09, 3)
+    kb = torch.from_numpy(data["k"]).view(torch.float8_e4m3fn).to(torch.float32) * 2.0 ** -6
+    vb = torch.from_numpy(data["v"]).view(torch.float8_e4m3fn).to(torch.float32) * 2.0 ** -7
+    q = to_dev(data["q"], dev)
+    o16, l16 = api.attn_decode(q, kb.to(torch.bfloat16).to(dev), vb.to(torch.bfloat16).to(dev),
+                               scale=0.09, num_splits=3)
+    torch.cuda.synchronize()
+    assert np.abs(o8 - bf16_to_np(o16)).max() <= 2 ** -6
+    assert np.abs(l8 - f32_to_np(l16)).max() <= 1e-4
+
+
 def test_decode_split_counts_agree(api, dev):
     """1, 2, 8, 64 chunks and the library's choice agree closely (fp32 merge)."""
     import torch

@@ -219,6 +219,51 @@ def attn_decode_paged(q, k_pages, v_pages, block_table, seqlens_k, o=None, lse=N
     return o, lse
 
 
+def attn_decode_fp8(q, k_cache, v_cache, k_scale, v_scale, seqlens_k=None, o=None, lse=None,
+                    scale=None, num_splits=0, workspace=None, want_lse=True, stream=None):
+    """Decode against an fp8 (e4m3fn) KV cache; returns ``(o, lse)``.
+
+    q ``[B,Hq,d]`` bf16; k_cache/v_cache ``[B,Skv,Hkv,d]`` of e4m3fn codes
+    (``torch.uint8`` or ``torch.float8_e4m3fn``), holding ``k / k_scale`` and
+    ``v / v_scale``; seqlens_k an optional int32 GPU ``[B]`` as in
+    :func:`attn_decode_varlen`.
+    """
+    def codes(t, name):
+        if isinstance(t, torch.Tensor) and t.dtype == torch.float8_e4m3fn:
+            t = t.view(torch.uint8)
+        _need(t, name, torch.uint8, 4)
+        return t
+
+    _need(q, "q", torch.bfloat16, 3)
+    k_cache, v_cache = codes(k_cache, "k_cache"), codes(v_cache, "v_cache")
+    B, Hq, d = q.shape
+    Skv, Hkv = k_cache.shape[1], k_cache.shape[2]
+    if tuple(v_cache.shape) != tuple(k_cache.shape) or k_cache.shape[0] != B or \
+            k_cache.shape[3] != d:
+        raise ValueError("shape mismatch")
+    if seqlens_k is not None:
+        _need(seqlens_k, "seqlens_k", torch.int32, 1)
+        if seqlens_k.shape[0] != B:
+            raise ValueError("seqlens_k must have one entry per sequence")
+    if o is None:
+        o = torch.empty_like(q)
+    _need(o, "o", torch.bfloat16, 3)
+    if lse is None and want_lse:
+        lse = torch.empty((B, Hq), dtype=torch.float32, device=q.device)
+    if lse is not None:
+        _need(lse, "lse", torch.float32, 2)
+    nbytes = attn_decode_workspace_bytes(B, Hq, Hkv, Skv, d, num_splits)
+    if workspace is None and nbytes > 0:
+        workspace = torch.empty(nbytes, dtype=torch.uint8, device=q.device)
+    ws_bytes = 0 if workspace is None else workspace.numel() * workspace.element_size()
+    st = _lib.load().attn_decode_fp8(_ptr(q), _ptr(k_cache), _ptr(v_cache), _ptr(o), _ptr(lse),
+                                     _ptr(seqlens_k), B, Hq, Hkv, Skv, d, _scale(scale, d),
+                                     float(k_scale), float(v_scale), int(num_splits),
+                                     _ptr(workspace), ws_bytes, _stream(stream))
+    _check(st, "attn_decode_fp8")
+    return o, lse
+
+
 def _decode(q, k_cache, v_cache, seqlens_k, o, lse, scale, num_splits, workspace, want_lse,
             stream):
     _need(q, "q", torch.bfloat16, 3)

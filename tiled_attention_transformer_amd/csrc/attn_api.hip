@@ -182,15 +182,24 @@ struct PagedCache {
     int page_size, max_pages, num_pages;
 };
 
+// An fp8 (e4m3fn) cache: stored codes times a per-tensor scale.
+struct Fp8Cache {
+    float k_scale, v_scale;
+};
+
 attn_status_t decode_impl(const void *q, const void *k_cache, const void *v_cache, void *o,
                           float *lse, const int *seqlens, int B, int Hq, int Hkv, int Skv, int d,
                           float scale, int num_splits, void *workspace, size_t workspace_bytes,
-                          hipStream_t stream, const PagedCache *paged = nullptr) {
+                          hipStream_t stream, const PagedCache *paged = nullptr,
+                          const Fp8Cache *fp8 = nullptr) {
     if (!q || !k_cache || !v_cache || !o) return ATTN_ERR_NULLPTR;
     if (!decode_sizes_ok(B, Hq, Hkv, Skv, d)) return ATTN_ERR_SHAPE;
     if (!d_ok(d)) return ATTN_ERR_UNSUPPORTED_D;
     if (Hq % Hkv) return ATTN_ERR_GQA_RATIO;
     if (!scale_ok(scale)) return ATTN_ERR_SCALE;
+    if (fp8 && (!scale_ok(fp8->k_scale) || !scale_ok(fp8->v_scale) ||
+                !scale_ok(scale * fp8->k_scale)))
+        return ATTN_ERR_SCALE;
     if (num_splits > 65536) return ATTN_ERR_SHAPE;
     if (!aligned(q, 16) || !aligned(k_cache, 16) || !aligned(v_cache, 16) || !aligned(o, 16) ||
         (lse && !aligned(lse, 4)))
@@ -204,8 +213,8 @@ attn_status_t decode_impl(const void *q, const void *k_cache, const void *v_cach
     if ((int64_t)B * Hkv * sh.ncb * sh.nsplit > 0x7fffffff) return ATTN_ERR_SHAPE;
     attn::DecParams p{};
     p.q = (const __bf16 *)q;
-    p.k = (const __bf16 *)k_cache;
-    p.v = (const __bf16 *)v_cache;
+    p.k = k_cache;
+    p.v = v_cache;
     p.o = (__bf16 *)o;
     p.lse = lse;
     p.seqlens = seqlens;
@@ -228,7 +237,14 @@ attn_status_t decode_impl(const void *q, const void *k_cache, const void *v_cach
     p.nsplit = sh.nsplit;
     p.chunk = sh.chunk;
     p.c = scale * attn::kLog2e;
-    return from_hip(attn::launch_decode(p, d, stream));
+    p.v_scale = 1.f;
+    if (fp8) {
+        // scores use the stored key codes: the key scale joins the softmax
+        // scale; the value scale multiplies the output
+        p.c = scale * fp8->k_scale * attn::kLog2e;
+        p.v_scale = fp8->v_scale;
+    }
+    return from_hip(attn::launch_decode(p, d, fp8 != nullptr, stream));
 }
 
 }  // namespace
@@ -273,6 +289,17 @@ attn_status_t attn_decode_paged(const void *q, const void *k_pages, const void *
     return decode_impl(q, k_pages, v_pages, o, lse, seqlens_k, B, Hq, Hkv,
                        max_pages_per_seq * page_size, d, scale, num_splits, workspace,
                        workspace_bytes, stream, &pc);
+}
+
+attn_status_t attn_decode_fp8(const void *q, const void *k_cache, const void *v_cache, void *o,
+                              float *lse, const int *seqlens_k, int B, int Hq, int Hkv,
+                              int Skv, int d, float scale, float k_scale, float v_scale,
+                              int num_splits, void *workspace, size_t workspace_bytes,
+                              hipStream_t stream) {
+    if (seqlens_k && !aligned(seqlens_k, 4)) return ATTN_ERR_ALIGNMENT;
+    const Fp8Cache f{k_scale, v_scale};
+    return decode_impl(q, k_cache, v_cache, o, lse, seqlens_k, B, Hq, Hkv, Skv, d, scale,
+                       num_splits, workspace, workspace_bytes, stream, nullptr, &f);
 }
 
 }  // extern "C"

@@ -19,8 +19,9 @@
 //    one pass over that range of K and V;
 //  * the four waves split an item's keys: wave v takes 32-key tiles v, v+4,
 //    v+8, ... (so together they read 128 consecutive keys at a time) and
-//    streams them through a private 2-stage LDS ring with buffer loads that
-//    write straight to LDS.  No wave waits for another while streaming:
+//    streams them through a private LDS ring (2 stages of bf16 tiles, or 4
+//    of fp8 tiles: the same 32 KB) with buffer loads that write straight to
+//    LDS.  No wave waits for another while streaming:
 //    a ring shared by the workgroup needs a barrier per tile, and that
 //    barrier alone held a plain load stream of this shape to ~5.35 TB/s
 //    where private rings reach ~5.9 TB/s;
@@ -28,7 +29,9 @@
 //    output) for its keys: S^T = K Q^T and O^T += V^T P^T on
 //    v_mfma_f32_32x32x16_bf16, V read with ds_read_b64_tr_b16; rows are
 //    unpadded and their 16-byte chunks XOR-swizzled by row so both operand
-//    reads are free of bank conflicts;
+//    reads are free of bank conflicts.  An fp8 (e4m3fn) cache stays fp8 in
+//    LDS and is widened to bf16 in registers (v_cvt_scalef32_pk_bf16_fp8,
+//    exact) right before the MFMAs; V then comes through ds_read_b64_tr_b8;
 //  * at the end of an item the four waves merge their states through LDS
 //    (log-sum-exp weights, then a fixed-order sum, so results are
 //    deterministic) and the result goes out: bf16 O and LSE when the item is
@@ -47,45 +50,83 @@ namespace {
 constexpr int NT = kDecThreads;          // 4 waves
 constexpr int NWV = NT / 64;
 constexpr int NCOL = kDecCols;           // query heads per block (MFMA columns)
-constexpr int TK = 32;                   // keys per wave tile
 
-template <int D>
+// LDS plan of the split kernel for one cached element type: bf16, or fp8
+// (OCP e4m3fn codes).  Tiles are 32 keys either way; an fp8 tile is half the
+// bytes, so the same ring holds four stages instead of two and each wave
+// keeps three tiles in flight instead of one.  The stream is bound by how
+// many bytes are in flight, not by the compute per tile.
+template <int D, bool F8>
 struct DecLay {
-    static constexpr int CPR = D / 8;                  // 16-byte chunks per row
-    static constexpr int T_ELEMS = TK * D;             // one K or V tile
-    static constexpr int STAGE = 2 * T_ELEMS;          // K, then V
-    static constexpr int LOADS = T_ELEMS / 512;        // wave-wide loads per K (or V) tile
-    static constexpr int RING = 2 * STAGE;             // two stages per wave
+    static constexpr int EB = F8 ? 1 : 2;              // bytes per cached element
+    static constexpr int TK = 32;                      // keys per wave tile
+    static constexpr int STAGES = F8 ? 4 : 2;          // ring stages per wave
+    static constexpr int NB = TK / 32;                 // 32-key MFMA blocks per tile
+    static constexpr int NP = TK / 16;                 // 16-key parts per tile (own descriptors)
+    static constexpr int RB = D * EB;                  // bytes per cached row
+    static constexpr int CPR = RB / 16;                // 16-byte chunks per row
+    static constexpr int T_BYTES = TK * RB;            // one K or V tile
+    static constexpr int STAGE = 2 * T_BYTES;          // K, then V
+    static constexpr int LOADS = T_BYTES / 1024;       // wave-wide loads per K (or V) tile
+    static constexpr int RING = STAGES * STAGE;        // the wave's ring
     static constexpr int MERGE = NCOL * D;             // fp32 output block for the merge
     static constexpr int LSE = NWV * NCOL;             // per-wave LSEs (fp32)
-    // LDS in bf16 elements: the rings, then the fp32 merge areas
-    static constexpr int TOTAL = NWV * RING + 2 * (MERGE + LSE);
+    // LDS bytes: the rings, then the fp32 merge areas
+    static constexpr int TOTAL = NWV * RING + 4 * (MERGE + LSE);
     static_assert((CPR & (CPR - 1)) == 0 && 32 % CPR == 0, "chunk swizzle needs a power of two");
-    static_assert(T_ELEMS % 512 == 0, "a tile must be whole wave loads");
+    static_assert(T_BYTES % 1024 == 0, "a tile must be whole wave loads");
+    static_assert(16 % (1024 / RB) == 0, "a load must stay within a 16-key part");
+    static_assert((STAGES & (STAGES - 1)) == 0 && STAGES <= 4, "stage count");
 };
 
-// Chunk swizzles (physical chunk = logical chunk ^ f(row)).  K is read by
-// rows (lane = key row, 16 bytes), so 16 consecutive rows must hit distinct
-// chunks; V is read by 4 consecutive rows at a time (transposing reads), so
-// those 4 rows must hit distinct 64-byte column groups.
-template <int D>
-__device__ __forceinline__ int swz_k(int row) { return row & (D / 8 - 1); }
-template <int D>
-__device__ __forceinline__ int swz_v(int row) { return (4 * (row & 3)) & (D / 8 - 1); }
+// Chunk swizzles (physical chunk = logical chunk ^ f(row)); LDS serves 256
+// bytes (64 banks) per cycle, so the 16-byte chunks one cycle reads must
+// cover distinct 16-byte bank groups.
+//  * bf16: K is read by rows (lane = key row, 16 bytes), so 16 consecutive
+//    rows must hit distinct chunks; V is read by 4 consecutive rows at a time
+//    (ds_read_b64_tr_b16), so those 4 rows must hit distinct 64-byte groups.
+//  * fp8: rows are 128 (d = 128) or 64 (d = 64) bytes, so 2 or 4 rows share a
+//    256-byte bank line.  K reads 16 consecutive rows per chunk; V's
+//    ds_read_b64_tr_b8 has each 16-lane group read 8 rows x 16 bytes, and the
+//    swizzle keeps any two groups of one read apart.  (Checked exhaustively
+//    on the CPU for both head sizes.)
+template <int D, bool F8>
+__device__ __forceinline__ int swz_k(int row) {
+    if constexpr (F8) return D == 128 ? (row >> 1) & 7 : (row >> 2) & 3;
+    else return row & (D / 8 - 1);
+}
+template <int D, bool F8>
+__device__ __forceinline__ int swz_v(int row) {
+    if constexpr (F8) return D == 128 ? ((row & 2) | ((row >> 1) & 4) | ((row >> 2) & 1)) : (row >> 2) & 3;
+    else return (4 * (row & 3)) & (D / 8 - 1);
+}
 
-template <int D>
+// Eight fp8 (e4m3fn) codes -> bf16x8, exactly (every e4m3fn value is a bf16
+// value); v_cvt_scalef32_pk_bf16_fp8 with scale 1 converts two codes.
+__device__ __forceinline__ bf16x8 fp8x8_to_bf16(uint32_t lo, uint32_t hi) {
+    const bf16x2 a = __builtin_amdgcn_cvt_scalef32_pk_bf16_fp8(lo, 1.0f, false);
+    const bf16x2 b = __builtin_amdgcn_cvt_scalef32_pk_bf16_fp8(lo, 1.0f, true);
+    const bf16x2 c = __builtin_amdgcn_cvt_scalef32_pk_bf16_fp8(hi, 1.0f, false);
+    const bf16x2 d = __builtin_amdgcn_cvt_scalef32_pk_bf16_fp8(hi, 1.0f, true);
+    const bf16x4 ab = __builtin_shufflevector(a, b, 0, 1, 2, 3);
+    const bf16x4 cd = __builtin_shufflevector(c, d, 0, 1, 2, 3);
+    return __builtin_shufflevector(ab, cd, 0, 1, 2, 3, 4, 5, 6, 7);
+}
+
+template <int D, bool F8>
 __global__ __launch_bounds__(NT)
 void attn_decode_split_kernel(DecParams p) {
-    using L = DecLay<D>;
-    __shared__ __attribute__((aligned(16))) __bf16 lds[L::TOTAL];
+    using L = DecLay<D, F8>;
+    constexpr int TK = L::TK;
+    __shared__ __attribute__((aligned(16))) unsigned char lds[L::TOTAL];
 
     const int tid = threadIdx.x;
     const int lane = tid & 63;
     const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
     const int g = lane >> 5;
     const int col = lane & 31;
-    const int64_t hd_k = (int64_t)p.Hkv * D;
-    __bf16 *ring = lds + wave * L::RING;
+    const int64_t hd_k = (int64_t)p.Hkv * D;     // elements between consecutive keys
+    unsigned char *ring = lds + wave * L::RING;
     float *merge_o = reinterpret_cast<float *>(lds + NWV * L::RING);
     float *merge_l = merge_o + L::MERGE;
 
@@ -123,12 +164,12 @@ void attn_decode_split_kernel(DecParams p) {
     // this wave's tiles of an item: w, w + NWV, ...
     auto wave_tiles = [&](const Item &it) { return wave < it.ntiles ? (it.ntiles - wave + NWV - 1) / NWV : 0; };
 
-    // Load plan: load m of a tensor (m < LOADS) fills slots 64m .. 64m+63 of
-    // the tile; lane L's slot is (row, physical chunk).  A tile is read as
-    // two halves of 16 keys, each through its own buffer descriptor (in a
-    // paged cache the halves may sit in different pages); a load never
-    // straddles the halves, and its offset is relative to its half.
-    static_assert((TK / 2) % (512 / D) == 0, "a load must stay within a half tile");
+    // Load plan: load m of a tensor (m < LOADS) fills bytes 1024m ..
+    // 1024m+1023 of the tile; lane L's 16-byte slot is (row, physical
+    // chunk).  A tile is read as parts of 16 keys, each through its own
+    // buffer descriptor (in a paged cache the parts may sit in different
+    // pages); a load never straddles two parts, and its offset is relative
+    // to its part.
     uint32_t goff[2 * L::LOADS];
 #pragma unroll
     for (int pp = 0; pp < 2 * L::LOADS; ++pp) {
@@ -136,8 +177,8 @@ void attn_decode_split_kernel(DecParams p) {
         const int m = isv ? pp - L::LOADS : pp;
         const int slot = 64 * m + lane;
         const int row = slot / L::CPR;
-        const int lc = (slot % L::CPR) ^ (isv ? swz_v<D>(row) : swz_k<D>(row));
-        goff[pp] = (uint32_t)((row % (TK / 2)) * hd_k + 8 * lc) * 2u;
+        const int lc = (slot % L::CPR) ^ (isv ? swz_v<D, F8>(row) : swz_k<D, F8>(row));
+        goff[pp] = (uint32_t)((row % 16) * hd_k * L::EB + 16 * lc);
     }
 
     // This wave's load stream: its tiles of every item, in order.  `li` is
@@ -157,15 +198,17 @@ void attn_decode_split_kernel(DecParams p) {
         }
     };
     lskip();
+    const unsigned char *kbase = static_cast<const unsigned char *>(p.k);
+    const unsigned char *vbase = static_cast<const unsigned char *>(p.v);
     auto issue_next = [&]() {
         if (li >= my_items) return;
         const int key0 = litem.k_lo + TK * (wave + NWV * lt);
         const int rows = min(TK, litem.k_lo + litem.nkeys - key0);
-        __amdgpu_buffer_rsrc_t kr[2], vr[2];
+        __amdgpu_buffer_rsrc_t kr[L::NP], vr[L::NP];
 #pragma unroll
-        for (int h = 0; h < 2; ++h) {
-            const int rh = min(max(rows - h * (TK / 2), 0), TK / 2);   // valid rows of the half
-            const int kh = key0 + h * (TK / 2);
+        for (int h = 0; h < L::NP; ++h) {
+            const int rh = min(max(rows - 16 * h, 0), 16);   // valid rows of the part
+            const int kh = key0 + 16 * h;
             int64_t row0 = 0;
             bool ok = rh > 0;
             if (p.block_table != nullptr) {
@@ -178,21 +221,21 @@ void attn_decode_split_kernel(DecParams p) {
             } else {
                 row0 = ((int64_t)litem.b * p.Skv + kh) * hd_k;
             }
-            row0 += (int64_t)litem.hk * D;
+            row0 = (row0 + (int64_t)litem.hk * D) * L::EB;   // bytes
             // the descriptors end at the last valid key: rows past it read zeros
-            const int nbytes = ok ? (int)(((int64_t)(rh - 1) * hd_k + D) * 2) : 0;
-            kr[h] = buffer_rsrc(ok ? p.k + row0 : p.k, nbytes);
-            vr[h] = buffer_rsrc(ok ? p.v + row0 : p.v, nbytes);
+            const int nbytes = ok ? (int)(((int64_t)(rh - 1) * hd_k + D) * L::EB) : 0;
+            kr[h] = buffer_rsrc(ok ? kbase + row0 : kbase, nbytes);
+            vr[h] = buffer_rsrc(ok ? vbase + row0 : vbase, nbytes);
         }
-        __bf16 *dst = ring + lstage * L::STAGE;
+        unsigned char *dst = ring + lstage * L::STAGE;
 #pragma unroll
         for (int pp = 0; pp < 2 * L::LOADS; ++pp) {
             const int m = pp % L::LOADS;
-            const int h = (m * (512 / D)) / (TK / 2);          // rows of load m: m * 512/D ..
+            const int h = (m * (1024 / L::RB)) / 16;          // rows of load m: m * 1024/RB ..
             buffer_lds_dma16(pp >= L::LOADS ? vr[h] : kr[h], goff[pp],
-                             dst + (pp >= L::LOADS ? L::T_ELEMS : 0) + 512 * m);
+                             dst + (pp >= L::LOADS ? L::T_BYTES : 0) + 1024 * m);
         }
-        lstage ^= 1;
+        lstage = (lstage + 1) & (L::STAGES - 1);
         ++lt;
         ++lcnt;
         lskip();
@@ -201,27 +244,47 @@ void attn_decode_split_kernel(DecParams p) {
     // Query rows of an item (heads h0 .. h0+ncols-1, contiguous in memory),
     // as the B operand of S^T = K Q^T: column `col` is query head h0 + col.
     // The descriptor covers the item's heads only, so other columns are 0.
+    // bf16 caches: MFMA t contracts d = 16t .. 16t+15, lane half g holding
+    // 16t + 8g ..  fp8 caches: a lane reads 16 fp8 codes (two MFMAs' worth)
+    // of a key row at once, so MFMA u = 2t + j contracts d = 32t + 16g + 8j
+    // .. +7 in lane half g; the query takes the same order.
     auto load_q = [&](const Item &it, bf16x8 (&q)[D / 16]) {
         const __amdgpu_buffer_rsrc_t qr =
             buffer_rsrc(p.q + ((int64_t)it.b * p.Hq + it.h0) * D, it.ncols * D * 2);
-        const uint32_t o0 = (uint32_t)((col * D + 8 * g) * 2);
+        const uint32_t o0 = (uint32_t)((col * D + (F8 ? 16 : 8) * g) * 2);
 #pragma unroll
-        for (int t = 0; t < D / 16; ++t)
-            q[t] = __builtin_bit_cast(bf16x8, __builtin_amdgcn_raw_buffer_load_b128(qr, o0 + 32 * t, 0, 0));
+        for (int t = 0; t < D / 16; ++t) {
+            const uint32_t ot = F8 ? 64 * (t >> 1) + 16 * (t & 1) : 32 * t;
+            q[t] = __builtin_bit_cast(bf16x8, __builtin_amdgcn_raw_buffer_load_b128(qr, o0 + ot, 0, 0));
+        }
     };
 
-    // Per-lane operand offsets (elements, within a stage).  K: row col,
-    // logical chunk 2t + g.  V: the transposing read of keys 4g + e (+16kk,
-    // +8) and columns 32*db + 16*dh + 4*s.
-    int kof[D / 16];
+    // Per-lane operand offsets (bytes, within a stage).
+    //  K (bf16): row col, logical chunk 2t + g.  K (fp8): row col, logical
+    //  chunk 2t + g for MFMAs 2t and 2t+1 (low and high 8 bytes).
+    //  V (bf16): the transposing read of keys 4g + e (+16kk, +8) and columns
+    //  32*db + 16*dh + 4*s.  V (fp8): 16-lane group G reads keys
+    //  8(b/4) + 4g + b%4 (b = 0..7, two lanes per key, 8 bytes each) of the
+    //  16 columns 32*db + 16*(G%2) ..; lane i of the group receives column i,
+    //  in the key order of the P^T operand.
+    constexpr int NKO = F8 ? D / 32 : D / 16;
+    int kof[NKO];
 #pragma unroll
-    for (int t = 0; t < D / 16; ++t) kof[t] = col * D + 8 * ((2 * t + g) ^ swz_k<D>(col));
-    const int tr_e = (lane & 15) >> 2, tr_s = lane & 3, tr_dh = (lane >> 4) & 1;
+    for (int t = 0; t < NKO; ++t) kof[t] = col * L::RB + 16 * ((2 * t + g) ^ swz_k<D, F8>(col));
     int vof[D / 32];
+    if constexpr (F8) {
+        const int grp = lane >> 4, bi = (lane & 15) >> 1, hh = lane & 1;
+        const int vkey = 8 * (bi >> 2) + 4 * (grp >> 1) + (bi & 3);
 #pragma unroll
-    for (int db = 0; db < D / 32; ++db) {
-        const int vlc = 4 * db + 2 * tr_dh + (tr_s >> 1);
-        vof[db] = L::T_ELEMS + (4 * g + tr_e) * D + 8 * (vlc ^ swz_v<D>(tr_e)) + 4 * (tr_s & 1);
+        for (int db = 0; db < D / 32; ++db)
+            vof[db] = L::T_BYTES + vkey * L::RB + 16 * ((2 * db + (grp & 1)) ^ swz_v<D, F8>(vkey)) + 8 * hh;
+    } else {
+        const int tr_e = (lane & 15) >> 2, tr_s = lane & 3, tr_dh = (lane >> 4) & 1;
+#pragma unroll
+        for (int db = 0; db < D / 32; ++db) {
+            const int vlc = 4 * db + 2 * tr_dh + (tr_s >> 1);
+            vof[db] = L::T_BYTES + (4 * g + tr_e) * L::RB + 16 * (vlc ^ swz_v<D, F8>(tr_e)) + 8 * (tr_s & 1);
+        }
     }
 
     f32x16 oacc[D / 32];
@@ -230,11 +293,12 @@ void attn_decode_split_kernel(DecParams p) {
     const float c = p.c;
     bf16x8 qf[D / 16], qn[D / 16];
 
-    // The first item's query rows, then the first two tiles of the stream:
-    // the rows are older than both tiles, so the first tile wait covers them.
+    // The first item's query rows, then the first tiles of the stream (one
+    // per stage): the rows are older than every tile, so the first tile wait
+    // covers them.
     if (my_items > 0) load_q(get_item(0), qf);
-    issue_next();
-    issue_next();
+#pragma unroll
+    for (int i = 0; i < L::STAGES; ++i) issue_next();
 
     int cstage = 0;                              // stage of the tile being computed
     int ccnt = 0;                                // tiles computed so far
@@ -252,29 +316,50 @@ void attn_decode_split_kernel(DecParams p) {
         lsum = 0.f;
 
         for (int tw = 0; tw < nmine; ++tw) {
-            // this tile complete.  Loads complete in order, so when the next
-            // tile of the stream has been issued, everything but its loads
-            // (and anything issued after it) must be done; otherwise, and
+            // this tile complete.  Loads complete in order, so everything but
+            // the loads of the tiles issued after this one must be done;
             // after output stores (which share the counter), wait for all.
-            if (lcnt >= ccnt + 2 && !stores) wait_vmcnt<2 * L::LOADS>();
+            const int ahead = stores ? 0 : min(lcnt - ccnt - 1, L::STAGES - 1);
+            if (ahead >= 3) wait_vmcnt<3 * 2 * L::LOADS>();
+            else if (ahead == 2) wait_vmcnt<2 * 2 * L::LOADS>();
+            else if (ahead == 1) wait_vmcnt<2 * L::LOADS>();
             else wait_vmcnt<0>();
             stores = false;
-            const __bf16 *st = ring + cstage * L::STAGE;
+            const unsigned char *st = ring + cstage * L::STAGE;
 
-            // S^T for the tile's 32 keys
-            f32x16 s = f32x16{};
+            // S^T for the tile's keys, 32 at a time
+            f32x16 s[L::NB];
 #pragma unroll
-            for (int t = 0; t < D / 16; ++t) s = mfma32x32x16(ld_lds_bf16x8(st + kof[t]), qf[t], s);
+            for (int kb = 0; kb < L::NB; ++kb) {
+                s[kb] = f32x16{};
+                const unsigned char *sk = st + kb * 32 * L::RB;
+                if constexpr (F8) {
+#pragma unroll
+                    for (int t = 0; t < D / 32; ++t) {
+                        const u32x4 raw = *reinterpret_cast<const u32x4 *>(sk + kof[t]);
+                        s[kb] = mfma32x32x16(fp8x8_to_bf16(raw[0], raw[1]), qf[2 * t], s[kb]);
+                        s[kb] = mfma32x32x16(fp8x8_to_bf16(raw[2], raw[3]), qf[2 * t + 1], s[kb]);
+                    }
+                } else {
+#pragma unroll
+                    for (int t = 0; t < D / 16; ++t)
+                        s[kb] = mfma32x32x16(ld_lds_bf16x8((const __bf16 *)(sk + kof[t])), qf[t], s[kb]);
+                }
+            }
             const int kt = TK * (wave + NWV * tw);  // first key of the tile, within the item
             if (kt + TK > it.nkeys) {
 #pragma unroll
-                for (int r = 0; r < 16; ++r)
-                    if (kt + 8 * (r >> 2) + 4 * g + (r & 3) >= it.nkeys) s[r] = -__builtin_inff();
+                for (int kb = 0; kb < L::NB; ++kb)
+#pragma unroll
+                    for (int r = 0; r < 16; ++r)
+                        if (kt + 32 * kb + 8 * (r >> 2) + 4 * g + (r & 3) >= it.nkeys) s[kb][r] = -__builtin_inff();
             }
             // online softmax, lazy rescale (reference max moves by > kRescaleSlack)
             float mx = -__builtin_inff();
 #pragma unroll
-            for (int r = 0; r < 16; ++r) mx = fmaxf(mx, s[r]);
+            for (int kb = 0; kb < L::NB; ++kb)
+#pragma unroll
+                for (int r = 0; r < 16; ++r) mx = fmaxf(mx, s[kb][r]);
             const float mt = half_swap_max(mx) * c;
             const bool raise = mt > m + kRescaleSlack;
             if (__builtin_amdgcn_ballot_w64(raise)) {
@@ -290,27 +375,36 @@ void attn_decode_split_kernel(DecParams p) {
             const float m_use = m == -__builtin_inff() ? 0.f : m;
             float rs = 0.f;
 #pragma unroll
-            for (int r = 0; r < 16; ++r) {
-                s[r] = fast_exp2(__builtin_fmaf(s[r], c, -m_use));
-                rs += s[r];
-            }
+            for (int kb = 0; kb < L::NB; ++kb)
+#pragma unroll
+                for (int r = 0; r < 16; ++r) {
+                    s[kb][r] = fast_exp2(__builtin_fmaf(s[kb][r], c, -m_use));
+                    rs += s[kb][r];
+                }
             lsum += rs;
             // O^T += V^T P^T, 16 keys at a time, all D columns
 #pragma unroll
             for (int kk = 0; kk < TK / 16; ++kk) {
-                const bf16x8 pk = pack_p8(s, 8 * kk);
+                const bf16x8 pk = pack_p8(s[kk >> 1], 8 * (kk & 1));
 #pragma unroll
                 for (int db = 0; db < D / 32; ++db) {
-                    const s16x4 lo = lds_read_tr(st + vof[db] + 16 * kk * D);
-                    const s16x4 hi = lds_read_tr(st + vof[db] + (16 * kk + 8) * D);
-                    oacc[db] = mfma32x32x16(concat_tr(lo, hi), pk, oacc[db]);
+                    bf16x8 va;
+                    if constexpr (F8) {
+                        const u32x2 raw = lds_read_tr8(st + vof[db] + 16 * kk * L::RB);
+                        va = fp8x8_to_bf16(raw[0], raw[1]);
+                    } else {
+                        const s16x4 lo = lds_read_tr((const __bf16 *)(st + vof[db] + 16 * kk * L::RB));
+                        const s16x4 hi = lds_read_tr((const __bf16 *)(st + vof[db] + (16 * kk + 8) * L::RB));
+                        va = concat_tr(lo, hi);
+                    }
+                    oacc[db] = mfma32x32x16(va, pk, oacc[db]);
                 }
             }
             // the next item's query rows, ahead of this wave's next tile load
             if (tw == nmine - 1 && ci + 1 < my_items) load_q(get_item(ci + 1), qn);
             // this stage is consumed: refill it with the tile after next
             issue_next();
-            cstage ^= 1;
+            cstage = (cstage + 1) & (L::STAGES - 1);
             ++ccnt;
         }
         if (nmine == 0 && ci + 1 < my_items) load_q(get_item(ci + 1), qn);
@@ -334,7 +428,9 @@ void attn_decode_split_kernel(DecParams p) {
         }
         // weight of this wave's normalised output, times 1 / l for the
         // normalisation: exp2(lse2 - M) / wsum / l = exp2(m - M) / wsum
-        const float f = lt2 > 0.f ? fast_exp2(m - M) / wsum : 0.f;
+        // (times the value scale of an fp8 cache)
+        float f = lt2 > 0.f ? fast_exp2(m - M) / wsum : 0.f;
+        if constexpr (F8) f *= p.v_scale;
 #pragma unroll
         for (int db = 0; db < D / 32; ++db)
 #pragma unroll
@@ -424,7 +520,7 @@ __global__ __launch_bounds__(64) void attn_decode_combine_kernel(DecParams p) {
     if (p.lse != nullptr && t == 0) p.lse[bh] = lse;
 }
 
-template <int D>
+template <int D, bool F8>
 hipError_t launch_t(DecParams p, hipStream_t s) {
     int cus = 0;
     hipError_t e = current_cu_count(&cus);
@@ -444,7 +540,7 @@ hipError_t launch_t(DecParams p, hipStream_t s) {
     if (items > 0x7fffffff) return hipErrorInvalidConfiguration;
     const int blocks = (int)(items < cus ? items : cus);
     if (blocks <= 0) return hipSuccess;
-    hipLaunchKernelGGL((attn_decode_split_kernel<D>), dim3((unsigned)blocks), dim3(NT), 0, s, p);
+    hipLaunchKernelGGL((attn_decode_split_kernel<D, F8>), dim3((unsigned)blocks), dim3(NT), 0, s, p);
     e = hipGetLastError();
     if (e != hipSuccess || p.nsplit == 1) return e;
     hipLaunchKernelGGL(attn_decode_combine_kernel<D>, dim3((unsigned)(p.B * p.Hq)), dim3(64), 0,
@@ -454,9 +550,14 @@ hipError_t launch_t(DecParams p, hipStream_t s) {
 
 }  // namespace
 
-hipError_t launch_decode(const DecParams &p, int d, hipStream_t s) {
-    if (d == 128) return launch_t<128>(p, s);
-    if (d == 64) return launch_t<64>(p, s);
+hipError_t launch_decode(const DecParams &p, int d, bool fp8, hipStream_t s) {
+    if (fp8) {
+        if (d == 128) return launch_t<128, true>(p, s);
+        if (d == 64) return launch_t<64, true>(p, s);
+    } else {
+        if (d == 128) return launch_t<128, false>(p, s);
+        if (d == 64) return launch_t<64, false>(p, s);
+    }
     return hipErrorInvalidValue;
 }
 

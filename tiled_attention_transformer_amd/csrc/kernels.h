@@ -23,10 +23,9 @@ constexpr int kFwdThreads = 64 * kFwdWaves;
 constexpr int kFwdBr = 32 * kFwdWaves;
 constexpr int kFwdBc = 64;
 
-// Decode: 4 waves per workgroup, 64-key tiles; one work item serves up to
-// 32 query heads of one KV head.
+// Decode: 4 waves per workgroup; one work item serves up to 32 query heads
+// of one KV head.
 constexpr int kDecThreads = 256;
-constexpr int kDecBc = 64;
 constexpr int kDecCols = 32;
 
 // Compute units of the current device.  Cached per device after the first
@@ -68,7 +67,8 @@ struct FwdParams {
 };
 
 struct DecParams {
-    const __bf16 *q, *k, *v;
+    const __bf16 *q;
+    const void *k, *v;       // bf16, or fp8 (e4m3fn) codes for an fp8 cache
     __bf16 *o;
     float *lse;              // may be null
     float *ws_o, *ws_lse;    // split partials (null when nsplit == 1)
@@ -81,10 +81,11 @@ struct DecParams {
     int B, Hq, Hkv, group, Skv;
     int ncb;                 // blocks of <= 32 query heads per KV head
     int nsplit, chunk;       // key chunks and keys per chunk
-    float c;                 // scale * log2(e)
+    float c;                 // scale * log2(e) (times the key scale of an fp8 cache)
+    float v_scale;           // value scale of an fp8 cache (unused for bf16)
 };
 
 hipError_t launch_fwd(const FwdParams &p, int d, bool causal, bool varlen, hipStream_t s);
-hipError_t launch_decode(const DecParams &p, int d, hipStream_t s);
+hipError_t launch_decode(const DecParams &p, int d, bool fp8, hipStream_t s);
 
 }  // namespace attn

@@ -78,6 +78,18 @@ __device__ __forceinline__ s16x4 lds_read_tr(const __bf16 *__restrict__ p) {
     return __builtin_amdgcn_ds_read_tr16_b64_v4i16((lds_s16x4 *)(p));
 }
 
+// LDS transpose read of bytes (ds_read_b64_tr_b8).  Within each group of 16
+// lanes, lanes 2b and 2b+1 point at bytes 0..7 and 8..15 of "row" b
+// (b = 0..7); lane i of the group then receives byte i of rows 0..7, row b in
+// byte b.  Used to fetch 8 keys of one value column from a row-major fp8 V
+// tile.
+__device__ __forceinline__ u32x2 lds_read_tr8(const unsigned char *__restrict__ p) {
+    typedef int i32x2 __attribute__((ext_vector_type(2)));
+    typedef __attribute__((address_space(3))) i32x2 lds_i32x2;
+    const i32x2 r = __builtin_amdgcn_ds_read_tr8_b64_v2i32((lds_i32x2 *)(p));
+    return __builtin_bit_cast(u32x2, r);
+}
+
 __device__ __forceinline__ bf16x8 concat_tr(s16x4 lo, s16x4 hi) {
     typedef short s16x8 __attribute__((ext_vector_type(8)));
     s16x8 v = __builtin_shufflevector(lo, hi, 0, 1, 2, 3, 4, 5, 6, 7);
