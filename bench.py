@@ -97,28 +97,30 @@ def write_traffic(fetch_dir: str, write_dir: str):
     import glob
 
     def per_kernel(d, counter):
+        """kernel name -> counter values of its dispatches"""
         (path,) = glob.glob(os.path.join(d, "**", "*counter_collection.csv"), recursive=True)
         acc = {}
         for r in csv.DictReader(open(path)):
             if r["Counter_Name"] != counter:
                 continue
             acc.setdefault(r["Kernel_Name"], []).append(float(r["Counter_Value"]))
-        return {k: sum(v) / len(v) for k, v in acc.items()}
+        return acc
 
-    fetch, write = per_kernel(fetch_dir, "FETCH_SIZE"), per_kernel(write_dir, "WRITE_SIZE")
+    fetch_all, write_all = per_kernel(fetch_dir, "FETCH_SIZE"), per_kernel(write_dir, "WRITE_SIZE")
+    fetch = {k: sum(v) / len(v) for k, v in fetch_all.items()}
+    write = {k: sum(v) / len(v) for k, v in write_all.items()}
     copy_kib = float(1 << 20)
 
     def copy_value(d):
-        # the runtime's device-to-device copy kernel; dtype conversions made
-        # while preparing inputs are elementwise "copy" kernels of torch
-        vals = [v for k, v in d.items() if "copyBuffer" in k]
-        if not vals:
-            vals = [v for k, v in d.items() if "copy" in k.lower()]
+        # the 1 GiB calibration copy: the largest dispatch of the runtime's
+        # device-to-device copy kernel (the run makes a few small copies
+        # too; torch's dtype conversions are elementwise kernels)
+        vals = [max(v) for k, v in d.items() if "copyBuffer" in k]
         if len(vals) != 1:
-            sys.exit("expected exactly one copy kernel in the counter run")
+            sys.exit("expected exactly one device copy kernel in the counter run")
         return vals[0]
 
-    f_scale, w_scale = copy_kib / copy_value(fetch), copy_kib / copy_value(write)
+    f_scale, w_scale = copy_kib / copy_value(fetch_all), copy_kib / copy_value(write_all)
     out = {"kernel_hash": kernel_hash(),
            "calibration": {"fetch_scale": round(f_scale, 4), "write_scale": round(w_scale, 4),
                            "copy_bytes": 1 << 30}}
