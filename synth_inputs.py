@@ -17,6 +17,11 @@ Recipe (one ``numpy.random.default_rng(seed)`` stream per workload):
   stored as the FP8 E4M3 ("e4m3fn") codes of ``x / scale`` clipped to
   [-448, 448], rounded to nearest by torch's float8_e4m3fn conversion (a
   per-tensor quantiser of the usual kind; the codes span the format's range).
+* k-means assignment: a Gaussian mixture with one component per centroid:
+  component means ``mu ~ N(0, 1)`` [K, d], labels ``integers(0, K, N)``,
+  points ``x = mu[label] + 0.5 * N(0, 1)`` [N, d] and centroids
+  ``c = mu + 0.25 * N(0, 1)`` [K, d] (a k-means state part way through its
+  iterations), drawn in that order in float32, each rounded once to bf16.
 * ragged batch: the 16 lengths are drawn first with
   ``integers(lo, hi + 1, nseq)`` (inclusive bounds), then q, k, v over the
   packed ``[total, H, d]`` layout.
@@ -31,6 +36,7 @@ import numpy as np
 __all__ = [
     "f32_to_bf16_bits", "bf16_to_f32", "bf16_to_f64", "CONFIGS",
     "make_prefill", "make_decode", "make_decode_fp8", "make_varlen", "make_config",
+    "make_kmeans",
 ]
 
 
@@ -121,6 +127,16 @@ def make_decode_fp8(seed, B, Hq, Hkv, Skv, d):
         out[name] = codes
         out[name + "_scale"] = float(sc)
     return out
+
+
+def make_kmeans(seed, N, K, d):
+    """Points x [N,d] and centroids c [K,d] as bf16 bit patterns (mixture recipe above)."""
+    rng = np.random.default_rng(seed)
+    mu = rng.standard_normal((K, d), dtype=np.float32)
+    label = rng.integers(0, K, N)
+    x = mu[label] + np.float32(0.5) * rng.standard_normal((N, d), dtype=np.float32)
+    c = mu + np.float32(0.25) * rng.standard_normal((K, d), dtype=np.float32)
+    return dict(x=f32_to_bf16_bits(x), c=f32_to_bf16_bits(c), label=label)
 
 
 def make_paged(seed, B, Hq, Hkv, d, page_size, max_pages, num_pages):

@@ -67,3 +67,11 @@ def test_fp8_cache_generator():
         assert a[n + "_scale"] > 0 and np.isfinite(a[n + "_scale"])
         # the scale is float32: max|x| / 448
         assert np.float32(a[n + "_scale"]) == a[n + "_scale"]
+
+
+def test_kmeans_generator():
+    a = si.make_kmeans(2, 100, 7, 16)
+    b = si.make_kmeans(2, 100, 7, 16)
+    assert np.array_equal(a["x"], b["x"]) and np.array_equal(a["c"], b["c"])
+    assert a["x"].shape == (100, 16) and a["c"].shape == (7, 16) and a["x"].dtype == np.uint16
+    assert a["label"].min() >= 0 and a["label"].max() < 7

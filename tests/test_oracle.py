@@ -527,3 +527,82 @@ def test_decode_fp8_brute_force_one_row():
             want = sum(w[j] * vs * vd[0, j, 0, t] for j in range(6)) / tot
             assert abs(o[0, h, t] - want) < 1e-12
         assert abs(lse[0, h] - (m + math.log(tot))) < 1e-12
+
+
+# ------------------------------------------------- k-means assignment
+
+def _km(seed=3, N=200, K=37, d=16):
+    data = si.make_kmeans(seed, N, K, d)
+    return si.bf16_to_f64(data["x"]), si.bf16_to_f64(data["c"])
+
+
+def test_kmeans_brute_force_python_loops():
+    """Nearest centroid by plain Python loops over points, centroids and coordinates."""
+    x, c = _km(N=25, K=9, d=5)
+    idx, dist = ref.kmeans_assign(x, c)
+    for n in range(25):
+        best, best_k = None, None
+        for k in range(9):
+            s = 0.0
+            for i in range(5):
+                s += (x[n, i] - c[k, i]) ** 2
+            if best is None or s < best:
+                best, best_k = s, k
+        assert idx[n] == best_k and abs(dist[n] - best) <= 1e-12 * max(1.0, best)
+
+
+def test_kmeans_distance_expansion_identity():
+    """|x - c|^2 = |x|^2 + |c|^2 - 2 x.c (checked through a matrix product)."""
+    x, c = _km()
+    D = ref.kmeans_distances(x, c)
+    E = (x * x).sum(1)[:, None] + (c * c).sum(1)[None, :] - 2.0 * (x @ c.T)
+    assert np.allclose(D, E, rtol=1e-12, atol=1e-10)
+    assert np.all(D >= 0)
+
+
+def test_kmeans_one_dimension_nearest_on_a_line():
+    """d = 1: the nearest centroid found by bisection in the sorted centroid list."""
+    rng = np.random.default_rng(4)
+    c = np.unique(rng.standard_normal(50))[:, None]          # sorted, distinct
+    x = rng.standard_normal(400)[:, None] * 1.5
+    idx, dist = ref.kmeans_assign(x, c)
+    cs = c[:, 0]
+    j = np.clip(np.searchsorted(cs, x[:, 0]), 1, len(cs) - 1)
+    left, right = cs[j - 1], cs[j]
+    pick = np.where(np.abs(x[:, 0] - left) <= np.abs(right - x[:, 0]), j - 1, j)
+    assert np.array_equal(idx, pick)
+    assert np.allclose(dist, (x[:, 0] - cs[pick]) ** 2, rtol=0, atol=1e-15)
+
+
+def test_kmeans_ties_go_to_the_lowest_index():
+    """Duplicated centroids: the first copy wins; a point on a centroid has distance 0."""
+    x, c = _km(N=60, K=10, d=8)
+    c2 = np.concatenate([c[:3], c[5:6], c[3:]])              # centroid 5 also at index 3
+    idx, dist = ref.kmeans_assign(x, c2)
+    base, bd = ref.kmeans_assign(x, c)
+    want = np.where(base < 3, base, np.where(base == 5, 3, base + 1))
+    assert np.array_equal(idx, want) and np.array_equal(dist, bd)
+    on, d0 = ref.kmeans_assign(c2[[6, 3, 0]], c2)
+    assert list(on) == [3, 3, 0] and np.all(d0 == 0)
+
+
+def test_kmeans_permutation_translation_and_scaling():
+    """Relabelled centroids relabel the answer; a common shift or scale changes
+    no assignment (scale a multiplies the distances by a^2)."""
+    x, c = _km()
+    idx, dist = ref.kmeans_assign(x, c)
+    perm = np.random.default_rng(5).permutation(c.shape[0])
+    ip, dp = ref.kmeans_assign(x, c[perm])
+    assert np.array_equal(perm[ip], idx) and np.allclose(dp, dist, rtol=1e-13)
+    t = np.random.default_rng(6).standard_normal(c.shape[1]) * 3
+    it, dt = ref.kmeans_assign(x + t, c + t)
+    assert np.array_equal(it, idx) and np.allclose(dt, dist, rtol=1e-9, atol=1e-9)
+    isc, dsc = ref.kmeans_assign(4.0 * x, 4.0 * c)
+    assert np.array_equal(isc, idx) and np.allclose(dsc, 16.0 * dist, rtol=1e-13)
+
+
+def test_kmeans_mixture_recovers_labels():
+    """Well separated mixture (the input recipe): every point goes to its own component."""
+    data = si.make_kmeans(8, 500, 20, 64)
+    idx, _ = ref.kmeans_assign(si.bf16_to_f64(data["x"]), si.bf16_to_f64(data["c"]))
+    assert np.array_equal(idx, data["label"])
