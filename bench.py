@@ -151,8 +151,9 @@ def write_traffic(fetch_dir: str, write_dir: str):
 def extra_workloads(api, dev, stream, which="all", calls=5, dec_ms=None):
     """Context lines beside the headline: the long causal workload (B1 H32
     S16384 d128), the ragged causal batch (16 sequences, lengths drawn
-    U{128..8192} with seed 5, H32 d128) and the decode workload's sizes with
-    an fp8 (e4m3fn) KV cache.  Timing only: the inputs are seeded N(0,1)
+    U{128..8192} with seed 5, H32 d128), the decode workload's sizes with
+    an fp8 (e4m3fn) KV cache, and the fused k-means assignment (N=65536,
+    K=1024, d=128; algorithmic FLOP 2*N*K*d).  Timing only: the inputs are seeded N(0,1)
     draws made on the GPU (the lengths follow the same recipe as the test
     inputs); K of the long workload is scaled per head by U(0.5, 2) as in its
     test recipe; the fp8 cache holds the codes of x / (max|x| / 448) per
@@ -202,6 +203,24 @@ def extra_workloads(api, dev, stream, which="all", calls=5, dec_ms=None):
     del q, codes, o, lse, ws
     if which == "fp8":
         return out
+
+    # fused k-means assignment (N=65536 points, K=1024 centroids, d=128: the
+    # Flash-KMeans article's assignment workload), mixture recipe as in the tests
+    gen.manual_seed(7)
+    N, K = 65536, 1024
+    mu = torch.randn((K, d), generator=gen, device=dev, dtype=torch.float32)
+    lab = torch.randint(0, K, (N,), generator=gen, device=dev)
+    x = (mu[lab] + 0.5 * torch.randn((N, d), generator=gen, device=dev)).to(torch.bfloat16)
+    c = (mu + 0.25 * torch.randn((K, d), generator=gen, device=dev)).to(torch.bfloat16)
+    idx = torch.empty(N, dtype=torch.int32, device=dev)
+    dist = torch.empty(N, dtype=torch.float32, device=dev)
+    ms = timed(lambda: api.attn_kmeans_assign(x, c, idx=idx, dist=dist, stream=stream))
+    fl = 2.0 * N * K * d
+    out["kmeans_assign_N65536_K1024_d128"] = {
+        "ms": round(ms, 5), "TFLOP/s": round(fl / (ms * 1e-3) / 1e12, 1),
+        "frac_of_2500": round(fl / (ms * 1e-3) / 1e12 / PEAK_BF16_TFLOPS, 4),
+        "algorithmic_flop": fl, "kernel": "kmeans_assign_kernel<128>"}
+    del mu, lab, x, c, idx, dist
 
     # long causal prefill
     gen.manual_seed(3)

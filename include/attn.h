@@ -214,6 +214,26 @@ attn_status_t attn_decode_fp8(const void *q, const void *k_cache, const void *v_
                               int num_splits, void *workspace, size_t workspace_bytes,
                               hipStream_t stream);
 
+/*
+ * Fused k-means assignment (FlashAssign): for every point, the nearest
+ * centroid in squared Euclidean distance, without writing the N x K
+ * distance matrix (lefilia.fr, "Flash-KMeans : un K-Means exact et optimisé
+ * pour les E/S, plus de 200 fois plus rapide que FAISS sur GPU", the
+ * paragraph on the assignment phase).
+ *   x    : [N, d] bf16 points          c : [K, d] bf16 centroids
+ *   idx  : [N] int32, idx[n] = argmin_k |x_n - c_k|^2; among equal computed
+ *          distances the lowest k
+ *   dist : [N] fp32 (or NULL), |x_n - c_idx[n]|^2 (clamped at 0)
+ * The distance is compared as |c_k|^2 - 2 x_n . c_k with fp32 accumulation
+ * of bf16 products (|x_n|^2 is common to all k); dist adds |x_n|^2.  d must
+ * be 64 or 128; N, K >= 1.  x and c 16-byte aligned, idx and dist 4-byte
+ * aligned.  No workspace; deterministic.  Errors: ATTN_ERR_NULLPTR (x, c or
+ * idx NULL), ATTN_ERR_SHAPE, ATTN_ERR_UNSUPPORTED_D, ATTN_ERR_ALIGNMENT,
+ * ATTN_ERR_HIP.
+ */
+attn_status_t attn_kmeans_assign(const void *x, const void *c, int *idx, float *dist, int N, int K,
+                                 int d, hipStream_t stream);
+
 /* Bytes of decode workspace for these sizes (0 when num_splits resolves to
  * 1; num_splits <= 0 means the library's choice, as in attn_decode).  Returns
  * 0 for invalid sizes. */

@@ -33,7 +33,7 @@ def lib():
 
 def test_library_exports_every_declared_symbol(lib):
     names = declared_functions()
-    assert len(names) == 10, names
+    assert len(names) == 11, names
     raw = ctypes.CDLL(_lib.LIB_PATH)
     for n in names:
         assert hasattr(raw, n), n
@@ -195,6 +195,24 @@ def test_decode_fp8_validation(lib):
     assert decode_fp8(lib, scale=1e-30, ks=1e-30) == SCALE    # product underflows to 0
     assert decode_fp8(lib, ws=None) == WS
     assert decode_fp8(lib, wsb=16) == WS
+
+
+def kmeans(lib, x=P, c=P, idx=P, dist=P, N=1000, K=64, d=128):
+    return lib.attn_kmeans_assign(x, c, idx, dist, N, K, d, None)
+
+
+def test_kmeans_assign_validation(lib):
+    assert kmeans(lib, x=None) == NULLPTR
+    assert kmeans(lib, c=None) == NULLPTR
+    assert kmeans(lib, idx=None) == NULLPTR
+    assert kmeans(lib, N=0) == SHAPE
+    assert kmeans(lib, K=-1) == SHAPE
+    assert kmeans(lib, d=96) == BAD_D
+    assert kmeans(lib, d=256) == BAD_D
+    assert kmeans(lib, x=P + 8) == ALIGN
+    assert kmeans(lib, c=P + 4) == ALIGN
+    assert kmeans(lib, idx=P + 2) == ALIGN
+    assert kmeans(lib, dist=P + 1) == ALIGN
 
 
 def test_decode_split_choice(lib):

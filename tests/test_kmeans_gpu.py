@@ -1,0 +1,156 @@
+"""GPU parity of the fused k-means assignment against the fp64 oracle.
+
+The kernel compares |c|^2 - 2 x.c in fp32 (bf16 inputs, fp32 accumulation);
+the oracle takes exact distances.  An index is therefore checked in two
+ways: where the oracle's best and second-best distances are further apart
+than twice the kernel's rounding bound, the index must equal the oracle's;
+elsewhere the chosen centroid's exact distance must lie within that bound
+of the minimum.  Exact ties (duplicated centroids) must go to the lowest
+index.  The reported distance must match the exact distance of the chosen
+centroid within the bound.
+"""
+import numpy as np
+import pytest
+
+import synth_inputs as si
+from oracle import ref
+from tests.gpu_util import to_dev
+
+pytestmark = pytest.mark.gpu
+
+U32 = 2.0 ** -24      # fp32 unit roundoff
+
+
+@pytest.fixture(scope="module")
+def api():
+    from tiled_attention_transformer_amd import api as a
+    a._lib.load()
+    return a
+
+
+def _run(api, dev, x_bits, c_bits):
+    import torch
+    idx, dist = api.attn_kmeans_assign(to_dev(x_bits, dev), to_dev(c_bits, dev))
+    torch.cuda.synchronize()
+    return idx.cpu().numpy().astype(np.int64), dist.cpu().numpy().astype(np.float64)
+
+
+def _bound(x, c):
+    """Per-point bound on the kernel's fp32 error in |c|^2 - 2 x.c (and in the
+    reported distance): 4 d u (|x|^2 + 2 |x| max|c| + max|c|^2)."""
+    d = x.shape[1]
+    nx = np.sqrt((x * x).sum(1))
+    nc = np.sqrt((c * c).sum(1)).max()
+    return 4.0 * d * U32 * (nx * nx + 2.0 * nx * nc + nc * nc)
+
+
+def check(idx, dist, x, c, what, points=None):
+    """idx/dist of the points `points` (all when None) against the oracle."""
+    if points is None:
+        points = np.arange(x.shape[0])
+    xs = x[points]
+    D = ref.kmeans_distances(xs, c)
+    o_idx = np.argmin(D, axis=1)
+    dmin = D[np.arange(len(points)), o_idx]
+    B = _bound(xs, c)
+    got = idx[points]
+    assert np.all((got >= 0) & (got < c.shape[0])), what + ": index out of range"
+    chosen = D[np.arange(len(points)), got]
+    assert np.all(chosen - dmin <= 2 * B), what + ": chosen centroid not nearest within the bound"
+    if c.shape[0] > 1:
+        part = np.partition(D, 1, axis=1)
+        clear = part[:, 1] - part[:, 0] > 4 * B
+    else:
+        clear = np.ones(len(points), dtype=bool)
+    mism = np.nonzero(clear & (got != o_idx))[0]
+    assert mism.size == 0, "%s: %d clear-cut points differ (first %s)" % (what, mism.size, points[mism[:5]])
+    assert np.all(np.abs(dist[points] - chosen) <= 2 * B), what + ": distance off"
+    return float(clear.mean())
+
+
+KMEANS = [  # N, K, d
+    (1000, 37, 128),       # one partial centroid tile; ragged point tile
+    (256, 64, 128),        # exactly one tile each way
+    (257, 65, 64),         # one point / one centroid past a tile
+    (1, 1, 128),           # a single point and centroid
+    (3000, 1, 64),         # one centroid: every index 0
+    (700, 300, 64),        # several tiles, ragged
+    (5000, 1024, 128),     # the page's K and d
+    (4096, 2000, 128),     # centroid count not a multiple of 64
+]
+
+
+@pytest.mark.parametrize("case", KMEANS, ids=lambda c: "N%d_K%d_d%d" % c)
+def test_kmeans_assign_matches_oracle(api, dev, case):
+    N, K, d = case
+    data = si.make_kmeans(100 + N + K, N, K, d)
+    idx, dist = _run(api, dev, data["x"], data["c"])
+    x, c = si.bf16_to_f64(data["x"]), si.bf16_to_f64(data["c"])
+    frac = check(idx, dist, x, c, str(case))
+    assert frac > 0.99, "the mixture should be clear-cut for nearly every point"
+
+
+def test_kmeans_workload_sampled_points(api, dev):
+    """N = 65536 points, K = 1024 centroids, d = 128 (the page's assignment
+    workload), every output checked for range and 2048 sampled points against
+    the oracle."""
+    N, K, d = 65536, 1024, 128
+    data = si.make_kmeans(7, N, K, d)
+    idx, dist = _run(api, dev, data["x"], data["c"])
+    assert np.all((idx >= 0) & (idx < K)) and np.all(np.isfinite(dist)) and np.all(dist >= 0)
+    pts = np.unique(np.concatenate([np.arange(0, 300), np.arange(N - 300, N),
+                                    np.random.default_rng(1).integers(0, N, 1448)]))
+    x, c = si.bf16_to_f64(data["x"]), si.bf16_to_f64(data["c"])
+    check(idx, dist, x, c, "workload", points=pts)
+    # on this well separated mixture every point goes to its own component
+    assert np.mean(idx == data["label"]) > 0.999
+
+
+def test_kmeans_duplicated_centroids_pick_the_lowest_index(api, dev):
+    """Bit-identical centroid rows give bit-identical computed distances, so an
+    exact tie must go to the lowest index -- across tiles, 32-row blocks and the
+    two lane halves."""
+    N, K, d = 2000, 300, 128
+    data = si.make_kmeans(21, N, K, d)
+    c = data["c"].copy()
+    pairs = [(5, 40), (5, 77), (3, 100), (70, 64), (131, 290), (2, 6), (33, 32 + 64 * 2)]
+    for lo, hi in pairs:
+        c[hi] = c[lo]
+    idx, dist = _run(api, dev, data["x"], c)
+    x, cf = si.bf16_to_f64(data["x"]), si.bf16_to_f64(c)
+    check(idx, dist, x, cf, "duplicates")
+    losers = [max(a, b) for a, b in pairs]                    # the higher copy of each pair
+    assert not np.any(np.isin(idx, losers)), "a higher copy of a duplicated centroid won"
+    # the points of a copied component (label = the source row) now tie
+    # between the copies and must go to the lower one
+    for src, dst in pairs:
+        assert np.all(idx[data["label"] == src] == min(src, dst))
+
+
+def test_kmeans_points_on_centroids(api, dev):
+    """Points equal to centroids go to them (or to a lower identical copy) with
+    distance ~0."""
+    K, d = 200, 64
+    data = si.make_kmeans(22, 10, K, d)
+    pick = np.array([0, 1, 63, 64, 65, 127, 128, 199] * 40)
+    idx, dist = _run(api, dev, data["c"][pick], data["c"])
+    assert np.array_equal(idx, pick)
+    c = si.bf16_to_f64(data["c"])
+    assert np.all(dist <= _bound(c[pick], c))
+
+
+def test_kmeans_bitwise_deterministic(api, dev):
+    data = si.make_kmeans(23, 3000, 500, 128)
+    a = _run(api, dev, data["x"], data["c"])
+    b = _run(api, dev, data["x"], data["c"])
+    assert np.array_equal(a[0], b[0]) and np.array_equal(a[1], b[1])
+
+
+def test_kmeans_dist_optional(api, dev):
+    import torch
+    data = si.make_kmeans(24, 500, 70, 128)
+    x, c = to_dev(data["x"], dev), to_dev(data["c"], dev)
+    i1, d1 = api.attn_kmeans_assign(x, c)
+    i2, d2 = api.attn_kmeans_assign(x, c, want_dist=False)
+    torch.cuda.synchronize()
+    assert d2 is None and torch.equal(i1, i2)

@@ -22,6 +22,7 @@ SIGNATURES = {
                                _p, _sz, _p]),
     "attn_decode_fp8": (_i, [_p, _p, _p, _p, _p, _p, _i, _i, _i, _i, _i, _f, _f, _f, _i, _p, _sz,
                              _p]),
+    "attn_kmeans_assign": (_i, [_p, _p, _p, _p, _i, _i, _i, _p]),
     "attn_decode_workspace_bytes": (_sz, [_i, _i, _i, _i, _i, _i]),
     "attn_decode_pick_splits": (_i, [_i, _i, _i, _i]),
     "attn_status_string": (ctypes.c_char_p, [_i]),

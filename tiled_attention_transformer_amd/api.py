@@ -264,6 +264,34 @@ def attn_decode_fp8(q, k_cache, v_cache, k_scale, v_scale, seqlens_k=None, o=Non
     return o, lse
 
 
+def attn_kmeans_assign(x, c, idx=None, dist=None, want_dist=True, stream=None):
+    """Nearest centroid of every point; returns ``(idx, dist)``.
+
+    x ``[N,d]`` and c ``[K,d]`` bf16 GPU tensors; idx ``[N]`` int32, dist
+    ``[N]`` fp32 (squared distance to the chosen centroid, or None when
+    ``want_dist`` is false).
+    """
+    _need(x, "x", torch.bfloat16, 2)
+    _need(c, "c", torch.bfloat16, 2)
+    N, d = x.shape
+    K = c.shape[0]
+    if c.shape[1] != d:
+        raise ValueError("x and c must have the same dimension")
+    if idx is None:
+        idx = torch.empty(N, dtype=torch.int32, device=x.device)
+    _need(idx, "idx", torch.int32, 1)
+    if dist is None and want_dist:
+        dist = torch.empty(N, dtype=torch.float32, device=x.device)
+    if dist is not None:
+        _need(dist, "dist", torch.float32, 1)
+    if idx.shape[0] != N or (dist is not None and dist.shape[0] != N):
+        raise ValueError("idx and dist must have one entry per point")
+    st = _lib.load().attn_kmeans_assign(_ptr(x), _ptr(c), _ptr(idx), _ptr(dist), N, K, d,
+                                        _stream(stream))
+    _check(st, "attn_kmeans_assign")
+    return idx, dist
+
+
 def _decode(q, k_cache, v_cache, seqlens_k, o, lse, scale, num_splits, workspace, want_lse,
             stream):
     _need(q, "q", torch.bfloat16, 3)

@@ -10,7 +10,7 @@ HERE = os.path.dirname(os.path.abspath(__file__))
 CSRC = os.path.join(HERE, "csrc")
 BUILD = os.path.join(HERE, "_build")
 LIB = os.path.join(HERE, "libattn.so")
-SOURCES = ["attn_fwd.hip", "attn_decode.hip", "attn_api.hip"]
+SOURCES = ["attn_fwd.hip", "attn_decode.hip", "kmeans_assign.hip", "attn_api.hip"]
 HIPCC = os.environ.get("HIPCC", "/opt/rocm/bin/hipcc")
 
 # Packed fp32 vector instructions are kept out of the generated code.

@@ -302,4 +302,22 @@ attn_status_t attn_decode_fp8(const void *q, const void *k_cache, const void *v_
                        num_splits, workspace, workspace_bytes, stream, nullptr, &f);
 }
 
+attn_status_t attn_kmeans_assign(const void *x, const void *c, int *idx, float *dist, int N, int K,
+                                 int d, hipStream_t stream) {
+    if (!x || !c || !idx) return ATTN_ERR_NULLPTR;
+    if (N < 1 || K < 1 || (int64_t)N * d > kMaxElems || (int64_t)K * d > kMaxElems)
+        return ATTN_ERR_SHAPE;
+    if (!d_ok(d)) return ATTN_ERR_UNSUPPORTED_D;
+    if (!aligned(x, 16) || !aligned(c, 16) || !aligned(idx, 4) || (dist && !aligned(dist, 4)))
+        return ATTN_ERR_ALIGNMENT;
+    attn::AssignParams p{};
+    p.x = (const __bf16 *)x;
+    p.c = (const __bf16 *)c;
+    p.idx = idx;
+    p.dist = dist;
+    p.N = N;
+    p.K = K;
+    return from_hip(attn::launch_kmeans_assign(p, d, stream));
+}
+
 }  // extern "C"

@@ -85,7 +85,16 @@ struct DecParams {
     float v_scale;           // value scale of an fp8 cache (unused for bf16)
 };
 
+// k-means assignment: nearest centroid of every point
+struct AssignParams {
+    const __bf16 *x, *c;     // points [N, d], centroids [K, d]
+    int *idx;                // [N]
+    float *dist;             // [N], may be null
+    int N, K;
+};
+
 hipError_t launch_fwd(const FwdParams &p, int d, bool causal, bool varlen, hipStream_t s);
 hipError_t launch_decode(const DecParams &p, int d, bool fp8, hipStream_t s);
+hipError_t launch_kmeans_assign(const AssignParams &p, int d, hipStream_t s);
 
 }  // namespace attn
