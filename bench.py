@@ -68,9 +68,10 @@ TRAFFIC_PATH = os.path.join(ROOT, "profiles", "traffic.json")
 TRAFFIC_KERNELS = {"prefill": ["attn_fwd_kernel<128, true, false>"],
                    "decode": ["attn_decode_split_kernel<128, false>",
                               "attn_decode_combine_kernel<128>"],
-                   "decode_fp8": ["attn_decode_split_kernel<128, true>"]}
-# paths whose kernels only run with the fp8 extra (absent from a run without it)
-TRAFFIC_OPTIONAL = {"decode_fp8"}
+                   "decode_fp8": ["attn_decode_split_kernel<128, true>"],
+                   "kmeans": ["kmeans_assign_kernel<128>"]}
+# paths whose kernels only run with a context line (absent from a run without it)
+TRAFFIC_OPTIONAL = {"decode_fp8", "kmeans"}
 
 
 def load_traffic(kind: str):
@@ -148,7 +149,10 @@ def write_traffic(fetch_dir: str, write_dir: str):
     print(json.dumps(out))
 
 
-def extra_workloads(api, dev, stream, which="all", calls=5, dec_ms=None):
+EXTRAS = ("fp8", "kmeans", "long", "ragged")
+
+
+def extra_workloads(api, dev, stream, which=EXTRAS, calls=5, dec_ms=None):
     """Context lines beside the headline: the long causal workload (B1 H32
     S16384 d128), the ragged causal batch (16 sequences, lengths drawn
     U{128..8192} with seed 5, H32 d128), the decode workload's sizes with
@@ -157,8 +161,9 @@ def extra_workloads(api, dev, stream, which="all", calls=5, dec_ms=None):
     draws made on the GPU (the lengths follow the same recipe as the test
     inputs); K of the long workload is scaled per head by U(0.5, 2) as in its
     test recipe; the fp8 cache holds the codes of x / (max|x| / 448) per
-    tensor, as the test recipe does.  ``which`` = "fp8" runs the fp8 decode
-    only."""
+    tensor, as the test recipe does; the k-means points and centroids follow
+    the test recipe's mixture.  ``which`` names the lines to run (a subset of
+    EXTRAS)."""
     import torch
     out = {}
     gen = torch.Generator(device=dev)
@@ -177,6 +182,19 @@ def extra_workloads(api, dev, stream, which="all", calls=5, dec_ms=None):
         return float(np.mean([a.elapsed_time(b) for a, b in ev]))
 
     # decode with an fp8 KV cache (the decode workload's sizes)
+    if "fp8" in which:
+        fp8_decode(api, dev, stream, gen, d, timed, out, dec_ms)
+    if "kmeans" in which:
+        kmeans_assign(api, dev, stream, gen, d, timed, out)
+    if "long" in which:
+        long_causal(api, dev, stream, gen, d, timed, out)
+    if "ragged" in which:
+        ragged_causal(api, dev, stream, gen, d, timed, out)
+    return out
+
+
+def fp8_decode(api, dev, stream, gen, d, timed, out, dec_ms):
+    import torch
     gen.manual_seed(4)
     B, Hq, Hkv, Skv = 64, 32, 8, 4096
     q = torch.randn((B, Hq, d), generator=gen, device=dev, dtype=torch.float32).to(torch.bfloat16)
@@ -201,11 +219,12 @@ def extra_workloads(api, dev, stream, which="all", calls=5, dec_ms=None):
         "kernel": "attn_decode_split_kernel<128, true>",
         "speedup_vs_bf16_cache": None if dec_ms is None else round(dec_ms / ms, 3)}
     del q, codes, o, lse, ws
-    if which == "fp8":
-        return out
 
-    # fused k-means assignment (N=65536 points, K=1024 centroids, d=128: the
-    # Flash-KMeans article's assignment workload), mixture recipe as in the tests
+
+def kmeans_assign(api, dev, stream, gen, d, timed, out):
+    """fused k-means assignment (N=65536 points, K=1024 centroids, d=128: the
+    Flash-KMeans article's assignment workload), mixture recipe as in the tests"""
+    import torch
     gen.manual_seed(7)
     N, K = 65536, 1024
     mu = torch.randn((K, d), generator=gen, device=dev, dtype=torch.float32)
@@ -219,10 +238,13 @@ def extra_workloads(api, dev, stream, which="all", calls=5, dec_ms=None):
     out["kmeans_assign_N65536_K1024_d128"] = {
         "ms": round(ms, 5), "TFLOP/s": round(fl / (ms * 1e-3) / 1e12, 1),
         "frac_of_2500": round(fl / (ms * 1e-3) / 1e12 / PEAK_BF16_TFLOPS, 4),
-        "algorithmic_flop": fl, "kernel": "kmeans_assign_kernel<128>"}
+        "algorithmic_flop": fl, "traffic": load_traffic("kmeans"),
+        "kernel": "kmeans_assign_kernel<128>"}
     del mu, lab, x, c, idx, dist
 
-    # long causal prefill
+
+def long_causal(api, dev, stream, gen, d, timed, out):
+    import torch
     gen.manual_seed(3)
     B, H, S = 1, 32, 16384
     q, k, v = (torch.randn((B, S, H, d), generator=gen, device=dev, dtype=torch.float32)
@@ -238,7 +260,9 @@ def extra_workloads(api, dev, stream, which="all", calls=5, dec_ms=None):
         "frac_of_2500": round(fl / (ms * 1e-3) / 1e12 / PEAK_BF16_TFLOPS, 4)}
     del q, k, v, o, lse
 
-    # ragged causal batch
+
+def ragged_causal(api, dev, stream, gen, d, timed, out):
+    import torch
     lengths = np.random.default_rng(5).integers(128, 8192 + 1, 16)
     cu = np.zeros(17, dtype=np.int32)
     cu[1:] = np.cumsum(lengths)
@@ -257,7 +281,6 @@ def extra_workloads(api, dev, stream, which="all", calls=5, dec_ms=None):
         "ms": round(ms, 4), "TFLOP/s": round(fl / (ms * 1e-3) / 1e12, 1),
         "frac_of_2500": round(fl / (ms * 1e-3) / 1e12 / PEAK_BF16_TFLOPS, 4),
         "total_tokens": total, "algorithmic_flop": fl}
-    return out
 
 
 def cpu_baseline(spec, data, max_pairs):
@@ -287,8 +310,9 @@ def main():
     ap.add_argument("--warmup", type=int, default=200,
                     help="untimed steps first (the clocks need some tens of ms to settle)")
     ap.add_argument("--no-cpu-baseline", action="store_true")
-    ap.add_argument("--extra", choices=["all", "none", "fp8"], default="all",
-                    help="context workloads beside the headline (fp8: the fp8-cache decode only)")
+    ap.add_argument("--extra", default="all",
+                    help="context workloads beside the headline: all, none, or a comma list "
+                         "of %s" % ",".join(EXTRAS))
     ap.add_argument("--no-extra", action="store_true",
                     help="skip every context line (same as --extra none)")
     ap.add_argument("--cpu-pairs", type=float, default=2.0e8,
@@ -306,6 +330,8 @@ def main():
         print("bench.py runs on one GPU only; --gpus %d is not supported by this build"
               % args.gpus, file=sys.stderr)
         sys.exit(2)
+    if args.extra not in ("all", "none") and not set(args.extra.split(",")) <= set(EXTRAS):
+        sys.exit("--extra takes all, none, or a comma list of " + ",".join(EXTRAS))
     if args.steps < 1 or args.warmup < 0:
         sys.exit("steps must be >= 1 and warmup >= 0")
 
@@ -421,8 +447,9 @@ def main():
         },
         "kernel_hash": kernel_hash(),
     }
-    which = "none" if args.no_extra else args.extra
-    if which != "none":
+    which = () if args.no_extra or args.extra == "none" else \
+        EXTRAS if args.extra == "all" else tuple(args.extra.split(","))
+    if which:
         result["extra"] = extra_workloads(api, dev, stream, which=which, dec_ms=dec_avg)
     if not args.no_cpu_baseline:
         result["cpu_baseline"] = cpu_baseline(pspec, pdata, args.cpu_pairs)
