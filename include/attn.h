@@ -239,7 +239,9 @@ attn_status_t attn_kmeans_assign(const void *x, const void *c, int *idx, float *
  * 0 for invalid sizes. */
 size_t attn_decode_workspace_bytes(int B, int Hq, int Hkv, int Skv, int d, int num_splits);
 
-/* The number of KV chunks attn_decode uses when passed num_splits <= 0. */
+/* The number of KV chunks attn_decode uses when passed num_splits <= 0:
+ * about one work item per compute unit of an MI355X (256 items over the
+ * (sequence, KV head, head block) groups), but chunks of at least 512 keys. */
 int attn_decode_pick_splits(int B, int Hq, int Hkv, int Skv);
 
 /* Static text for a status code (never NULL). */

@@ -216,9 +216,14 @@ def test_kmeans_assign_validation(lib):
 
 
 def test_decode_split_choice(lib):
-    assert lib.attn_decode_pick_splits(64, 32, 8, 4096) == 4
-    assert lib.attn_decode_pick_splits(1, 32, 8, 4096) == 16
+    # about one work item per compute unit (256), chunks of at least 512 keys
+    assert lib.attn_decode_pick_splits(64, 32, 8, 4096) == 1      # 512 groups already
+    assert lib.attn_decode_pick_splits(4, 32, 8, 16384) == 8      # 32 groups x 8
+    assert lib.attn_decode_pick_splits(1, 32, 8, 32768) == 32     # 8 groups x 32
+    assert lib.attn_decode_pick_splits(1, 32, 8, 4096) == 8       # capped: 512-key chunks
+    assert lib.attn_decode_pick_splits(1, 64, 1, 100000) == 128   # two column blocks x 128
+    assert lib.attn_decode_pick_splits(1, 8, 1, 100000) == 196    # one group: capped by length
     assert lib.attn_decode_pick_splits(1, 1, 1, 100) == 1
     assert lib.attn_decode_pick_splits(1, 3, 2, 100) == 0
     auto = lib.attn_decode_workspace_bytes(1, 32, 8, 4096, 128, 0)
-    assert auto == lib.attn_decode_workspace_bytes(1, 32, 8, 4096, 128, 16)
+    assert auto == lib.attn_decode_workspace_bytes(1, 32, 8, 4096, 128, 8)

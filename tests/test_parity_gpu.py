@@ -139,6 +139,9 @@ DECODE = [  # B, Hq, Hkv, Skv, d, splits
     (64, 8, 4, 200, 128, 3),
     (32, 16, 8, 100, 128, 64),
     (128, 4, 2, 777, 64, 3),
+    # few groups, many chunks: the merge kernel's unrolled loop and its tail
+    (1, 32, 8, 5000, 128, 37),
+    (2, 8, 2, 3000, 64, 100),       # six trailing chunks empty
 ]
 
 

@@ -25,12 +25,14 @@ struct DecodeShape {
 };
 
 int pick_splits(int B, int Hq, int Hkv, int Skv) {
-    // Enough workgroups to give every CU several (256 CUs), but chunks of at
-    // least 256 keys so each workgroup streams a useful amount of K/V.
+    // About one work item per compute unit (an MI355X has 256), but chunks of
+    // at least 512 keys.  Measured on the decode kernels: more, shorter
+    // chunks spend their time in per-item setup and in the merge of the
+    // partials, fewer leave compute units idle.
     const int ncb = ceil_div(Hq / Hkv, attn::kDecCols);
     const int64_t base = (int64_t)B * Hkv * ncb;
-    int s = (int)((2048 + base - 1) / base);
-    const int max_by_len = ceil_div(Skv, 256);
+    int s = (int)((256 + base - 1) / base);
+    const int max_by_len = ceil_div(Skv, 512);
     if (s > max_by_len) s = max_by_len;
     if (s < 1) s = 1;
     return s;

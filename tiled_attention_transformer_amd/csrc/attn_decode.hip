@@ -490,34 +490,101 @@ void attn_decode_split_kernel(DecParams p) {
     wait_vmcnt<0>();                 // no load may outlive the workgroup
 }
 
-// Merge of the key-range partials: one 64-thread workgroup per (sequence,
+// Merge of the key-range partials: one 4-wave workgroup per (sequence,
 // query head); LSE = M + log(sum_s exp(lse_s - M)), O = sum_s exp(lse_s - LSE) O_s.
+// The splits are spread over the threads (for M and the sum) and over the
+// waves (for O, each wave taking splits w, w+4, ... with independent loads in
+// flight), then combined in a fixed order, so the result is deterministic.
+constexpr int CW = 4;                        // waves of the merge kernel
+
+__device__ __forceinline__ float wave_max(float x) {
+#pragma unroll
+    for (int o = 32; o >= 1; o >>= 1) x = fmaxf(x, __shfl_xor(x, o));
+    return x;
+}
+__device__ __forceinline__ float wave_sum(float x) {
+#pragma unroll
+    for (int o = 32; o >= 1; o >>= 1) x += __shfl_xor(x, o);
+    return x;
+}
+
 template <int D>
-__global__ __launch_bounds__(64) void attn_decode_combine_kernel(DecParams p) {
+__global__ __launch_bounds__(64 * CW) void attn_decode_combine_kernel(DecParams p) {
+    constexpr int PER = D / 64;                     // output elements per lane
+    __shared__ float red[CW];
+    __shared__ float part[CW - 1][D];
     const int bh = blockIdx.x;                      // b * Hq + h
-    const int t = threadIdx.x;
+    const int t = threadIdx.x, lane = t & 63, wave = t >> 6;
     const int64_t stride = (int64_t)p.B * p.Hq;
-    float M = -__builtin_inff();
-    for (int s = 0; s < p.nsplit; ++s) M = fmaxf(M, p.ws_lse[s * stride + bh]);
+    const float *lse_p = p.ws_lse + bh;
+
+    // M = max_s lse_s
+    float mx = -__builtin_inff();
+    for (int s = t; s < p.nsplit; s += 64 * CW) mx = fmaxf(mx, lse_p[s * stride]);
+    mx = wave_max(mx);
+    if (lane == 0) red[wave] = mx;
+    __syncthreads();
+    float M = red[0];
+#pragma unroll
+    for (int w = 1; w < CW; ++w) M = fmaxf(M, red[w]);
     const float Mu = M == -__builtin_inff() ? 0.f : M;
+    __syncthreads();
+    // tot = sum_s exp(lse_s - M)
+    float tt = 0.f;
+    for (int s = t; s < p.nsplit; s += 64 * CW) tt += fast_exp2((lse_p[s * stride] - Mu) * kLog2e);
+    tt = wave_sum(tt);
+    if (lane == 0) red[wave] = tt;
+    __syncthreads();
     float tot = 0.f;
-    for (int s = 0; s < p.nsplit; ++s) tot += fast_exp2((p.ws_lse[s * stride + bh] - Mu) * kLog2e);
+#pragma unroll
+    for (int w = 0; w < CW; ++w) tot += red[w];
     const float lse = tot > 0.f ? Mu + fast_log2(tot) * kLn2 : -__builtin_inff();
-    constexpr int PER = D / 64;
+
+    // O: wave w sums splits w, w+CW, ...; lane L holds elements PER*L ..
     float acc[PER];
 #pragma unroll
     for (int e = 0; e < PER; ++e) acc[e] = 0.f;
-    for (int s = 0; s < p.nsplit; ++s) {
-        const float ls = p.ws_lse[s * stride + bh];
-        const float w = tot > 0.f ? fast_exp2((ls - lse) * kLog2e) : 0.f;
-        const float *os = p.ws_o + (s * stride + bh) * D + PER * t;
+    if (tot > 0.f) {
+        const float *o_p = p.ws_o + (int64_t)bh * D + PER * lane;
+        int s = wave;
+#pragma unroll 1
+        for (; s + 3 * CW < p.nsplit; s += 4 * CW) {
+            float w4[4], v4[4][PER];
 #pragma unroll
-        for (int e = 0; e < PER; ++e) acc[e] += w * os[e];
+            for (int u = 0; u < 4; ++u) {
+                const int su = s + u * CW;
+                w4[u] = lse_p[su * stride];
+#pragma unroll
+                for (int e = 0; e < PER; ++e) v4[u][e] = o_p[su * stride * D + e];
+            }
+#pragma unroll
+            for (int u = 0; u < 4; ++u) {
+                const float w = fast_exp2((w4[u] - lse) * kLog2e);
+#pragma unroll
+                for (int e = 0; e < PER; ++e) acc[e] += w * v4[u][e];
+            }
+        }
+        for (; s < p.nsplit; s += CW) {
+            const float w = fast_exp2((lse_p[s * stride] - lse) * kLog2e);
+#pragma unroll
+            for (int e = 0; e < PER; ++e) acc[e] += w * o_p[s * stride * D + e];
+        }
     }
-    __bf16 *op = p.o + (int64_t)bh * D + PER * t;
+    if (wave > 0) {
 #pragma unroll
-    for (int e = 0; e < PER; ++e) op[e] = (__bf16)acc[e];
-    if (p.lse != nullptr && t == 0) p.lse[bh] = lse;
+        for (int e = 0; e < PER; ++e) part[wave - 1][PER * lane + e] = acc[e];
+    }
+    __syncthreads();
+    if (wave == 0) {
+#pragma unroll
+        for (int w = 1; w < CW; ++w)
+#pragma unroll
+            for (int e = 0; e < PER; ++e) acc[e] += part[w - 1][PER * lane + e];
+        __bf16 *op = p.o + (int64_t)bh * D + PER * lane;
+#pragma unroll
+        for (int e = 0; e < PER; ++e) op[e] = (__bf16)acc[e];
+        if (p.lse != nullptr && lane == 0) p.lse[bh] = lse;
+    }
 }
 
 template <int D, bool F8>
@@ -543,7 +610,7 @@ hipError_t launch_t(DecParams p, hipStream_t s) {
     hipLaunchKernelGGL((attn_decode_split_kernel<D, F8>), dim3((unsigned)blocks), dim3(NT), 0, s, p);
     e = hipGetLastError();
     if (e != hipSuccess || p.nsplit == 1) return e;
-    hipLaunchKernelGGL(attn_decode_combine_kernel<D>, dim3((unsigned)(p.B * p.Hq)), dim3(64), 0,
+    hipLaunchKernelGGL(attn_decode_combine_kernel<D>, dim3((unsigned)(p.B * p.Hq)), dim3(64 * CW), 0,
                        s, p);
     return hipGetLastError();
 }
