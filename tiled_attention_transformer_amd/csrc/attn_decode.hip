@@ -232,8 +232,10 @@ void attn_decode_split_kernel(DecParams p) {
         for (int pp = 0; pp < 2 * L::LOADS; ++pp) {
             const int m = pp % L::LOADS;
             const int h = (m * (1024 / L::RB)) / 16;          // rows of load m: m * 1024/RB ..
-            buffer_lds_dma16(pp >= L::LOADS ? vr[h] : kr[h], goff[pp],
-                             dst + (pp >= L::LOADS ? L::T_BYTES : 0) + 1024 * m);
+            // the cache is read once per call: non-temporal, so it streams
+            // past L2 and the infinity cache instead of thrashing them
+            buffer_lds_dma16<kNonTemporal>(pp >= L::LOADS ? vr[h] : kr[h], goff[pp],
+                                           dst + (pp >= L::LOADS ? L::T_BYTES : 0) + 1024 * m);
         }
         lstage = (lstage + 1) & (L::STAGES - 1);
         ++lt;

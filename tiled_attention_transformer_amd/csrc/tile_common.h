@@ -111,12 +111,20 @@ __device__ __forceinline__ __amdgpu_buffer_rsrc_t buffer_rsrc(const void *base, 
     return __builtin_amdgcn_make_buffer_rsrc(const_cast<void *>(base), 0, nbytes, 0x00020000);
 }
 
+// Cache policy of a load whose data is used once (the "nt" bit of the
+// gfx940-family cache-policy operand): streamed past L2 and the infinity
+// cache instead of evicting data that is reused.
+constexpr int kNonTemporal = 2;
+
 // Buffer load of 16 bytes per lane straight into LDS (buffer_load_dwordx4 ...
 // lds): lane L's bytes from byte offset voff land at lds_base + 16*L.
+// `policy` is the cache-policy operand (0, or kNonTemporal for data read
+// once).
+template <int POLICY = 0>
 __device__ __forceinline__ void buffer_lds_dma16(__amdgpu_buffer_rsrc_t r, uint32_t voff,
                                                  void *lds_base) {
     __builtin_amdgcn_raw_ptr_buffer_load_lds(r, (__attribute__((address_space(3))) void *)lds_base,
-                                             16, voff, 0, 0, 0);
+                                             16, voff, 0, 0, POLICY);
 }
 
 // s_waitcnt on the vector-memory counter only (at most n loads outstanding).
