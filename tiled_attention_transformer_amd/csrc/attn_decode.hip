@@ -21,7 +21,10 @@
 //    v+8, ... (so together they read 128 consecutive keys at a time) and
 //    streams them through a private LDS ring (2 stages of bf16 tiles, or 4
 //    of fp8 tiles: the same 32 KB) with buffer loads that write straight to
-//    LDS.  No wave waits for another while streaming:
+//    LDS.  The loads are non-temporal: each cache byte is read once per call,
+//    and streaming it past L2 and the infinity cache instead of through them
+//    measured 5.5 % faster for a bf16 cache and 20 % for an fp8 one.  No wave
+//    waits for another while streaming:
 //    a ring shared by the workgroup needs a barrier per tile, and that
 //    barrier alone held a plain load stream of this shape to ~5.35 TB/s
 //    where private rings reach ~5.9 TB/s;
