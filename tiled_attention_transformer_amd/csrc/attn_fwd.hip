@@ -54,11 +54,16 @@
 //    loaded, waves skip tiles above their own rows, and only tiles that cross
 //    the diagonal or the sequence end evaluate the mask;
 //  * item order: (tile rank, batch*head), so under the causal mask the
-//    longest items come first.  A persistent workgroup w takes positions w,
-//    then the mirror position of the next row of the list, and so on
-//    (boustrophedon), which pairs long items with short ones; the mirror is
-//    taken in steps of 8 so an item's head keeps the XCD of workgroup w
-//    (workgroups go round-robin over the 8 XCDs) and its K/V stays in one L2.
+//    list runs from the longest items to the shortest.  A persistent
+//    workgroup w takes position w in one row of the list and the mirror
+//    position in the next (boustrophedon), which pairs long items with
+//    short ones; the mirror is taken in steps of 8 so an item's head keeps
+//    the XCD of workgroup w (workgroups go round-robin over the 8 XCDs) and
+//    its K/V stays in one L2.  Each workgroup runs its rows from the last
+//    (short items) to the first, so every workgroup ends on a long item: the
+//    per-item overheads then fall where the next item's loads hide them
+//    rather than in the kernel's tail (measured ~5 % faster on the causal
+//    B4 H16 S2048 prefill than the reverse order, same HBM traffic).
 //    Ragged batches launch one workgroup per item instead: their item sizes
 //    are known only on the device, and the hardware dispatcher balances them.
 #include "kernels.h"
@@ -144,14 +149,19 @@ __device__ __forceinline__ FwdItem fwd_item(const FwdParams &p, int it) {
     return x;
 }
 
-// The r-th item of this workgroup (boustrophedon over rows of gridDim.x
-// items, mirrored in steps of 8 so the item's head stays on this XCD), or -1.
+// The r-th item of this workgroup, or -1: its items are one per row of
+// gridDim.x items (boustrophedon: position w in even rows, the mirror
+// position, in steps of 8 so the item's head stays on this XCD, in odd
+// rows), taken from the last row to the first.
 __device__ __forceinline__ int fwd_item_at(const FwdParams &p, int r) {
     const int G = gridDim.x, w = blockIdx.x;
-    int pos = w;
-    if (r & 1) pos = (G % 8 == 0) ? (G / 8 - 1 - w / 8) * 8 + (w % 8) : G - 1 - w;
-    const int64_t it = (int64_t)r * G + pos;
-    return it < p.nitems ? (int)it : -1;
+    const int mirror = (G % 8 == 0) ? (G / 8 - 1 - w / 8) * 8 + (w % 8) : G - 1 - w;
+    const int R = (p.nitems + G - 1) / G;                  // rows of G items
+    const bool last_ok = (int64_t)(R - 1) * G + (((R - 1) & 1) ? mirror : w) < p.nitems;
+    const int nv = last_ok ? R : R - 1;                   // rows holding an item of w
+    if (r >= nv) return -1;
+    const int row = nv - 1 - r;                           // the rows in reverse order
+    return row * G + ((row & 1) ? mirror : w);
 }
 
 template <int D, bool CAUSAL, bool VARLEN>
