@@ -77,6 +77,42 @@ attn_status_t attn_fwd(const void *q, const void *k, const void *v, void *o, flo
                        int causal, hipStream_t stream);
 
 /*
+ * Prefill with the key range split across workgroups (split-KV), for shapes
+ * with few query tiles (few sequences, heads or rows, e.g. a chunk of new
+ * tokens against a long cache), where attn_fwd would leave compute units
+ * idle.  Same arguments and result as attn_fwd (up to fp32 rounding
+ * order), plus:
+ *   num_splits : key shares per query tile (each tile's own key tiles, cut
+ *                into num_splits runs of equal length); <= 0 lets the
+ *                library choose (about one work item per compute unit, and
+ *                shares that average at least 1024 keys -- otherwise the
+ *                partials' traffic outweighs the gain; 1 when no split
+ *                pays); 1 is attn_fwd exactly.
+ *   workspace  : DEVICE scratch of at least
+ *                attn_fwd_splitkv_workspace_bytes(...) bytes, 16-byte
+ *                aligned, owned by the caller (NULL allowed when that is 0);
+ *                it holds each share's normalised output (fp32) and
+ *                log-sum-exp, merged by LSE = M + log(sum_s exp(lse_s - M)),
+ *                O = sum_s exp(lse_s - LSE) O_s -- the same merge as decode.
+ * Deterministic for given sizes and num_splits.  Errors as attn_fwd, plus
+ * ATTN_ERR_WORKSPACE and ATTN_ERR_SHAPE for num_splits > 1024.  The
+ * splitting is the decode's key-range split (lecompute.fr, "FlashAttention-4
+ * : limites du calcul matriciel", section "Déplacer une partie des
+ * exponentielles": partial results under their own scale, merged by a common
+ * one) applied to prefill.
+ */
+attn_status_t attn_fwd_splitkv(const void *q, const void *k, const void *v, void *o, float *lse,
+                               int B, int Hq, int Hkv, int Sq, int Skv, int d, float scale,
+                               int causal, int num_splits, void *workspace,
+                               size_t workspace_bytes, hipStream_t stream);
+
+/* Bytes of attn_fwd_splitkv workspace for these sizes and mask (0 when
+ * num_splits resolves to 1; num_splits <= 0 means the library's choice, which
+ * depends on causal).  Returns 0 for invalid sizes. */
+size_t attn_fwd_splitkv_workspace_bytes(int B, int Hq, int Sq, int Skv, int d, int causal,
+                                        int num_splits);
+
+/*
  * Forward over a packed ragged batch (variable lengths).
  *   q, o : [total_q, Hq, d] bf16      k, v : [total_k, Hkv, d] bf16
  *   lse  : [Hq, total_q] fp32 (or NULL)

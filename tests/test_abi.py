@@ -33,7 +33,7 @@ def lib():
 
 def test_library_exports_every_declared_symbol(lib):
     names = declared_functions()
-    assert len(names) == 11, names
+    assert len(names) == 13, names
     raw = ctypes.CDLL(_lib.LIB_PATH)
     for n in names:
         assert hasattr(raw, n), n
@@ -213,6 +213,39 @@ def test_kmeans_assign_validation(lib):
     assert kmeans(lib, c=P + 4) == ALIGN
     assert kmeans(lib, idx=P + 2) == ALIGN
     assert kmeans(lib, dist=P + 1) == ALIGN
+
+
+def fwd_split(lib, q=P, o=P, B=1, Hq=32, Hkv=8, Sq=512, Skv=8192, d=128, scale=0.1, causal=1,
+              splits=4, ws=P, wsb=1 << 30):
+    return lib.attn_fwd_splitkv(q, P, P, o, None, B, Hq, Hkv, Sq, Skv, d, scale, causal, splits,
+                                ws, wsb, None)
+
+
+def test_fwd_splitkv_validation(lib):
+    assert fwd_split(lib, q=None) == NULLPTR
+    assert fwd_split(lib, o=None) == NULLPTR
+    assert fwd_split(lib, Sq=0) == SHAPE
+    assert fwd_split(lib, d=96) == BAD_D
+    assert fwd_split(lib, Hq=6, Hkv=4) == GQA
+    assert fwd_split(lib, scale=float("nan")) == SCALE
+    assert fwd_split(lib, q=P + 2) == ALIGN
+    assert fwd_split(lib, ws=None) == WS
+    need = lib.attn_fwd_splitkv_workspace_bytes(1, 32, 512, 8192, 128, 1, 4)
+    assert need == 4 * 32 * 512 * 129 * 4
+    assert fwd_split(lib, wsb=need - 4) == WS
+    assert fwd_split(lib, ws=P + 8) == ALIGN
+    assert fwd_split(lib, splits=2000) == SHAPE
+    ws = lambda *a: lib.attn_fwd_splitkv_workspace_bytes(*a)
+    # library's choice: ~one item per CU (256), shares averaging >= 1024 keys
+    assert ws(1, 32, 256, 8192, 128, 1, 0) == 7 * 32 * 256 * 129 * 4     # 32 items; 8064 keys
+    assert ws(1, 32, 256, 16384, 128, 1, 0) == 8 * 32 * 256 * 129 * 4    # 32 items x 8
+    assert ws(1, 32, 512, 8192, 128, 1, 0) == 4 * 32 * 512 * 129 * 4     # 64 items x 4
+    assert ws(1, 8, 4096, 4096, 128, 1, 0) == 2 * 8 * 4096 * 129 * 4     # 128 items; 2048 keys
+    assert ws(1, 32, 1024, 1024, 128, 1, 0) == 0       # causal: 512 keys per row on average
+    assert ws(1, 32, 1024, 1024, 128, 0, 0) == 0       # full rows: 1024 keys, one share
+    assert ws(4, 16, 2048, 2048, 128, 1, 0) == 0       # 512 items: no split
+    assert ws(1, 32, 512, 8192, 128, 1, 1) == 0
+    assert ws(0, 32, 512, 8192, 128, 1, 4) == 0
 
 
 def test_decode_split_choice(lib):

@@ -372,6 +372,56 @@ def test_decode_equals_prefill_last_row(api, dev):
     assert np.abs(f32_to_np(l_d) - f32_to_np(l_p[:, :, -1])).max() <= 1e-4
 
 
+# ---------------------------------------------------- split-KV prefill
+
+SPLITKV = [  # B, Sq, Skv, Hq, Hkv, d, causal, splits
+    (1, 512, 8192, 32, 8, 128, True, 4),      # a chunk of new tokens against a long cache
+    (2, 300, 300, 4, 4, 64, True, 3),         # ragged tile ends, d = 64
+    (1, 1000, 1000, 8, 2, 128, False, 0),     # library's choice, non-causal GQA
+    (1, 256, 256, 2, 2, 64, True, 8),         # more shares than key tiles: empty shares
+    (3, 100, 5000, 4, 4, 128, True, 16),      # one partial query tile per head
+    (1, 1024, 1024, 32, 32, 128, True, 0),    # few query tiles, library's choice
+]
+
+
+@pytest.mark.parametrize("case", SPLITKV, ids=lambda c: "B%d_Sq%d_Skv%d_Hq%d_Hkv%d_d%d_%s_s%d" % (
+    c[0], c[1], c[2], c[3], c[4], c[5], "causal" if c[6] else "full", c[7]))
+def test_fwd_splitkv_matches_oracle(api, dev, case):
+    import torch
+    B, Sq, Skv, Hq, Hkv, d, causal, splits = case
+    data = si.make_prefill(60 + Sq + Skv, B, Hq, Hkv, Sq, Skv, d)
+    scale = si.default_scale(d)
+    q, k, v = (to_dev(data[n], dev) for n in "qkv")
+    o, lse = api.attn_fwd_splitkv(q, k, v, scale=scale, causal=causal, num_splits=splits)
+    torch.cuda.synchronize()
+    o_ref, lse_ref = cpu.attn_full(data["q"], data["k"], data["v"], scale, causal)
+    assert_close(bf16_to_np(o), o_ref, f32_to_np(lse), lse_ref, str(case))
+
+
+def test_fwd_splitkv_one_split_is_attn_fwd_bitwise(api, dev):
+    import torch
+    data = si.make_prefill(71, 2, 8, 4, 700, 700, 128)
+    q, k, v = (to_dev(data[n], dev) for n in "qkv")
+    o1, l1 = api.attn_fwd(q, k, v, causal=True)
+    o2, l2 = api.attn_fwd_splitkv(q, k, v, causal=True, num_splits=1)
+    torch.cuda.synchronize()
+    assert torch.equal(o1.view(torch.int16), o2.view(torch.int16)) and torch.equal(l1, l2)
+
+
+def test_fwd_splitkv_split_counts_agree(api, dev):
+    """2, 5 and 13 shares agree with the unsplit forward to fp32 merge rounding."""
+    import torch
+    data = si.make_prefill(72, 1, 16, 4, 640, 4000, 128)
+    q, k, v = (to_dev(data[n], dev) for n in "qkv")
+    o1, l1 = api.attn_fwd(q, k, v, causal=True)
+    torch.cuda.synchronize()
+    for s in (2, 5, 13):
+        o2, l2 = api.attn_fwd_splitkv(q, k, v, causal=True, num_splits=s)
+        torch.cuda.synchronize()
+        assert np.abs(bf16_to_np(o2) - bf16_to_np(o1)).max() <= 2 ** -6, s
+        assert np.abs(f32_to_np(l2) - f32_to_np(l1)).max() <= 1e-4, s
+
+
 # ------------------------------------------------- invariants and equivalences
 
 def test_constant_v_gives_the_constant(api, dev):

@@ -97,6 +97,46 @@ def attn_fwd(q, k, v, o=None, lse=None, scale=None, causal=False, want_lse=True,
     return o, lse
 
 
+def attn_fwd_splitkv_workspace_bytes(B, Hq, Sq, Skv, d, causal=False, num_splits=0) -> int:
+    return int(_lib.load().attn_fwd_splitkv_workspace_bytes(B, Hq, Sq, Skv, d, int(bool(causal)),
+                                                            num_splits))
+
+
+def attn_fwd_splitkv(q, k, v, o=None, lse=None, scale=None, causal=False, num_splits=0,
+                     workspace=None, want_lse=True, stream=None):
+    """Prefill with the key range split across workgroups; returns ``(o, lse)``.
+
+    As :func:`attn_fwd`; ``num_splits <= 0`` lets the library choose and
+    ``workspace`` (a uint8 GPU tensor of at least
+    :func:`attn_fwd_splitkv_workspace_bytes` bytes) is allocated here if
+    omitted.
+    """
+    _need(q, "q", torch.bfloat16, 4)
+    _need(k, "k", torch.bfloat16, 4)
+    _need(v, "v", torch.bfloat16, 4)
+    B, Sq, Hq, d = q.shape
+    Skv, Hkv = k.shape[1], k.shape[2]
+    if tuple(v.shape) != tuple(k.shape) or k.shape[0] != B or k.shape[3] != d:
+        raise ValueError("shape mismatch")
+    if o is None:
+        o = torch.empty_like(q)
+    _need(o, "o", torch.bfloat16, 4)
+    if lse is None and want_lse:
+        lse = torch.empty((B, Hq, Sq), dtype=torch.float32, device=q.device)
+    if lse is not None:
+        _need(lse, "lse", torch.float32, 3)
+    nbytes = attn_fwd_splitkv_workspace_bytes(B, Hq, Sq, Skv, d, causal, num_splits)
+    if workspace is None and nbytes > 0:
+        workspace = torch.empty(nbytes, dtype=torch.uint8, device=q.device)
+    ws_bytes = 0 if workspace is None else workspace.numel() * workspace.element_size()
+    st = _lib.load().attn_fwd_splitkv(_ptr(q), _ptr(k), _ptr(v), _ptr(o), _ptr(lse), B, Hq, Hkv,
+                                      Sq, Skv, d, _scale(scale, d), int(bool(causal)),
+                                      int(num_splits), _ptr(workspace), ws_bytes,
+                                      _stream(stream))
+    _check(st, "attn_fwd_splitkv")
+    return o, lse
+
+
 def attn_varlen_check(cu_seqlens_host, total: int) -> int:
     """Validate a host copy of cumulative offsets; returns the longest length."""
     import numpy as np

@@ -108,16 +108,21 @@ struct FwdItem {
     int b, h;
     int Sq, Skv;            // query rows and keys of the sequence
     int q0;                 // first query row of the item
-    int nt;                 // key tiles any row of the item may see (0: none)
+    int nt;                 // key tiles of the item (0: none)
+    int t0;                 // first key tile of the item (split-KV: its share)
+    int sp;                 // key split of the item (split-KV), else 0
     int64_t qrow0, krow0;   // first query / key row of the sequence
 };
 
-template <bool CAUSAL, bool VARLEN>
+template <bool CAUSAL, bool VARLEN, bool SPLIT>
 __device__ __forceinline__ FwdItem fwd_item(const FwdParams &p, int it) {
     FwdItem x;
     const int BH = p.nbatch * p.Hq;
-    const int rank = it / BH;
-    const int bh = it - rank * BH;
+    const int rs = it / BH;
+    const int bh = it - rs * BH;
+    // split-KV items are (rank, split) pairs in rank-major order
+    const int rank = SPLIT ? rs / p.nsplit : rs;
+    x.sp = SPLIT ? rs - rank * p.nsplit : 0;
     x.b = bh / p.Hq;
     x.h = bh - x.b * p.Hq;
     if constexpr (VARLEN) {
@@ -146,6 +151,13 @@ __device__ __forceinline__ FwdItem fwd_item(const FwdParams &p, int it) {
     // one past the last key any row of the item may see (bottom-right causal)
     if (CAUSAL) kend = min(x.Skv, x.q0 + BR + (x.Skv - x.Sq));
     x.nt = (x.q0 < x.Sq && kend > 0) ? (kend + BC - 1) / BC : 0;
+    x.t0 = 0;
+    if constexpr (SPLIT) {
+        // the tile's own key tiles cut into nsplit shares of equal length
+        const int ct = (x.nt + p.nsplit - 1) / p.nsplit;
+        x.t0 = min(x.sp * ct, x.nt);
+        x.nt = min(ct, x.nt - x.t0);
+    }
     return x;
 }
 
@@ -164,9 +176,10 @@ __device__ __forceinline__ int fwd_item_at(const FwdParams &p, int r) {
     return row * G + ((row & 1) ? mirror : w);
 }
 
-template <int D, bool CAUSAL, bool VARLEN>
+template <int D, bool CAUSAL, bool VARLEN, bool SPLIT>
 __global__ __launch_bounds__(NT) __attribute__((amdgpu_waves_per_eu(2, 2)))
 void attn_fwd_kernel(FwdParams p) {
+    static_assert(!(VARLEN && SPLIT), "split-KV is for fixed batches");
     using L = FwdLay<D>;
     __shared__ __attribute__((aligned(16))) __bf16 lds[NS * L::STAGE];
 
@@ -178,13 +191,13 @@ void attn_fwd_kernel(FwdParams p) {
     const int64_t hd_q = (int64_t)p.Hq * D;
     const int64_t hd_k = (int64_t)p.Hkv * D;
 
-    auto item = [&](int r) { return fwd_item<CAUSAL, VARLEN>(p, fwd_item_at(p, r)); };
+    auto item = [&](int r) { return fwd_item<CAUSAL, VARLEN, SPLIT>(p, fwd_item_at(p, r)); };
     // next item after position r that has key tiles, or -1
     auto next_tiled = [&](int r) -> int {
         for (int s = r + 1;; ++s) {
             const int it = fwd_item_at(p, s);
             if (it < 0) return -1;
-            if (fwd_item<CAUSAL, VARLEN>(p, it).nt > 0) return s;
+            if (fwd_item<CAUSAL, VARLEN, SPLIT>(p, it).nt > 0) return s;
         }
     };
 
@@ -229,8 +242,8 @@ void attn_fwd_kernel(FwdParams p) {
         if (r >= 0) {
             const FwdItem x = item(r);
             l_tiles = x.nt;
-            l_keys = x.Skv;
-            l_off = x.krow0 * hd_k + (int64_t)(x.h / p.group) * D;
+            l_keys = x.Skv - x.t0 * BC;
+            l_off = (x.krow0 + (int64_t)x.t0 * BC) * hd_k + (int64_t)(x.h / p.group) * D;
         }
     };
     auto issue_next = [&]() {
@@ -302,13 +315,14 @@ void attn_fwd_kernel(FwdParams p) {
     float lsum = 0.f;                // this lane's share of the running sum
     const float c = p.c;
 
-    // geometry of the item being computed (wave-uniform, except qr)
-    int Skv = 0, off = 0, wrow0 = 0, qr = 0, ntw = 0;
+    // geometry of the item being computed (wave-uniform, except qr); kt0 is
+    // the key offset of its first tile (split-KV shares), else 0
+    int Skv = 0, off = 0, wrow0 = 0, qr = 0, ntw = 0, kt0 = 0;
 
     // Mask keys past each row's causal limit or past the sequence end; only
     // tiles that cross the diagonal or the end need it.
     auto mask = [&](int t, f32x16 (&s)[BC / 32]) {
-        const int key0 = t * BC;
+        const int key0 = kt0 + t * BC;
         if (key0 + BC > Skv || (CAUSAL && key0 + BC - 1 > wrow0 + off)) {
             int lim = Skv - 1;
             if (CAUSAL) lim = min(lim, qr + off);
@@ -529,6 +543,27 @@ void attn_fwd_kernel(FwdParams p) {
         const int rows = min(32, x.Sq - wr0);
         const float lt = zero ? 0.f : half_swap_sum(lsum);
         const float inv = lt > 0.f ? 1.f / lt : 0.f;
+        if constexpr (SPLIT) {
+            // this split's share: the normalised output (fp32) and its
+            // natural-log LSE, merged with the other shares by a second kernel
+            const int64_t row0 = (((int64_t)x.sp * p.nbatch + x.b) * p.Hq + x.h) * x.Sq + wr0;
+            const __amdgpu_buffer_rsrc_t ro = buffer_rsrc(p.ws_o + row0 * D, rows * D * 4);
+            const uint32_t oo = (uint32_t)((col * D + 4 * g) * 4);
+#pragma unroll
+            for (int db = 0; db < D / 32; ++db)
+#pragma unroll
+                for (int rq = 0; rq < 4; ++rq) {
+                    const f32x4 v4 = {oacc[db][4 * rq] * inv, oacc[db][4 * rq + 1] * inv,
+                                      oacc[db][4 * rq + 2] * inv, oacc[db][4 * rq + 3] * inv};
+                    __builtin_amdgcn_raw_buffer_store_b128(__builtin_bit_cast(u32x4, zero ? f32x4{} : v4), ro,
+                                                           oo + (32 * db + 8 * rq) * 4, 0, 0);
+                }
+            const __amdgpu_buffer_rsrc_t rl = buffer_rsrc(p.ws_lse + row0, rows * 4);
+            const float v = lt > 0.f ? (m + fast_log2(lt)) * kLn2 : -__builtin_inff();
+            __builtin_amdgcn_raw_buffer_store_b32(__builtin_bit_cast(uint32_t, v), rl,
+                                                  g == 0 ? (uint32_t)(col * 4) : 0x80000000u, 0, 0);
+            return;
+        }
         const __bf16 *ob = p.o + (x.qrow0 + wr0) * hd_q + (int64_t)x.h * D;
         const __amdgpu_buffer_rsrc_t ro = buffer_rsrc(ob, (int)(((int64_t)(rows - 1) * hd_q + D) * 2));
         const uint32_t oo = (uint32_t)((col * hd_q + 4 * g) * 2);
@@ -560,7 +595,7 @@ void attn_fwd_kernel(FwdParams p) {
         if (w0 >= x.Sq || x.nt == 0) return 0;
         int wk = x.Skv;
         if (CAUSAL) wk = min(x.Skv, min(w0 + 32, x.Sq) + (x.Skv - x.Sq));
-        return wk > 0 ? min(x.nt, (wk + BC - 1) / BC) : 0;
+        return wk > 0 ? min(x.nt, max((wk + BC - 1) / BC - x.t0, 0)) : 0;
     };
     // items after position r0 and before r1 (-1: to the end) that have rows
     // but no keys: O = 0, LSE = -inf
@@ -568,7 +603,7 @@ void attn_fwd_kernel(FwdParams p) {
         for (int r = r0 + 1; r1 < 0 || r < r1; ++r) {
             const int it = fwd_item_at(p, r);
             if (it < 0) break;
-            const FwdItem x = fwd_item<CAUSAL, VARLEN>(p, it);
+            const FwdItem x = fwd_item<CAUSAL, VARLEN, SPLIT>(p, it);
             if (x.q0 < x.Sq && x.nt == 0) {
                 write_out(x, true);
                 stores = true;
@@ -584,6 +619,7 @@ void attn_fwd_kernel(FwdParams p) {
         off = x.Skv - x.Sq;                       // bottom-right causal offset
         wrow0 = x.q0 + 32 * wave;                 // first row of this wave
         qr = wrow0 + col;                         // this lane's query row
+        kt0 = x.t0 * BC;
         ntw = wave_tiles(x);
         rB = next_tiled(r);
         ntB = 0;
@@ -651,10 +687,46 @@ void attn_fwd_kernel(FwdParams p) {
     wait_vmcnt<0>();                 // no load may outlive the workgroup
 }
 
-template <int D, bool CAUSAL, bool VARLEN>
+// Merge of the split-KV shares, one wave per query row: LSE = M + log(sum_s
+// exp(lse_s - M)), O = sum_s exp(lse_s - LSE) O_s (the decode merge, per row).
+template <int D>
+__global__ __launch_bounds__(256) void attn_fwd_merge_kernel(FwdParams p) {
+    constexpr int PER = D / 64;
+    const int64_t rows = (int64_t)p.nbatch * p.Hq * p.Sq;
+    const int64_t row = (int64_t)blockIdx.x * 4 + (threadIdx.x >> 6);   // (b, h, i)
+    if (row >= rows) return;
+    const int lane = threadIdx.x & 63;
+    const float *lse_p = p.ws_lse + row;
+    float M = -__builtin_inff();
+    for (int s = 0; s < p.nsplit; ++s) M = fmaxf(M, lse_p[s * rows]);
+    const float Mu = M == -__builtin_inff() ? 0.f : M;
+    float tot = 0.f;
+    for (int s = 0; s < p.nsplit; ++s) tot += fast_exp2((lse_p[s * rows] - Mu) * kLog2e);
+    const float lse = tot > 0.f ? Mu + fast_log2(tot) * kLn2 : -__builtin_inff();
+    float acc[PER];
+#pragma unroll
+    for (int e = 0; e < PER; ++e) acc[e] = 0.f;
+    if (tot > 0.f) {
+        const float *o_p = p.ws_o + row * D + PER * lane;
+        for (int s = 0; s < p.nsplit; ++s) {
+            const float w = fast_exp2((lse_p[s * rows] - lse) * kLog2e);
+#pragma unroll
+            for (int e = 0; e < PER; ++e) acc[e] += w * o_p[s * rows * D + e];
+        }
+    }
+    // row = (b * Hq + h) * Sq + i; O is [B, Sq, Hq, d], LSE [B, Hq, Sq]
+    const int64_t i = row % p.Sq, bh = row / p.Sq;
+    const int64_t b = bh / p.Hq, h = bh % p.Hq;
+    __bf16 *op = p.o + ((b * p.Sq + i) * p.Hq + h) * D + PER * lane;
+#pragma unroll
+    for (int e = 0; e < PER; ++e) op[e] = (__bf16)acc[e];
+    if (p.lse != nullptr && lane == 0) p.lse[row] = lse;
+}
+
+template <int D, bool CAUSAL, bool VARLEN, bool SPLIT>
 hipError_t launch_t(const FwdParams &p_in, hipStream_t s) {
     FwdParams p = p_in;
-    const int64_t items = (int64_t)p.ntiles * p.nbatch * p.Hq;
+    const int64_t items = (int64_t)p.ntiles * p.nbatch * p.Hq * (SPLIT ? p.nsplit : 1);
     if (items <= 0) return hipSuccess;
     if (items > 0x7fffffff) return hipErrorInvalidConfiguration;
     p.nitems = (int)items;
@@ -667,8 +739,12 @@ hipError_t launch_t(const FwdParams &p_in, hipStream_t s) {
         if (e != hipSuccess) return e;
         if (cus > 0 && grid > cus) grid = cus;
     }
-    hipLaunchKernelGGL((attn_fwd_kernel<D, CAUSAL, VARLEN>), dim3((unsigned)grid), dim3(NT), 0,
-                       s, p);
+    hipLaunchKernelGGL((attn_fwd_kernel<D, CAUSAL, VARLEN, SPLIT>), dim3((unsigned)grid), dim3(NT),
+                       0, s, p);
+    hipError_t e = hipGetLastError();
+    if (!SPLIT || e != hipSuccess) return e;
+    const int64_t rows = (int64_t)p.nbatch * p.Hq * p.Sq;
+    hipLaunchKernelGGL(attn_fwd_merge_kernel<D>, dim3((unsigned)((rows + 3) / 4)), dim3(256), 0, s, p);
     return hipGetLastError();
 }
 
@@ -676,13 +752,21 @@ hipError_t launch_t(const FwdParams &p_in, hipStream_t s) {
 
 hipError_t launch_fwd(const FwdParams &p, int d, bool causal, bool varlen, hipStream_t s) {
     if (d == 128) {
-        if (varlen) return causal ? launch_t<128, true, true>(p, s) : launch_t<128, false, true>(p, s);
-        return causal ? launch_t<128, true, false>(p, s) : launch_t<128, false, false>(p, s);
+        if (varlen)
+            return causal ? launch_t<128, true, true, false>(p, s) : launch_t<128, false, true, false>(p, s);
+        return causal ? launch_t<128, true, false, false>(p, s) : launch_t<128, false, false, false>(p, s);
     }
     if (d == 64) {
-        if (varlen) return causal ? launch_t<64, true, true>(p, s) : launch_t<64, false, true>(p, s);
-        return causal ? launch_t<64, true, false>(p, s) : launch_t<64, false, false>(p, s);
+        if (varlen)
+            return causal ? launch_t<64, true, true, false>(p, s) : launch_t<64, false, true, false>(p, s);
+        return causal ? launch_t<64, true, false, false>(p, s) : launch_t<64, false, false, false>(p, s);
     }
+    return hipErrorInvalidValue;
+}
+
+hipError_t launch_fwd_split(const FwdParams &p, int d, bool causal, hipStream_t s) {
+    if (d == 128) return causal ? launch_t<128, true, false, true>(p, s) : launch_t<128, false, false, true>(p, s);
+    if (d == 64) return causal ? launch_t<64, true, false, true>(p, s) : launch_t<64, false, false, true>(p, s);
     return hipErrorInvalidValue;
 }
 

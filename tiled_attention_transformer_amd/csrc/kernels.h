@@ -62,8 +62,13 @@ struct FwdParams {
     int Sq, Skv;             // fixed batch only
     int total_q, total_k;    // varlen only
     int ntiles;              // query tiles per (batch, head)
-    int nitems;              // ntiles * nbatch * Hq (set by the launcher)
+    int nitems;              // ntiles * nbatch * Hq (* nsplit; set by the launcher)
     float c;                 // scale * log2(e)
+    // split-KV prefill (fixed batches): each query tile's key tiles are cut
+    // into nsplit shares; split s of a tile writes its normalised output and
+    // natural-log LSE to ws_o [nsplit, B, Hq, Sq, d] and ws_lse [nsplit, B, Hq, Sq]
+    int nsplit;
+    float *ws_o, *ws_lse;
 };
 
 struct DecParams {
@@ -94,6 +99,7 @@ struct AssignParams {
 };
 
 hipError_t launch_fwd(const FwdParams &p, int d, bool causal, bool varlen, hipStream_t s);
+hipError_t launch_fwd_split(const FwdParams &p, int d, bool causal, hipStream_t s);
 hipError_t launch_decode(const DecParams &p, int d, bool fp8, hipStream_t s);
 hipError_t launch_kmeans_assign(const AssignParams &p, int d, hipStream_t s);
 
