@@ -344,6 +344,23 @@ def test_decode_fp8_power_of_two_scales_equal_bf16_cache(api, dev):
     assert np.abs(l8 - f32_to_np(l16)).max() <= 1e-4
 
 
+def test_decode_workspace_reused_across_shapes(api, dev):
+    """One workspace (uninitialised) serves successive split decodes of
+    different shapes: nothing in it carries over from one call to the next."""
+    import torch
+    cases = [(1, 32, 8, 5000, 128, 37), (3, 16, 4, 3000, 64, 9), (2, 8, 2, 9000, 128, 64),
+             (1, 32, 8, 5000, 128, 37)]
+    need = max(api.attn_decode_workspace_bytes(B, Hq, Hkv, S, d, s) for B, Hq, Hkv, S, d, s in cases)
+    ws = torch.full((need,), 0x7F, dtype=torch.uint8, device=dev)
+    for B, Hq, Hkv, Skv, d, splits in cases:
+        data = si.make_decode(90 + Skv, B, Hq, Hkv, Skv, d)
+        q, k, v = (to_dev(data[x], dev) for x in "qkv")
+        o, lse = api.attn_decode(q, k, v, num_splits=splits, workspace=ws)
+        torch.cuda.synchronize()
+        o_ref, lse_ref = cpu.decode_full(data["q"], data["k"], data["v"], si.default_scale(d))
+        assert_close(bf16_to_np(o), o_ref, f32_to_np(lse), lse_ref, str((B, Hq, Hkv, Skv, d, splits)))
+
+
 def test_decode_split_counts_agree(api, dev):
     """1, 2, 8, 64 chunks and the library's choice agree closely (fp32 merge)."""
     import torch
