@@ -437,7 +437,7 @@ def main():
                        "min": round(float(pre_ms.min()), 5), "cold": round(cold_prefill_ms, 5)},
         "roofline": {"bound": "mfma", "achieved": round(tflops, 2), "peak": PEAK_BF16_TFLOPS,
                      "unit": "TFLOP/s", "frac": round(tflops / PEAK_BF16_TFLOPS, 4),
-                     "traffic": traffic, "kernel": "attn_fwd_kernel<128,causal>"},
+                     "traffic": traffic, "kernel": "attn_fwd_kernel<128, true, false, false>"},
         "decode": {
             "value": round(gbs, 1), "unit": "GB/s",
             "ms": {"mean": round(dec_avg, 5), "median": round(float(np.median(dec_ms)), 5),
@@ -445,7 +445,7 @@ def main():
             "roofline": {"bound": "hbm", "achieved": round(gbs, 1), "peak": PEAK_HBM_GBS,
                          "unit": "GB/s", "frac": round(gbs / PEAK_HBM_GBS, 4),
                          "traffic": load_traffic("decode"),
-                         "kernel": "attn_decode_split_kernel<128> (whole sequences per "
+                         "kernel": "attn_decode_split_kernel<128, false> (whole sequences per "
                                    "workgroup, waves merged in the kernel; the combine kernel "
                                    "runs only when the groups do not fill the GPU)"},
         },
