@@ -65,7 +65,7 @@ def decode_bytes(B, Hq, Hkv, Skv, d, kv_elem_bytes=2):
 
 TRAFFIC_PATH = os.path.join(ROOT, "profiles", "traffic.json")
 # which kernels make up each reported path (substrings of the rocprofv3 names)
-TRAFFIC_KERNELS = {"prefill": ["attn_fwd_kernel<128, true, false>"],
+TRAFFIC_KERNELS = {"prefill": ["attn_fwd_kernel<128, true, false, false>"],
                    "decode": ["attn_decode_split_kernel<128, false>",
                               "attn_decode_combine_kernel<128>"],
                    "decode_fp8": ["attn_decode_split_kernel<128, true>"],
