@@ -1,0 +1,237 @@
+"""GPU parity over seeded random shapes, for every attention entry point.
+
+The hand-picked cases elsewhere pin the edges one at a time; here a fixed
+seed draws shapes that combine them: batch and head counts, GQA ratios, query
+and key lengths on and off tile boundaries (including 1 and Sq > Skv under
+the bottom-right causal mask), d = 64 and 128, the softmax scale, the size of
+the query vectors, split counts, per-sequence cache lengths and page sizes.
+Every output is compared with the fp64 oracle on the same bf16 inputs, to the
+same bars as the other parity tests (O max-abs 2e-2 against the unrounded
+oracle, LSE max-abs 1e-3; rows with no allowed key must be O = 0, LSE = -inf).
+
+The logits stay within twice the default spread (scale times query size at
+most 2 / sqrt(d)): the 2e-2 bar on bf16 outputs assumes weights that average
+several keys, and much sharper rows put a single bf16 value of V, rounded
+once more, into O.
+"""
+import numpy as np
+import pytest
+
+import synth_inputs as si
+from oracle import cpu, ref
+from tests.gpu_util import assert_close, bf16_to_np, f32_to_np, to_dev
+
+pytestmark = pytest.mark.gpu
+
+
+@pytest.fixture(scope="module")
+def api():
+    from tiled_attention_transformer_amd import api as a
+    a._lib.load()
+    return a
+
+
+def _length(rng, hi):
+    """A length in [1, hi]: often on or next to a multiple of 64, else uniform."""
+    kind = rng.integers(4)
+    if kind == 0:
+        return int(min(hi, max(1, 64 * rng.integers(1, hi // 64 + 2) + rng.integers(-1, 2))))
+    if kind == 1:
+        return int(rng.integers(1, 9))
+    return int(rng.integers(1, hi + 1))
+
+
+def _logit_factors(rng, d):
+    """(softmax scale, power-of-two factor on q) with scale * factor in
+    [0.25, 2] / sqrt(d)."""
+    qf = float(2.0 ** rng.integers(-1, 2))                   # 0.5, 1 or 2
+    tot = float(np.exp(rng.uniform(np.log(0.25), np.log(2.0))))
+    scale = float(np.float32(tot / qf / np.sqrt(d)))
+    return scale, qf
+
+
+def _scale_bits(bits, f):
+    """bf16 bit patterns times a power of two (exact for these magnitudes)."""
+    return si.f32_to_bf16_bits((si.bf16_to_f64(bits) * f).astype(np.float32))
+
+
+def _draw_prefill(n, seed=2027):
+    rng = np.random.default_rng(seed)
+    cases = []
+    for i in range(n):
+        d = int(rng.choice([64, 128]))
+        Hkv = int(rng.choice([1, 2, 4]))
+        Hq = Hkv * int(rng.choice([1, 2, 4, 8]))
+        B = int(rng.integers(1, 4))
+        Sq = _length(rng, 700)
+        Skv = Sq if rng.random() < 0.4 else _length(rng, 900)
+        causal = bool(rng.random() < 0.6)
+        splits = int(rng.choice([0, 1, 2, 3, 5, 9]))
+        cases.append((i, B, Sq, Skv, Hq, Hkv, d, causal, splits))
+    return cases
+
+
+PREFILL = _draw_prefill(24)
+
+
+@pytest.mark.parametrize("case", PREFILL, ids=lambda c: "%d_B%d_Sq%d_Skv%d_Hq%d_Hkv%d_d%d_%s_s%d" % (
+    *c[:7], "causal" if c[7] else "full", c[8]))
+def test_random_prefill_and_splitkv(api, dev, case):
+    import torch
+    i, B, Sq, Skv, Hq, Hkv, d, causal, splits = case
+    rng = np.random.default_rng(500 + i)
+    scale, qf = _logit_factors(rng, d)
+    data = si.make_prefill(900 + i, B, Hq, Hkv, Sq, Skv, d)
+    data["q"] = _scale_bits(data["q"], qf)
+    print("random prefill", case, "scale %.6g q x%g" % (scale, qf), flush=True)
+    q, k, v = (to_dev(data[x], dev) for x in "qkv")
+    o1, l1 = api.attn_fwd(q, k, v, scale=scale, causal=causal)
+    o2, l2 = api.attn_fwd_splitkv(q, k, v, scale=scale, causal=causal, num_splits=splits)
+    torch.cuda.synchronize()
+    o_ref, lse_ref = cpu.attn_full(data["q"], data["k"], data["v"], scale, causal)
+    assert_close(bf16_to_np(o1), o_ref, f32_to_np(l1), lse_ref, "attn_fwd %s" % (case,))
+    assert_close(bf16_to_np(o2), o_ref, f32_to_np(l2), lse_ref, "attn_fwd_splitkv %s" % (case,))
+    if causal and Sq > Skv:
+        dead = Sq - Skv
+        for o in (o1, o2):
+            assert torch.count_nonzero(o[:, :dead].float()).item() == 0
+
+
+def _draw_varlen(n, seed=2028):
+    rng = np.random.default_rng(seed)
+    cases = []
+    for i in range(n):
+        d = int(rng.choice([64, 128]))
+        Hkv = int(rng.choice([1, 2, 4]))
+        Hq = Hkv * int(rng.choice([1, 2, 4]))
+        nseq = int(rng.integers(1, 7))
+        lq, lk = [], []
+        for _ in range(nseq):
+            r = rng.random()
+            if r < 0.5:                      # self-attention
+                a = _length(rng, 600)
+                lq.append(a)
+                lk.append(a)
+            elif r < 0.8:                    # a chunk of new tokens after a prefix
+                a = _length(rng, 300)
+                lq.append(a)
+                lk.append(a + int(rng.integers(0, 500)))
+            else:                            # either side may be empty
+                lq.append(int(rng.integers(0, 200)))
+                lk.append(int(rng.integers(0, 200)))
+        if sum(lq) == 0:
+            lq[0] = 1
+        if sum(lk) == 0:
+            lk[-1] = 1
+        causal = bool(rng.random() < 0.6)
+        cases.append((i, d, Hq, Hkv, causal, tuple(lq), tuple(lk)))
+    return cases
+
+
+VARLEN = _draw_varlen(12)
+
+
+@pytest.mark.parametrize("case", VARLEN, ids=lambda c: "%d_d%d_Hq%d_Hkv%d_%s_n%d" % (
+    *c[:4], "causal" if c[4] else "full", len(c[5])))
+def test_random_varlen(api, dev, case):
+    import torch
+    i, d, Hq, Hkv, causal, lq, lk = case
+    rng = np.random.default_rng(600 + i)
+    scale, qf = _logit_factors(rng, d)
+    data = si.make_varlen_cross(950 + i, lq, lk, H=Hq, d=d, Hkv=Hkv)
+    data["q"] = _scale_bits(data["q"], qf)
+    cq, ck = data["cu_seqlens_q"], data["cu_seqlens_k"]
+    print("random varlen", case, "scale %.6g q x%g" % (scale, qf), flush=True)
+    kd, vd = to_dev(data["k"], dev), to_dev(data["v"], dev)
+    qd = to_dev(data["q"], dev)
+    o, lse = api.attn_fwd_varlen(qd, kd, vd, torch.from_numpy(cq).to(dev),
+                                 torch.from_numpy(ck).to(dev), max(lq), max(lk),
+                                 scale=scale, causal=causal)
+    torch.cuda.synchronize()
+    o, lse = bf16_to_np(o), f32_to_np(lse)
+    rows = np.array([(s, h, r) for s in range(len(lq)) for h in range(Hq) for r in range(lq[s])],
+                    dtype=np.int64)
+    o_ref, lse_ref = cpu.varlen_rows(data["q"], data["k"], data["v"], cq, ck, scale, causal, rows)
+    tok = cq[rows[:, 0]] + rows[:, 2]
+    assert_close(o[tok, rows[:, 1]], o_ref, lse[rows[:, 1], tok], lse_ref, str(case))
+    dead = ~np.isfinite(lse_ref)
+    assert np.all(o[tok[dead], rows[dead, 1]] == 0)
+
+
+def _draw_decode(n, seed=2029):
+    rng = np.random.default_rng(seed)
+    cases = []
+    for i in range(n):
+        kind = ["dense", "varlen", "paged", "fp8"][i % 4]
+        d = int(rng.choice([64, 128]))
+        Hkv = int(rng.choice([1, 2, 4, 8]))
+        Hq = Hkv * int(rng.choice([1, 2, 4, 8, 16]))
+        B = int(rng.choice([1, 2, 5, 16, 40]))
+        Skv = _length(rng, 2000)
+        splits = int(rng.choice([0, 0, 1, 2, 7, 16, 40]))
+        page = int(16 * rng.integers(1, 9))
+        cases.append((i, kind, B, Hq, Hkv, Skv, d, splits, page))
+    return cases
+
+
+DECODE = _draw_decode(16)
+
+
+@pytest.mark.parametrize("case", DECODE, ids=lambda c: "%d_%s_B%d_Hq%d_Hkv%d_Skv%d_d%d_s%d_p%d" % c)
+def test_random_decode(api, dev, case):
+    import torch
+    i, kind, B, Hq, Hkv, Skv, d, splits, page = case
+    rng = np.random.default_rng(700 + i)
+    scale, qf = _logit_factors(rng, d)
+    lengths = None
+    if kind != "dense":
+        lengths = rng.integers(0, Skv + 1, B).astype(np.int32)
+        lengths[rng.integers(B)] = Skv                       # one full cache
+    print("random decode", case, "scale %.6g q x%g" % (scale, qf), flush=True)
+    if kind == "fp8":
+        data = si.make_decode_fp8(980 + i, B, Hq, Hkv, Skv, d)
+        data["q"] = _scale_bits(data["q"], qf)
+        q = to_dev(data["q"], dev)
+        k, v = (torch.from_numpy(data[x]).to(dev) for x in "kv")
+        o, lse = api.attn_decode_fp8(q, k, v, data["k_scale"], data["v_scale"],
+                                     seqlens_k=torch.from_numpy(lengths).to(dev), scale=scale,
+                                     num_splits=splits)
+        torch.cuda.synchronize()
+        o_ref, lse_ref = ref.decode_fp8(si.bf16_to_f64(data["q"]), data["k"], data["v"], scale,
+                                        data["k_scale"], data["v_scale"], seqlens=lengths)
+        assert_close(bf16_to_np(o), o_ref, f32_to_np(lse), lse_ref, str(case))
+        return
+    if kind == "paged":
+        maxp = (Skv + page - 1) // page
+        data = si.make_paged(980 + i, B, Hq, Hkv, d, page, maxp, B * maxp + 5)
+        data["q"] = _scale_bits(data["q"], qf)
+        dense_k = si.gather_pages(data["k_pages"], data["block_table"])
+        dense_v = si.gather_pages(data["v_pages"], data["block_table"])
+        lengths = np.minimum(lengths, maxp * page).astype(np.int32)
+        o, lse = api.attn_decode_paged(to_dev(data["q"], dev), to_dev(data["k_pages"], dev),
+                                       to_dev(data["v_pages"], dev),
+                                       torch.from_numpy(data["block_table"]).to(dev),
+                                       torch.from_numpy(lengths).to(dev), scale=scale,
+                                       num_splits=splits)
+    else:
+        data = si.make_decode(980 + i, B, Hq, Hkv, Skv, d)
+        data["q"] = _scale_bits(data["q"], qf)
+        dense_k, dense_v = data["k"], data["v"]
+        q, k, v = (to_dev(data[x], dev) for x in "qkv")
+        if kind == "dense":
+            o, lse = api.attn_decode(q, k, v, scale=scale, num_splits=splits)
+        else:
+            o, lse = api.attn_decode_varlen(q, k, v, torch.from_numpy(lengths).to(dev),
+                                            scale=scale, num_splits=splits)
+    torch.cuda.synchronize()
+    if lengths is None:
+        o_ref, lse_ref = cpu.decode_full(data["q"], dense_k, dense_v, scale)
+    else:
+        o_ref = np.zeros((B, Hq, d))
+        lse_ref = np.full((B, Hq), -np.inf)
+        for b, n in enumerate(lengths):
+            if n > 0:
+                ob, lb = cpu.decode_full(data["q"][b:b + 1], dense_k[b:b + 1, :n],
+                                         dense_v[b:b + 1, :n], scale)
+                o_ref[b], lse_ref[b] = ob[0], lb[0]
+    assert_close(bf16_to_np(o), o_ref, f32_to_np(lse), lse_ref, str(case))
