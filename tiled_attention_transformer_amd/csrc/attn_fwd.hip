@@ -566,16 +566,27 @@ void attn_fwd_kernel(FwdParams p) {
         }
         const __bf16 *ob = p.o + (x.qrow0 + wr0) * hd_q + (int64_t)x.h * D;
         const __amdgpu_buffer_rsrc_t ro = buffer_rsrc(ob, (int)(((int64_t)(rows - 1) * hd_q + D) * 2));
-        const uint32_t oo = (uint32_t)((col * hd_q + 4 * g) * 2);
+        // A lane holds four runs of 4 columns of its row per 32-column block
+        // (at 8q + 4g); swapping one run of each pair with the other half of
+        // the wave gives every lane 8 consecutive columns (lower half: 16k +
+        // 0..7, upper half: 16k + 8..15), so each row is written in 32-byte
+        // pieces by 16-byte stores instead of 16-byte pieces by 8-byte ones
+        const uint32_t oo = (uint32_t)((col * hd_q + 8 * g) * 2);
 #pragma unroll
         for (int db = 0; db < D / 32; ++db)
 #pragma unroll
-            for (int rq = 0; rq < 4; ++rq) {
-                const bf16x4 v4 = zero ? bf16x4{} :
-                    to_bf16x4(oacc[db][4 * rq] * inv, oacc[db][4 * rq + 1] * inv,
-                              oacc[db][4 * rq + 2] * inv, oacc[db][4 * rq + 3] * inv);
-                __builtin_amdgcn_raw_buffer_store_b64(__builtin_bit_cast(u32x2, v4), ro,
-                                                      oo + (32 * db + 8 * rq) * 2, 0, 0);
+            for (int k = 0; k < 2; ++k) {
+                const f32x16 &a = oacc[db];
+                const int r = 8 * k;
+                const bf16x4 lo = zero ? bf16x4{} :
+                    to_bf16x4(a[r] * inv, a[r + 1] * inv, a[r + 2] * inv, a[r + 3] * inv);
+                const bf16x4 hi = zero ? bf16x4{} :
+                    to_bf16x4(a[r + 4] * inv, a[r + 5] * inv, a[r + 6] * inv, a[r + 7] * inv);
+                const u32x2 ul = __builtin_bit_cast(u32x2, lo), uh = __builtin_bit_cast(u32x2, hi);
+                const auto s0 = __builtin_amdgcn_permlane32_swap(ul[0], uh[0], false, false);
+                const auto s1 = __builtin_amdgcn_permlane32_swap(ul[1], uh[1], false, false);
+                const u32x4 v = {(uint32_t)s0[0], (uint32_t)s1[0], (uint32_t)s0[1], (uint32_t)s1[1]};
+                __builtin_amdgcn_raw_buffer_store_b128(v, ro, oo + (32 * db + 16 * k) * 2, 0, 0);
             }
         if (p.lse != nullptr) {
             int64_t l0;
