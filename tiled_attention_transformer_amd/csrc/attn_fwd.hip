@@ -44,9 +44,11 @@
 //    product (converted to bf16) without touching LDS.  V stays row-major in
 //    LDS and is read as the A operand with ds_read_b64_tr_b16;
 //  * software pipeline inside each wave: iteration j issues the MFMAs of
-//    S_{j+1} and, interleaved with them, the softmax of S_j; then P_j * V_j.
-//    Both parts run as groups of four MFMAs split by scheduling barriers, and
-//    every LDS operand read is issued one group ahead of its MFMAs;
+//    S_{j+1} and of P_j * V_j, interleaved with the softmax of S_j: group g
+//    holds the score MFMAs of two d-slices, weight chunk g and the P * V
+//    MFMAs of the key slices whose weights chunk g-1 made.  Groups are split
+//    by scheduling barriers, and every LDS operand read is issued one group
+//    ahead of its MFMAs;
 //  * softmax in base 2: P = exp2(s*c - m) with c = scale*log2(e) folded into
 //    one FMA; the reference max m moves only when a row max grows by more
 //    than 2^8, so most tiles skip the output rescale; LSE = (m + log2 l)*ln 2;
@@ -383,12 +385,14 @@ void attn_fwd_kernel(FwdParams p) {
     // scheduling barriers, so that every LDS read is issued one group ahead
     // of the MFMAs that consume it (in-order issue would otherwise stall each
     // MFMA on its own read).  Group g of the score product covers d-slices
-    // 2g, 2g+1 (FPG fragments); weight chunk g makes pk[] entries of the same
-    // rank.
+    // 2g, 2g+1 (FPG fragments); weight chunk g makes the pk[] entries of key
+    // slices KPG*g .. KPG*g + KPG-1.
     constexpr int NG = D / 32;                   // score groups per tile
     constexpr int FPG = 2 * (BC / 32);           // K fragments per group
     constexpr int VPL = (BC / 2) / NG;           // weights per lane per chunk
     constexpr int NV = 2 * (D / 32);             // V transpose reads per key slice
+    constexpr int KPG = (BC / 16) / NG;          // key slices per weight chunk
+    static_assert(KPG * NG == BC / 16, "weight chunks must cover whole key slices");
     static_assert(VPL % 8 == 0, "a weight chunk must fill whole pk entries");
     auto read_k = [&](int n, int grp, bf16x8 (&kf)[FPG]) {
         const __bf16 *ks = lds + lane_base(n, k_lane);
@@ -430,16 +434,6 @@ void attn_fwd_kernel(FwdParams p) {
         for (int db = 0; db < D / 32; ++db)
             oacc[db] = mfma32x32x16(concat_tr(vf[2 * db], vf[2 * db + 1]), pk[kk], oacc[db]);
     };
-    // O += P_j V_j, V fragments read one key slice ahead
-    auto pv = [&](int n, s16x4 (&vf)[2][NV], const bf16x8 (&pk)[BC / 16]) {
-#pragma unroll
-        for (int kk = 0; kk < BC / 16; ++kk) {
-            __builtin_amdgcn_sched_barrier(0);
-            if (kk + 1 < BC / 16) read_v(n, kk + 1, vf[(kk + 1) & 1]);
-            mfma_v(kk, vf[kk & 1], pk);
-        }
-        __builtin_amdgcn_sched_barrier(0);
-    };
 
     int cn = 0;              // stream number of the tile being computed
     bool stores = false;     // output stores issued since the last full wait
@@ -461,8 +455,8 @@ void attn_fwd_kernel(FwdParams p) {
 
     // One pipeline step of item-local tile j (stream tile cn): wait for tile
     // cn+1, refill the stage of tile cn-1 with the next tile of the stream,
-    // then the scores of tile cn+1 on the matrix cores interleaved with the
-    // softmax of S_j, then O += P_j V_j.  scur holds S_j, snext receives the
+    // then the scores of tile cn+1 and O += P_j V_j on the matrix cores,
+    // interleaved with the softmax of S_j.  scur holds S_j, snext receives the
     // scores of tile cn+1, which on the item's last tile is the first tile of
     // the next item (computed with that item's query rows).  j >= nt is a
     // no-op (the loop below is unrolled by two).
@@ -492,19 +486,33 @@ void attn_fwd_kernel(FwdParams p) {
             const float m_use = m == -__builtin_inff() ? 0.f : m;
             float rs = 0.f;
             bf16x8 pk[BC / 16];
-            s16x4 vf[2][NV];
+            s16x4 vf[2 * KPG][NV];
 #pragma unroll
             for (int kb = 0; kb < BC / 32; ++kb) snext[kb] = f32x16{};
+            // group gr: the scores of tile cn+1 for d-slices 2gr, 2gr+1,
+            // weight chunk gr of tile cn, and O += P V for the key slices
+            // whose weights the previous chunk made, so the matrix products
+            // of both halves share the groups with the softmax arithmetic
 #pragma unroll
             for (int gr = 0; gr < NG; ++gr) {
                 __builtin_amdgcn_sched_barrier(0);
                 if (gr + 1 < NG) read_k(cn + 1, gr + 1, kf[(gr + 1) & 1]);
-                else read_v(cn, 0, vf[0]);
+#pragma unroll
+                for (int u = 0; u < KPG; ++u) read_v(cn, gr * KPG + u, vf[(gr & 1) * KPG + u]);
                 mfma_k(gr, kf[gr & 1], snext);
                 weight_chunk(gr, scur, pk, m_use, rs);
+                if (gr > 0) {
+#pragma unroll
+                    for (int u = 0; u < KPG; ++u)
+                        mfma_v((gr - 1) * KPG + u, vf[((gr - 1) & 1) * KPG + u], pk);
+                }
             }
+            __builtin_amdgcn_sched_barrier(0);
+#pragma unroll
+            for (int u = 0; u < KPG; ++u)
+                mfma_v((NG - 1) * KPG + u, vf[((NG - 1) & 1) * KPG + u], pk);
+            __builtin_amdgcn_sched_barrier(0);
             lsum += rs;
-            pv(cn, vf, pk);
             __builtin_amdgcn_s_setprio(0);
         } else {
             // no tile of this item for this wave; it may still owe the first
