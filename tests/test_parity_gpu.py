@@ -61,6 +61,31 @@ def test_small_prefill_matches_oracle(api, dev, case):
         assert np.all(o[:, :Sq - Skv] == 0)
 
 
+# Batches wide enough for 256-row items on 8-wave workgroups (at least one
+# item per CU of a 256-CU GPU); the cases above, with fewer items, run
+# 128-row items on 4-wave workgroups.  Both paths compute each row the same
+# way; these pin the wide path's edges.
+WIDE = [  # B, Sq, Skv, Hq, Hkv, d, causal
+    (16, 300, 300, 16, 16, 128, True),    # ragged last query and key tiles
+    (16, 200, 77, 16, 8, 64, True),       # Sq > Skv: leading rows fully masked
+    (16, 129, 257, 16, 4, 128, True),     # Sq < Skv, bottom-right causal
+    (8, 260, 333, 32, 8, 128, False),
+]
+
+
+@pytest.mark.parametrize("case", WIDE, ids=lambda c: "B%d_Sq%d_Skv%d_Hq%d_Hkv%d_d%d_%s" % (
+    *c[:6], "causal" if c[6] else "full"))
+def test_wide_batch_prefill_matches_oracle(api, dev, case):
+    B, Sq, Skv, Hq, Hkv, d, causal = case
+    data = si.make_prefill(300 + Sq + Skv, B, Hq, Hkv, Sq, Skv, d)
+    scale = si.default_scale(d)
+    o, lse = run_fwd(api, dev, data, scale, causal)
+    o_ref, lse_ref = cpu.attn_full(data["q"], data["k"], data["v"], scale, causal)
+    assert_close(o, o_ref, lse, lse_ref, str(case))
+    if causal and Sq > Skv:
+        assert np.all(o[:, :Sq - Skv] == 0)
+
+
 def test_tiny_config_whole_and_golden(api, dev):
     """Workload 1 (B1 H2 S256 d64, non-causal) compared in full."""
     spec, data = si.make_config(1)

@@ -18,7 +18,9 @@
 //  * one work item = 256 query rows of one (batch, head); a workgroup of 8
 //    waves runs one item at a time, one workgroup per CU (two waves per
 //    SIMD); each wave owns 32 rows and keeps its Q fragment, running max/sum
-//    and fp32 output accumulator in registers;
+//    and fp32 output accumulator in registers.  A fixed batch with fewer
+//    256-row items than CUs runs 128-row items on 4-wave workgroups instead
+//    (one wave per SIMD, twice as many items, so more CUs work);
 //  * K and V tiles of 64 keys move HBM -> LDS with buffer loads that write
 //    straight to LDS (buffer_load_dwordx4 ... lds, no register staging) into
 //    a 4-stage ring: while tile j is consumed, tile j+1 is ready and tiles
@@ -75,13 +77,12 @@ namespace attn {
 
 namespace {
 
-constexpr int NW = kFwdWaves;
-constexpr int NT = kFwdThreads;
-constexpr int BR = kFwdBr;
 constexpr int BC = kFwdBc;
 constexpr int NS = 4;                 // LDS ring stages
 
-template <int D>
+// NW waves per workgroup (8, or 4 for grids with fewer 256-row items than
+// CUs), 32 query rows each
+template <int D, int NW>
 struct FwdLay {
     static constexpr int KP = D + 8;                 // K row pitch (elements)
     // V rows are read with transposing reads: a half-wave reads 64 bytes of
@@ -105,7 +106,8 @@ struct FwdLay {
     static_assert(KR + VR <= NW && KW >= 1 && VW >= 1, "load plan");
 };
 
-// One work item: query rows q0 .. q0+BR-1 of one (batch or sequence, head).
+// One work item: query rows q0 .. q0+BR-1 (BR = 32 per wave) of one (batch or
+// sequence, head).
 struct FwdItem {
     int b, h;
     int Sq, Skv;            // query rows and keys of the sequence
@@ -116,7 +118,7 @@ struct FwdItem {
     int64_t qrow0, krow0;   // first query / key row of the sequence
 };
 
-template <bool CAUSAL, bool VARLEN, bool SPLIT>
+template <bool CAUSAL, bool VARLEN, bool SPLIT, int BR>
 __device__ __forceinline__ FwdItem fwd_item(const FwdParams &p, int it) {
     FwdItem x;
     const int BH = p.nbatch * p.Hq;
@@ -178,11 +180,13 @@ __device__ __forceinline__ int fwd_item_at(const FwdParams &p, int r) {
     return row * G + ((row & 1) ? mirror : w);
 }
 
-template <int D, bool CAUSAL, bool VARLEN, bool SPLIT>
-__global__ __launch_bounds__(NT) __attribute__((amdgpu_waves_per_eu(2, 2)))
+template <int D, bool CAUSAL, bool VARLEN, bool SPLIT, int NW>
+__global__ __launch_bounds__(64 * NW) __attribute__((amdgpu_waves_per_eu(NW / 4, NW / 4)))
 void attn_fwd_kernel(FwdParams p) {
     static_assert(!(VARLEN && SPLIT), "split-KV is for fixed batches");
-    using L = FwdLay<D>;
+    static_assert(NW == 4 || NW == 8, "one or two waves per SIMD");
+    constexpr int BR = 32 * NW;
+    using L = FwdLay<D, NW>;
     __shared__ __attribute__((aligned(16))) __bf16 lds[NS * L::STAGE];
 
     const int tid = threadIdx.x;
@@ -193,13 +197,13 @@ void attn_fwd_kernel(FwdParams p) {
     const int64_t hd_q = (int64_t)p.Hq * D;
     const int64_t hd_k = (int64_t)p.Hkv * D;
 
-    auto item = [&](int r) { return fwd_item<CAUSAL, VARLEN, SPLIT>(p, fwd_item_at(p, r)); };
+    auto item = [&](int r) { return fwd_item<CAUSAL, VARLEN, SPLIT, BR>(p, fwd_item_at(p, r)); };
     // next item after position r that has key tiles, or -1
     auto next_tiled = [&](int r) -> int {
         for (int s = r + 1;; ++s) {
             const int it = fwd_item_at(p, s);
             if (it < 0) return -1;
-            if (fwd_item<CAUSAL, VARLEN, SPLIT>(p, it).nt > 0) return s;
+            if (fwd_item<CAUSAL, VARLEN, SPLIT, BR>(p, it).nt > 0) return s;
         }
     };
 
@@ -622,7 +626,7 @@ void attn_fwd_kernel(FwdParams p) {
         for (int r = r0 + 1; r1 < 0 || r < r1; ++r) {
             const int it = fwd_item_at(p, r);
             if (it < 0) break;
-            const FwdItem x = fwd_item<CAUSAL, VARLEN, SPLIT>(p, it);
+            const FwdItem x = fwd_item<CAUSAL, VARLEN, SPLIT, BR>(p, it);
             if (x.q0 < x.Sq && x.nt == 0) {
                 write_out(x, true);
                 stores = true;
@@ -742,24 +746,33 @@ __global__ __launch_bounds__(256) void attn_fwd_merge_kernel(FwdParams p) {
     if (p.lse != nullptr && lane == 0) p.lse[row] = lse;
 }
 
-template <int D, bool CAUSAL, bool VARLEN, bool SPLIT>
+template <int D, bool CAUSAL, bool VARLEN, bool SPLIT, int NW = 8>
 hipError_t launch_t(const FwdParams &p_in, hipStream_t s) {
     FwdParams p = p_in;
+    // the host counts 256-row tiles; the 4-wave variant (fixed batches only)
+    // has 128-row ones
+    if constexpr (NW == 4) p.ntiles = (p.Sq + 127) / 128;
     const int64_t items = (int64_t)p.ntiles * p.nbatch * p.Hq * (SPLIT ? p.nsplit : 1);
     if (items <= 0) return hipSuccess;
     if (items > 0x7fffffff) return hipErrorInvalidConfiguration;
     p.nitems = (int)items;
     int grid = p.nitems;
-    if (!VARLEN) {
+    if constexpr (!VARLEN) {
         // one workgroup per CU (the LDS ring allows no more), each walking
         // its share of the items
         int cus = 0;
         const hipError_t e = current_cu_count(&cus);
         if (e != hipSuccess) return e;
+        if constexpr (NW == 8 && !SPLIT) {
+            // fewer 256-row items than CUs: 128-row items on 4-wave
+            // workgroups occupy more CUs (one wave per SIMD instead of two)
+            if (cus > 0 && items < cus && p.Sq > 128)
+                return launch_t<D, CAUSAL, VARLEN, SPLIT, 4>(p_in, s);
+        }
         if (cus > 0 && grid > cus) grid = cus;
     }
-    hipLaunchKernelGGL((attn_fwd_kernel<D, CAUSAL, VARLEN, SPLIT>), dim3((unsigned)grid), dim3(NT),
-                       0, s, p);
+    hipLaunchKernelGGL((attn_fwd_kernel<D, CAUSAL, VARLEN, SPLIT, NW>), dim3((unsigned)grid),
+                       dim3(64 * NW), 0, s, p);
     hipError_t e = hipGetLastError();
     if (!SPLIT || e != hipSuccess) return e;
     const int64_t rows = (int64_t)p.nbatch * p.Hq * p.Sq;

@@ -17,9 +17,10 @@ constexpr float kLog2e = 1.44269504088896340736f;
 // weights exp2(s*c - m) stay <= 2^8, far from fp32/bf16 overflow.
 constexpr float kRescaleSlack = 8.0f;
 
-// Prefill tile shape: 8 waves x 32 query rows, 64 keys per K/V tile.
+// Prefill tile shape: 8 waves x 32 query rows, 64 keys per K/V tile (the
+// host counts query tiles of kFwdBr rows; the launcher halves the tile, on
+// 4-wave workgroups, for fixed batches with fewer tiles than CUs).
 constexpr int kFwdWaves = 8;
-constexpr int kFwdThreads = 64 * kFwdWaves;
 constexpr int kFwdBr = 32 * kFwdWaves;
 constexpr int kFwdBc = 64;
 
