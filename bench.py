@@ -65,7 +65,7 @@ def decode_bytes(B, Hq, Hkv, Skv, d, kv_elem_bytes=2):
 
 TRAFFIC_PATH = os.path.join(ROOT, "profiles", "traffic.json")
 # which kernels make up each reported path (substrings of the rocprofv3 names)
-TRAFFIC_KERNELS = {"prefill": ["attn_fwd_kernel<128, true, false, false>"],
+TRAFFIC_KERNELS = {"prefill": ["attn_fwd_kernel<128, true, false, false, 8>"],
                    "decode": ["attn_decode_split_kernel<128, false>",
                               "attn_decode_combine_kernel<128>"],
                    "decode_fp8": ["attn_decode_split_kernel<128, true>"],
@@ -437,7 +437,7 @@ def main():
                        "min": round(float(pre_ms.min()), 5), "cold": round(cold_prefill_ms, 5)},
         "roofline": {"bound": "mfma", "achieved": round(tflops, 2), "peak": PEAK_BF16_TFLOPS,
                      "unit": "TFLOP/s", "frac": round(tflops / PEAK_BF16_TFLOPS, 4),
-                     "traffic": traffic, "kernel": "attn_fwd_kernel<128, true, false, false>"},
+                     "traffic": traffic, "kernel": "attn_fwd_kernel<128, true, false, false, 8>"},
         "decode": {
             "value": round(gbs, 1), "unit": "GB/s",
             "ms": {"mean": round(dec_avg, 5), "median": round(float(np.median(dec_ms)), 5),
