@@ -749,14 +749,22 @@ __global__ __launch_bounds__(256) void attn_fwd_merge_kernel(FwdParams p) {
 template <int D, bool CAUSAL, bool VARLEN, bool SPLIT, int NW = 8>
 hipError_t launch_t(const FwdParams &p_in, hipStream_t s) {
     FwdParams p = p_in;
-    // the host counts 256-row tiles; the 4-wave variant (fixed batches only)
-    // has 128-row ones
-    if constexpr (NW == 4) p.ntiles = (p.Sq + 127) / 128;
+    // the host counts 256-row tiles; the 4-wave variant has 128-row ones (a
+    // ragged batch: twice the count, an upper bound for every sequence; the
+    // items past a sequence's end have no rows and end at once)
+    if constexpr (NW == 4) p.ntiles = VARLEN ? 2 * p_in.ntiles : (p.Sq + 127) / 128;
     const int64_t items = (int64_t)p.ntiles * p.nbatch * p.Hq * (SPLIT ? p.nsplit : 1);
     if (items <= 0) return hipSuccess;
     if (items > 0x7fffffff) return hipErrorInvalidConfiguration;
     p.nitems = (int)items;
     int grid = p.nitems;
+    if constexpr (VARLEN && NW == 8) {
+        // fewer 256-row items than CUs: 128-row items on 4-wave workgroups
+        int cus = 0;
+        const hipError_t e = current_cu_count(&cus);
+        if (e != hipSuccess) return e;
+        if (cus > 0 && items < cus) return launch_t<D, CAUSAL, VARLEN, SPLIT, 4>(p_in, s);
+    }
     if constexpr (!VARLEN) {
         // one workgroup per CU (the LDS ring allows no more), each walking
         // its share of the items
