@@ -86,6 +86,35 @@ def test_wide_batch_prefill_matches_oracle(api, dev, case):
         assert np.all(o[:, :Sq - Skv] == 0)
 
 
+@pytest.mark.parametrize("causal", [False, True], ids=["full", "causal"])
+def test_wide_and_small_grid_paths_agree_bitwise(api, dev, causal):
+    """A 16-sequence batch runs 256-row items on 8-wave workgroups; its first
+    sequence alone (fewer items than CUs) runs 128-row items on 4-wave ones.
+    Each row is computed the same way, so the shared rows match bit for bit;
+    the same holds for a ragged batch and its first sequence."""
+    import torch
+    B, S, Hq, Hkv, d = 16, 700, 16, 4, 128
+    data = si.make_prefill(81, B, Hq, Hkv, S, S, d)
+    q, k, v = (to_dev(data[x], dev) for x in "qkv")
+    o_all, l_all = api.attn_fwd(q, k, v, causal=causal)
+    o_one, l_one = api.attn_fwd(q[:1].contiguous(), k[:1].contiguous(), v[:1].contiguous(),
+                                causal=causal)
+    torch.cuda.synchronize()
+    assert torch.equal(o_all[:1].view(torch.int16), o_one.view(torch.int16))
+    assert torch.equal(l_all[:1], l_one)
+    # ragged: 16 sequences of 700 tokens packed, against the first one alone
+    qv, kv, vv = (t.reshape(B * S, t.shape[2], d) for t in (q, k, v))
+    cu = torch.arange(0, (B + 1) * S, S, dtype=torch.int32, device=dev)
+    o_r, l_r = api.attn_fwd_varlen(qv, kv, vv, cu, cu, S, S, causal=causal)
+    cu1 = cu[:2].contiguous()
+    o_r1, l_r1 = api.attn_fwd_varlen(qv[:S].contiguous(), kv[:S].contiguous(), vv[:S].contiguous(),
+                                     cu1, cu1, S, S, causal=causal)
+    torch.cuda.synchronize()
+    assert torch.equal(o_r[:S].view(torch.int16), o_r1.view(torch.int16))
+    assert torch.equal(l_r[:, :S], l_r1)
+    assert torch.equal(o_r[:S].view(torch.int16), o_one[0].view(torch.int16))
+
+
 def test_tiny_config_whole_and_golden(api, dev):
     """Workload 1 (B1 H2 S256 d64, non-causal) compared in full."""
     spec, data = si.make_config(1)
