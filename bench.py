@@ -14,8 +14,8 @@ allowed query/key pair); the decode rate in algorithmic GB/s (K and V read
 once, plus Q, O and LSE) is reported beside it.  Kernel durations come from
 HIP events on the stream the kernels are launched on.
 
-Prints ONE JSON line.  ``--gpus N`` with N > 1 is refused: this build runs on
-one GPU.
+Prints ONE JSON line.  ``--gpus N`` with N > 1 is refused: the benchmark runs
+on one GPU.
 """
 from __future__ import annotations
 
@@ -331,7 +331,7 @@ def main():
         write_traffic(*args.write_traffic)
         return
     if args.gpus != 1:
-        print("bench.py runs on one GPU only; --gpus %d is not supported by this build"
+        print("bench.py runs on one GPU only; --gpus %d is not supported"
               % args.gpus, file=sys.stderr)
         sys.exit(2)
     if args.extra not in ("all", "none") and not set(args.extra.split(",")) <= set(EXTRAS):
@@ -349,8 +349,8 @@ def main():
     def to_dev(bits):
         return torch.from_numpy(np.ascontiguousarray(bits).view(np.int16)).view(torch.bfloat16).to(dev)
 
-    pspec, pdata = si.make_config(2)
-    dspec, ddata = si.make_config(4)
+    pspec, pdata = si.make_workload("causal_prefill")
+    dspec, ddata = si.make_workload("gqa_decode")
     q, k, v = (to_dev(pdata[n]) for n in "qkv")
     o = torch.empty_like(q)
     lse = torch.empty((pspec["B"], pspec["Hq"], pspec["Sq"]), dtype=torch.float32, device=dev)

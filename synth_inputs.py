@@ -34,8 +34,8 @@ from __future__ import annotations
 import numpy as np
 
 __all__ = [
-    "f32_to_bf16_bits", "bf16_to_f32", "bf16_to_f64", "CONFIGS",
-    "make_prefill", "make_decode", "make_decode_fp8", "make_varlen", "make_config",
+    "f32_to_bf16_bits", "bf16_to_f32", "bf16_to_f64", "WORKLOADS",
+    "make_prefill", "make_decode", "make_decode_fp8", "make_varlen", "make_workload",
     "make_kmeans",
 ]
 
@@ -68,17 +68,17 @@ def bf16_to_f64(bits: np.ndarray) -> np.ndarray:
 
 # The five workloads, with their sizes.  ``scale`` is the float32 value
 # 1/sqrt(d) that both sides receive.
-CONFIGS = {
-    1: dict(kind="prefill", name="tiny non-causal B1 H2 S256 d64", B=1, Hq=2, Hkv=2,
+WORKLOADS = {
+    "tiny": dict(kind="prefill", name="tiny non-causal B1 H2 S256 d64", B=1, Hq=2, Hkv=2,
             Sq=256, Skv=256, d=64, causal=False, seed=1),
-    2: dict(kind="prefill", name="causal prefill B4 H16 S2048 d128", B=4, Hq=16, Hkv=16,
+    "causal_prefill": dict(kind="prefill", name="causal prefill B4 H16 S2048 d128", B=4, Hq=16, Hkv=16,
             Sq=2048, Skv=2048, d=128, causal=True, seed=2),
-    3: dict(kind="prefill", name="long causal prefill B1 H32 S16384 d128 (K per head x U(0.5,2))",
+    "long_causal": dict(kind="prefill", name="long causal prefill B1 H32 S16384 d128 (K per head x U(0.5,2))",
             B=1, Hq=32, Hkv=32, Sq=16384, Skv=16384, d=128, causal=True, seed=3,
             k_head_scale=True),
-    4: dict(kind="decode", name="GQA decode B64 Hq32 Hkv8 Skv4096 d128 8 splits", B=64, Hq=32,
+    "gqa_decode": dict(kind="decode", name="GQA decode B64 Hq32 Hkv8 Skv4096 d128 8 splits", B=64, Hq=32,
             Hkv=8, Skv=4096, d=128, num_splits=8, seed=4),
-    5: dict(kind="varlen", name="ragged causal 16 seqs L~U[128,8192] H32 d128", nseq=16,
+    "ragged": dict(kind="varlen", name="ragged causal 16 seqs L~U[128,8192] H32 d128", nseq=16,
             lo=128, hi=8192, H=32, d=128, causal=True, seed=5),
 }
 
@@ -209,9 +209,9 @@ def make_varlen_cross(seed, lengths_q, lengths_k, H, d, Hkv=None):
                 cu_seqlens_q=cu_q, cu_seqlens_k=cu_k, lengths_q=lq, lengths_k=lk)
 
 
-def make_config(n: int):
-    """Inputs and the spec for one of the five workloads."""
-    spec = dict(CONFIGS[n])
+def make_workload(name: str):
+    """Inputs and the spec for one of the five named workloads."""
+    spec = dict(WORKLOADS[name])
     if spec["kind"] == "prefill":
         data = make_prefill(spec["seed"], spec["B"], spec["Hq"], spec["Hkv"], spec["Sq"],
                             spec["Skv"], spec["d"], spec.get("k_head_scale", False))

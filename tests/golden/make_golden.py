@@ -28,7 +28,7 @@ ROWS = [(0, 0, 0), (0, 0, 1), (0, 1, 127), (0, 1, 128), (0, 0, 255), (0, 1, 255)
 
 
 def tiny_case(causal):
-    spec = dict(si.CONFIGS[1])
+    spec = dict(si.WORKLOADS["tiny"])
     data = si.make_prefill(spec["seed"], spec["B"], spec["Hq"], spec["Hkv"], spec["Sq"],
                            spec["Skv"], spec["d"])
     scale = si.default_scale(spec["d"])

@@ -15,7 +15,7 @@ GOLDEN = os.path.join(os.path.dirname(os.path.abspath(__file__)), "golden")
 def test_oracle_reproduces_stored_rows(name):
     g = json.load(open(os.path.join(GOLDEN, name)))
     assert "FlashAttention-4" in g["citation"]
-    spec = si.CONFIGS[1]
+    spec = si.WORKLOADS["tiny"]
     data = si.make_prefill(spec["seed"], spec["B"], spec["Hq"], spec["Hkv"], spec["Sq"],
                            spec["Skv"], spec["d"])
     for fn in (ref.attention_rows, cpu.attn_rows):

@@ -43,7 +43,7 @@ def test_head_scaled_keys():
 
 
 def test_varlen_lengths_drawn_first_inclusive():
-    spec = si.CONFIGS[5]
+    spec = si.WORKLOADS["ragged"]
     rng = np.random.default_rng(spec["seed"])
     lengths = rng.integers(spec["lo"], spec["hi"] + 1, spec["nseq"])
     assert lengths.min() >= 128 and lengths.max() <= 8192 and len(lengths) == 16

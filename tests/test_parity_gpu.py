@@ -117,7 +117,7 @@ def test_wide_and_small_grid_paths_agree_bitwise(api, dev, causal):
 
 def test_tiny_config_whole_and_golden(api, dev):
     """Workload 1 (B1 H2 S256 d64, non-causal) compared in full."""
-    spec, data = si.make_config(1)
+    spec, data = si.make_workload("tiny")
     o, lse = run_fwd(api, dev, data, spec["scale"], False)
     o_ref, lse_ref = ref.attention(*(si.bf16_to_f64(data[n]) for n in "qkv"), spec["scale"], False)
     assert_close(o, o_ref, lse, lse_ref, "workload 1")
@@ -125,9 +125,9 @@ def test_tiny_config_whole_and_golden(api, dev):
 
 # -------------------------------------------------- the workloads at full size
 
-@pytest.mark.parametrize("n", [2, 3])
-def test_full_size_prefill_sampled_rows(api, dev, n):
-    spec, data = si.make_config(n)
+@pytest.mark.parametrize("n, name", [(2, "causal_prefill"), (3, "long_causal")], ids=["causal_prefill", "long_causal"])
+def test_full_size_prefill_sampled_rows(api, dev, n, name):
+    spec, data = si.make_workload(name)
     o, lse = run_fwd(api, dev, data, spec["scale"], True)
     rows = sample_rows(spec["B"], spec["Hq"], spec["Sq"], 160, seed=n,
                        extra_rows=(spec["Sq"] // 2, spec["Sq"] // 2 - 1, 63, 64))
@@ -142,7 +142,7 @@ def test_full_size_prefill_sampled_rows(api, dev, n):
 
 def test_decode_workload_whole(api, dev):
     import torch
-    spec, data = si.make_config(4)
+    spec, data = si.make_workload("gqa_decode")
     q, k, v = (to_dev(data[x], dev) for x in "qkv")
     o, lse = api.attn_decode(q, k, v, scale=spec["scale"], num_splits=spec["num_splits"])
     torch.cuda.synchronize()
@@ -152,7 +152,7 @@ def test_decode_workload_whole(api, dev):
 
 def test_varlen_workload_sampled_rows(api, dev):
     import torch
-    spec, data = si.make_config(5)
+    spec, data = si.make_workload("ragged")
     cu = data["cu_seqlens"]
     maxlen = api.attn_varlen_check(cu, int(cu[-1]))
     q, k, v = (to_dev(data[x], dev) for x in "qkv")
@@ -368,7 +368,7 @@ def test_decode_fp8_workload_sampled_sequences(api, dev):
     """The decode workload's sizes (B64 Hq32 Hkv8 Skv4096 d128, 8 chunks) with an fp8
     cache, in the launch configuration the benchmark times; the oracle checks
     eight whole sequences."""
-    spec = si.CONFIGS[4]
+    spec = si.WORKLOADS["gqa_decode"]
     B, Hq, Hkv, Skv, d = (spec[x] for x in ("B", "Hq", "Hkv", "Skv", "d"))
     data = si.make_decode_fp8(spec["seed"], B, Hq, Hkv, Skv, d)
     scale = si.default_scale(d)
@@ -542,7 +542,7 @@ def test_large_scores_do_not_overflow(api, dev):
 
 
 def test_bitwise_deterministic(api, dev):
-    spec = si.CONFIGS[2]
+    spec = si.WORKLOADS["causal_prefill"]
     data = si.make_prefill(16, 2, 8, 8, 1024, 1024, 128)
     a = run_fwd(api, dev, data, 0.088, True)
     for _ in range(3):
