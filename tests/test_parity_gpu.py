@@ -140,6 +140,22 @@ def test_full_size_prefill_sampled_rows(api, dev, n, name):
     np.testing.assert_array_equal(o[:, 0], v[:, 0, :, :].repeat(spec["Hq"] // spec["Hkv"], axis=1))
 
 
+@pytest.mark.parametrize("causal", [False, True], ids=["full", "causal"])
+def test_small_grid_long_items_sampled_rows(api, dev, causal):
+    """B1 H8 S4096 d128: 128 items of 256 rows, fewer than the CUs, so the
+    library runs 128-row items on 4-wave workgroups; each item walks up to
+    64 key tiles.  Sampled rows against the oracle, tile edges included."""
+    B, H, S, d = 1, 8, 4096, 128
+    data = si.make_prefill(46, B, H, H, S, S, d)
+    scale = si.default_scale(d)
+    o, lse = run_fwd(api, dev, data, scale, causal)
+    rows = sample_rows(B, H, S, 160, seed=46, extra_rows=(127, 128, 255, 256, 4095 - 128, 4095))
+    o_ref, lse_ref = cpu.attn_rows(data["q"], data["k"], data["v"], scale, causal, rows)
+    b, h, i = rows[:, 0], rows[:, 1], rows[:, 2]
+    assert_close(o[b, i, h], o_ref, lse[b, h, i], lse_ref, "B1 H8 S4096")
+    assert np.all(np.isfinite(o)) and np.all(np.isfinite(lse))
+
+
 def test_decode_workload_whole(api, dev):
     import torch
     spec, data = si.make_workload("gqa_decode")
