@@ -36,6 +36,7 @@ PEAK_HBM_GBS = 8000.0         # MI355X HBM3E
 METRIC = "attn fwd TFLOP/s (bf16 causal prefill) + decode KV GB/s, % of roofline"
 KERNEL_SOURCES = ["tiled_attention_transformer_amd/csrc/attn_fwd.hip",
                   "tiled_attention_transformer_amd/csrc/attn_decode.hip",
+                  "tiled_attention_transformer_amd/csrc/kmeans_assign.hip",
                   "tiled_attention_transformer_amd/csrc/tile_common.h",
                   "tiled_attention_transformer_amd/csrc/kernels.h"]
 
@@ -69,7 +70,7 @@ TRAFFIC_KERNELS = {"prefill": ["attn_fwd_kernel<128, true, false, false, 8>"],
                    "decode": ["attn_decode_split_kernel<128, false>",
                               "attn_decode_combine_kernel<128>"],
                    "decode_fp8": ["attn_decode_split_kernel<128, true>"],
-                   "kmeans": ["kmeans_assign_kernel<128>"]}
+                   "kmeans": ["kmeans_assign_kernel<128, 128>"]}
 # paths whose kernels only run with a context line (absent from a run without it)
 TRAFFIC_OPTIONAL = {"decode_fp8", "kmeans"}
 
@@ -243,7 +244,7 @@ def kmeans_assign(api, dev, stream, gen, d, timed, out):
         "ms": round(ms, 5), "TFLOP/s": round(fl / (ms * 1e-3) / 1e12, 1),
         "frac_of_2500": round(fl / (ms * 1e-3) / 1e12 / PEAK_BF16_TFLOPS, 4),
         "algorithmic_flop": fl, "traffic": load_traffic("kmeans"),
-        "kernel": "kmeans_assign_kernel<128>"}
+        "kernel": "kmeans_assign_kernel<128, 128>"}
     del mu, lab, x, c, idx, dist
 
 

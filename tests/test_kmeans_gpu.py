@@ -77,6 +77,8 @@ KMEANS = [  # N, K, d
     (700, 300, 64),        # several tiles, ragged
     (5000, 1024, 128),     # the page's K and d
     (4096, 2000, 128),     # centroid count not a multiple of 64
+    (3000, 1500, 64),      # 128-centroid tiles (K >= 1024), d = 64, ragged last tile
+    (2000, 1024, 64),      # exactly eight 128-centroid tiles
 ]
 
 
@@ -106,11 +108,12 @@ def test_kmeans_workload_sampled_points(api, dev):
     assert np.mean(idx == data["label"]) > 0.999
 
 
-def test_kmeans_duplicated_centroids_pick_the_lowest_index(api, dev):
+@pytest.mark.parametrize("K", [300, 1100], ids=["tiles64", "tiles128"])
+def test_kmeans_duplicated_centroids_pick_the_lowest_index(api, dev, K):
     """Bit-identical centroid rows give bit-identical computed distances, so an
     exact tie must go to the lowest index -- across tiles, 32-row blocks and the
-    two lane halves."""
-    N, K, d = 2000, 300, 128
+    two lane halves (64-centroid tiles below K = 1024, 128-centroid ones above)."""
+    N, d = 2000, 128
     data = si.make_kmeans(21, N, K, d)
     c = data["c"].copy()
     pairs = [(5, 40), (5, 77), (3, 100), (70, 64), (131, 290), (2, 6), (33, 32 + 64 * 2)]

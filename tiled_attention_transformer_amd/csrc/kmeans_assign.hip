@@ -16,8 +16,9 @@
 //    32w .. 32w+31 in registers as the B operand of S^T = C X^T
 //    (v_mfma_f32_32x32x16_bf16, fp32 accumulation), so every lane owns one
 //    point and half of each tile's centroid rows;
-//  * 64-centroid tiles stream through a 4-stage LDS ring filled by buffer
-//    loads written straight to LDS (every wave issues 1/8 of each tile), one
+//  * 64-centroid tiles (128 from K = 1024 on) stream through a 4-stage LDS
+//    ring filled by buffer loads written straight to LDS (every wave issues
+//    1/8 of each tile), one
 //    workgroup barrier per tile; rows are unpadded with XOR-swizzled 16-byte
 //    chunks, so the A-operand reads are free of bank conflicts;
 //  * -|c|^2 / 2 of the tile after the current one is computed by all 512
@@ -45,10 +46,9 @@ namespace {
 constexpr int KW = 8;                    // waves per workgroup
 constexpr int KT = 64 * KW;              // threads
 constexpr int KP = 32 * KW;              // points per workgroup
-constexpr int CT = 64;                   // centroids per tile
 constexpr int KSTG = 4;                  // ring stages
 
-template <int D>
+template <int D, int CT>          // CT centroids per tile
 struct AsgLay {
     static constexpr int RB = D * 2;                   // bytes per centroid row
     static constexpr int CPR = RB / 16;                // 16-byte chunks per row
@@ -72,10 +72,10 @@ __device__ __forceinline__ bool asg_better(float s1, int k1, float s2, int k2) {
     return s1 > s2 || (s1 == s2 && k1 < k2);
 }
 
-template <int D>
+template <int D, int CT>
 __global__ __launch_bounds__(KT)
 void kmeans_assign_kernel(AssignParams p) {
-    using L = AsgLay<D>;
+    using L = AsgLay<D, CT>;
     __shared__ __attribute__((aligned(16))) unsigned char lds[L::TOTAL];
     float *cnorm = reinterpret_cast<float *>(lds + L::RING);
 
@@ -125,16 +125,18 @@ void kmeans_assign_kernel(AssignParams p) {
         for (int i = 0; i < L::LPW; ++i) buffer_lds_dma16(cr, goff[i], dst + dst_off[i]);
     };
 
-    // -|c|^2/2 of tile j (-inf past the last centroid): 8 threads per
-    // centroid, D/8 elements each, summed by v_dot2_f32_bf16 and then across
-    // the 8 threads
-    const int nr_row = tid >> 3, nr_part = tid & 7;
+    // -|c|^2/2 of tile j (-inf past the last centroid): NPR threads per
+    // centroid, D/NPR elements each, summed by v_dot2_f32_bf16 and then across
+    // the NPR threads
+    constexpr int NPR = KT / CT;
+    constexpr int CPT = D / (8 * NPR);         // 16-byte chunks per thread
+    const int nr_row = tid / NPR, nr_part = tid % NPR;
     auto tile_norms = [&](int j) {
         const unsigned char *t = lds + (j % KSTG) * L::T_BYTES + nr_row * L::RB;
         float acc = 0.f;
 #pragma unroll
-        for (int i = 0; i < D / 64; ++i) {
-            const int lc = (D / 64) * nr_part + i;
+        for (int i = 0; i < CPT; ++i) {
+            const int lc = CPT * nr_part + i;
             const bf16x8 v = ld_lds_bf16x8((const __bf16 *)(t + 16 * (lc ^ asg_swz<D>(nr_row))));
 #pragma unroll
             for (int e = 0; e < 8; e += 2) {
@@ -142,9 +144,8 @@ void kmeans_assign_kernel(AssignParams p) {
                 acc = __builtin_amdgcn_fdot2_f32_bf16(w, w, acc, false);
             }
         }
-        acc += __shfl_xor(acc, 1);
-        acc += __shfl_xor(acc, 2);
-        acc += __shfl_xor(acc, 4);
+#pragma unroll
+        for (int m = 1; m < NPR; m <<= 1) acc += __shfl_xor(acc, m);
         if (nr_part == 0)
             cnorm[(j % KSTG) * CT + nr_row] = j * CT + nr_row < p.K ? -0.5f * acc : -__builtin_inff();
     };
@@ -187,7 +188,7 @@ void kmeans_assign_kernel(AssignParams p) {
         const unsigned char *st = lds + (j % KSTG) * L::T_BYTES;
         const float *nrm = cnorm + (j % KSTG) * CT;
 #pragma unroll
-        for (int kb = 0; kb < 2; ++kb) {
+        for (int kb = 0; kb < CT / 32; ++kb) {
             // accumulators start at -|c|^2/2 of this lane's rows 8q + 4g .. +3
             f32x16 s;
 #pragma unroll
@@ -199,7 +200,7 @@ void kmeans_assign_kernel(AssignParams p) {
 #pragma unroll
             for (int t = 0; t < D / 16; ++t)
                 s = mfma32x32x16(ld_lds_bf16x8((const __bf16 *)(st + kb * 32 * L::RB + aof[t])), xf[t], s);
-            const int blk = 2 * j + kb;
+            const int blk = (CT / 32) * j + kb;
 #pragma unroll
             for (int r = 0; r < 16; ++r) {
                 const bool gt = s[r] > best[r];
@@ -254,12 +255,18 @@ void kmeans_assign_kernel(AssignParams p) {
 hipError_t launch_kmeans_assign(const AssignParams &p, int d, hipStream_t s) {
     const int64_t blocks = ((int64_t)p.N + KP - 1) / KP;
     if (blocks > 0x7fffffff) return hipErrorInvalidConfiguration;
-    if (d == 128)
-        hipLaunchKernelGGL(kmeans_assign_kernel<128>, dim3((unsigned)blocks), dim3(KT), 0, s, p);
-    else if (d == 64)
-        hipLaunchKernelGGL(kmeans_assign_kernel<64>, dim3((unsigned)blocks), dim3(KT), 0, s, p);
-    else
+    // 128-centroid tiles halve the per-tile barrier, wait and norm work; with
+    // few centroids the half-empty last tile and the deeper prologue cost more
+    const bool wide = p.K >= 1024;
+    if (d == 128) {
+        if (wide) hipLaunchKernelGGL((kmeans_assign_kernel<128, 128>), dim3((unsigned)blocks), dim3(KT), 0, s, p);
+        else hipLaunchKernelGGL((kmeans_assign_kernel<128, 64>), dim3((unsigned)blocks), dim3(KT), 0, s, p);
+    } else if (d == 64) {
+        if (wide) hipLaunchKernelGGL((kmeans_assign_kernel<64, 128>), dim3((unsigned)blocks), dim3(KT), 0, s, p);
+        else hipLaunchKernelGGL((kmeans_assign_kernel<64, 64>), dim3((unsigned)blocks), dim3(KT), 0, s, p);
+    } else {
         return hipErrorInvalidValue;
+    }
     return hipGetLastError();
 }
 
