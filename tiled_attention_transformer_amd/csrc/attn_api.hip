@@ -229,6 +229,7 @@ attn_status_t attn_fwd_varlen(const void *q, const void *k, const void *v, void 
     p.group = Hq / Hkv;
     p.total_q = total_q;
     p.total_k = total_k;
+    p.max_len = max_seqlen_q > max_seqlen_k ? max_seqlen_q : max_seqlen_k;
     p.ntiles = ntiles;
     p.c = scale * attn::kLog2e;
     return from_hip(attn::launch_fwd(p, d, causal != 0, true, stream));

@@ -69,7 +69,9 @@
 //    rather than in the kernel's tail (measured ~5 % faster on the causal
 //    B4 H16 S2048 prefill than the reverse order, same HBM traffic).
 //    Ragged batches launch one workgroup per item instead: their item sizes
-//    are known only on the device, and the hardware dispatcher balances them.
+//    are known only on the device, and the hardware dispatcher balances them
+//    (unless every sequence is at most 512 tokens: items of one or two tiles
+//    keep a static walk balanced, and the persistent grid is used).
 #include "kernels.h"
 #include "tile_common.h"
 
@@ -764,6 +766,10 @@ hipError_t launch_t(const FwdParams &p_in, hipStream_t s) {
         const hipError_t e = current_cu_count(&cus);
         if (e != hipSuccess) return e;
         if (cus > 0 && items < cus) return launch_t<D, CAUSAL, VARLEN, SPLIT, 4>(p_in, s);
+        // short sequences only (at most two tiles per item, so a static walk
+        // stays balanced): a persistent grid, one workgroup per CU, whose
+        // load stream runs across items instead of a workgroup per item
+        if (cus > 0 && p.max_len <= 512) grid = cus;
     }
     if constexpr (!VARLEN) {
         // one workgroup per CU (the LDS ring allows no more), each walking

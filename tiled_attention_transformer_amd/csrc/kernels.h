@@ -61,6 +61,7 @@ struct FwdParams {
     int nbatch;              // B, or nseq for varlen
     int Hq, Hkv, group;      // group = Hq / Hkv
     int Sq, Skv;             // fixed batch only
+    int max_len;             // ragged batch: longest query or key sequence (launch choice)
     int total_q, total_k;    // varlen only
     int ntiles;              // query tiles per (batch, head)
     int nitems;              // ntiles * nbatch * Hq (* nsplit; set by the launcher)
