@@ -150,10 +150,10 @@ def write_traffic(fetch_dir: str, write_dir: str):
     print(json.dumps(out))
 
 
-EXTRAS = ("fp8", "kmeans", "long", "ragged")
+EXTRAS = ("decode_auto", "fp8", "kmeans", "long", "ragged")
 
 
-def extra_workloads(api, dev, stream, which=EXTRAS, calls=5, dec_ms=None):
+def extra_workloads(api, dev, stream, which=EXTRAS, calls=20, dec_ms=None, dec_inputs=None):
     """Context lines beside the headline: the long causal workload (B1 H32
     S16384 d128), the ragged causal batch (16 sequences, lengths drawn
     U{128..8192} with seed 5, H32 d128), the decode workload's sizes with
@@ -170,20 +170,40 @@ def extra_workloads(api, dev, stream, which=EXTRAS, calls=5, dec_ms=None):
     gen = torch.Generator(device=dev)
     d = 128
 
-    def timed(fn, warm=2, n=calls):
+    def timed(fn, warm=0, n=calls, settle=0.2):
         # fresh buffers: the first calls also pay first-touch address
-        # translation, so the short workloads take more warm-up calls
+        # translation, and the clocks ramp up under load, so calls run back
+        # to back for `settle` seconds first; then n calls back to back with
+        # an event at every call boundary
+        t = time.perf_counter()
+        while time.perf_counter() - t < settle:
+            for _ in range(5):
+                fn()
+            torch.cuda.synchronize()
         for _ in range(warm):
             fn()
-        ev = [(torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True))
-              for _ in range(n)]
-        for a, b in ev:
-            a.record(stream)
+        ev = [torch.cuda.Event(enable_timing=True) for _ in range(n + 1)]
+        ev[0].record(stream)
+        for i in range(n):
             fn()
-            b.record(stream)
+            ev[i + 1].record(stream)
         torch.cuda.synchronize()
-        return float(np.mean([a.elapsed_time(b) for a, b in ev]))
+        return float(np.mean([ev[i].elapsed_time(ev[i + 1]) for i in range(n)]))
 
+    # the decode workload with the library's split choice (whole sequences
+    # per workgroup, waves merged in the kernel, no workspace)
+    if "decode_auto" in which and dec_inputs is not None:
+        dq, dk, dv, do, dlse, spec = dec_inputs
+        ms = timed(lambda: api.attn_decode(dq, dk, dv, o=do, lse=dlse, scale=spec["scale"],
+                                           num_splits=0, stream=stream), n=50)
+        nb = decode_bytes(spec["B"], spec["Hq"], spec["Hkv"], spec["Skv"], spec["d"])
+        gbs = nb / (ms * 1e-3) / 1e9
+        out["decode_library_choice_B64_Hq32_Hkv8_Skv4096_d128"] = {
+            "ms": round(ms, 5), "GB/s": round(gbs, 1), "frac_of_8000": round(gbs / PEAK_HBM_GBS, 4),
+            "num_splits": api.attn_decode_pick_splits(spec["B"], spec["Hq"], spec["Hkv"], spec["Skv"]),
+            "algorithmic_bytes": nb, "traffic": load_traffic("decode_auto"),
+            "kernel": "attn_decode_split_kernel<128, false> (whole sequences per workgroup, "
+                      "the four waves merged in the kernel)"}
     # decode with an fp8 KV cache (the decode workload's sizes)
     if "fp8" in which:
         fp8_decode(api, dev, stream, gen, d, timed, out, dec_ms)
@@ -210,17 +230,19 @@ def fp8_decode(api, dev, stream, gen, d, timed, out, dec_ms):
         del x
     o = torch.empty_like(q)
     lse = torch.empty((B, Hq), dtype=torch.float32, device=dev)
-    ws = torch.empty(max(1, api.attn_decode_workspace_bytes(B, Hq, Hkv, Skv, d, 8)),
+    # the library's split choice (whole sequences per workgroup at these sizes)
+    ws = torch.empty(max(1, api.attn_decode_workspace_bytes(B, Hq, Hkv, Skv, d, 0)),
                      dtype=torch.uint8, device=dev)
     ms = timed(lambda: api.attn_decode_fp8(q, codes[0], codes[1], scales[0], scales[1], o=o,
-                                           lse=lse, num_splits=8, workspace=ws, stream=stream),
-               warm=50, n=50)
+                                           lse=lse, num_splits=0, workspace=ws, stream=stream),
+               n=50)
     nb = decode_bytes(B, Hq, Hkv, Skv, d, kv_elem_bytes=1)
     gbs = nb / (ms * 1e-3) / 1e9
     out["decode_fp8_kv_B64_Hq32_Hkv8_Skv4096_d128"] = {
         "ms": round(ms, 5), "GB/s": round(gbs, 1), "frac_of_8000": round(gbs / PEAK_HBM_GBS, 4),
         "algorithmic_bytes": nb, "traffic": load_traffic("decode_fp8"),
-        "kernel": "attn_decode_split_kernel<128, true>",
+        "kernel": "attn_decode_split_kernel<128, true> (library's split choice: whole "
+                  "sequences per workgroup)",
         "speedup_vs_bf16_cache": None if dec_ms is None else round(dec_ms / ms, 3)}
     del q, codes, o, lse, ws
 
@@ -237,8 +259,7 @@ def kmeans_assign(api, dev, stream, gen, d, timed, out):
     c = (mu + 0.25 * torch.randn((K, d), generator=gen, device=dev)).to(torch.bfloat16)
     idx = torch.empty(N, dtype=torch.int32, device=dev)
     dist = torch.empty(N, dtype=torch.float32, device=dev)
-    ms = timed(lambda: api.attn_kmeans_assign(x, c, idx=idx, dist=dist, stream=stream),
-               warm=50, n=50)
+    ms = timed(lambda: api.attn_kmeans_assign(x, c, idx=idx, dist=dist, stream=stream), n=50)
     fl = 2.0 * N * K * d
     out["kmeans_assign_N65536_K1024_d128"] = {
         "ms": round(ms, 5), "TFLOP/s": round(fl / (ms * 1e-3) / 1e12, 1),
@@ -312,8 +333,10 @@ def main():
     ap = argparse.ArgumentParser(description=__doc__.split("\n")[0])
     ap.add_argument("--gpus", type=int, default=1)
     ap.add_argument("--steps", type=int, default=100)
-    ap.add_argument("--warmup", type=int, default=200,
-                    help="untimed steps first (the clocks need some tens of ms to settle)")
+    ap.add_argument("--warmup", type=int, default=20, help="untimed steps before the timed ones")
+    ap.add_argument("--settle", type=float, default=0.5,
+                    help="seconds of back-to-back steps before the warm-up steps, so the "
+                         "GPU clocks have ramped up (reported as settle_s / settle_steps)")
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--extra", default="all",
                     help="context workloads beside the headline: all, none, or a comma list "
@@ -381,6 +404,19 @@ def main():
     torch.cuda.synchronize()
     cold_prefill_ms, cold_decode_ms = e0.elapsed_time(e1), e1.elapsed_time(e2)
 
+    # Clock settle: the GPU clocks take some tens of milliseconds of steady
+    # load to ramp up, so steps run back to back for args.settle seconds
+    # before the warm-up steps, whatever their count (reported apart).
+    settle_steps = 0
+    t_settle = time.perf_counter()
+    while time.perf_counter() - t_settle < args.settle:
+        for _ in range(10):
+            prefill()
+            decode()
+        settle_steps += 10
+        torch.cuda.synchronize()
+    settle_s = time.perf_counter() - t_settle
+
     for _ in range(args.warmup):
         prefill()
         decode()
@@ -391,20 +427,24 @@ def main():
         torch.cuda.synchronize()
         del src, dst
 
+    # Timed region: K steps launched back to back, with one event at every
+    # kernel boundary (before prefill i, between prefill i and decode i,
+    # after decode i = before prefill i+1) on the launch stream.
     K = args.steps
-    ev = [[torch.cuda.Event(enable_timing=True) for _ in range(3)] for _ in range(K)]
+    ev = [torch.cuda.Event(enable_timing=True) for _ in range(2 * K + 1)]
     torch.cuda.synchronize()
     t0 = time.perf_counter()
+    ev[0].record(stream)
     for i in range(K):
-        ev[i][0].record(stream)
         prefill()
-        ev[i][1].record(stream)
+        ev[2 * i + 1].record(stream)
         decode()
-        ev[i][2].record(stream)
+        ev[2 * i + 2].record(stream)
     torch.cuda.synchronize()
     wall = time.perf_counter() - t0
-    pre_ms = np.array([a.elapsed_time(b) for a, b, _ in ev])
-    dec_ms = np.array([b.elapsed_time(c) for _, b, c in ev])
+    pre_ms = np.array([ev[2 * i].elapsed_time(ev[2 * i + 1]) for i in range(K)])
+    dec_ms = np.array([ev[2 * i + 1].elapsed_time(ev[2 * i + 2]) for i in range(K)])
+    step_ms = ev[0].elapsed_time(ev[2 * K]) / K
 
     flops = prefill_flops(pspec["B"], pspec["Hq"], pspec["Sq"], pspec["Skv"], pspec["d"], True)
     nbytes = decode_bytes(dspec["B"], dspec["Hq"], dspec["Hkv"], dspec["Skv"], dspec["d"])
@@ -420,7 +460,10 @@ def main():
         "n_gpus": 1,
         "steps": K,
         "warmup": args.warmup,
-        "ms_per_step": round(wall * 1e3 / K, 4),
+        "ms_per_step": round(step_ms, 4),
+        "wall_ms_per_step": round(wall * 1e3 / K, 4),
+        "settle_s": round(settle_s, 3),
+        "settle_steps": settle_steps,
         "higher_is_better": True,
         "scaling": "weak",
         "vs_baseline": None,
@@ -428,7 +471,7 @@ def main():
         "data": "synthetic (seeded bf16 N(0,1))",
         "config": {
             "workload": "causal prefill B4 H16 Sq=Skv=2048 d128 + GQA decode B64 Hq32 Hkv8 "
-                        "Skv4096 d128, 8 KV chunks",
+                        "Skv4096 d128 split into %d KV chunks, then the LSE merge kernel" % nsplit,
             "prefill": {"B": 4, "Hq": 16, "Hkv": 16, "S": 2048, "d": 128, "causal": True,
                         "seed": pspec["seed"], "algorithmic_flop": flops},
             "decode": {"B": 64, "Hq": 32, "Hkv": 8, "Skv": 4096, "d": 128, "num_splits": nsplit,
@@ -446,16 +489,17 @@ def main():
             "roofline": {"bound": "hbm", "achieved": round(gbs, 1), "peak": PEAK_HBM_GBS,
                          "unit": "GB/s", "frac": round(gbs / PEAK_HBM_GBS, 4),
                          "traffic": load_traffic("decode"),
-                         "kernel": "attn_decode_split_kernel<128, false> (whole sequences per "
-                                   "workgroup, waves merged in the kernel; the combine kernel "
-                                   "runs only when the groups do not fill the GPU)"},
+                         "kernel": "attn_decode_split_kernel<128, false> (%d key chunks per "
+                                   "sequence) + attn_decode_combine_kernel<128> (LSE merge of "
+                                   "the chunks)" % nsplit},
         },
         "kernel_hash": kernel_hash(),
     }
     which = () if args.no_extra or args.extra == "none" else \
         EXTRAS if args.extra == "all" else tuple(args.extra.split(","))
     if which:
-        result["extra"] = extra_workloads(api, dev, stream, which=which, dec_ms=dec_avg)
+        result["extra"] = extra_workloads(api, dev, stream, which=which, dec_ms=dec_avg,
+                                          dec_inputs=(dq, dk, dv, do, dlse, dspec))
     if not args.no_cpu_baseline:
         result["cpu_baseline"] = cpu_baseline(pspec, pdata, args.cpu_pairs)
     print(json.dumps(result), flush=True)

@@ -20,8 +20,9 @@
  * ---------------------------------------
  *  * Tensors are contiguous, row-major, bfloat16 (q, k, v, o) and float32
  *    (lse), passed as raw DEVICE pointers.  The caller allocates and owns
- *    every buffer; the library allocates nothing and keeps no state between
- *    calls, so calls are thread-safe.
+ *    every buffer; the library allocates nothing.  The only state it keeps
+ *    between calls is a per-device cache of the compute-unit count (read
+ *    once, a property of the device), so calls are thread-safe.
  *  * Pointers to bf16 tensors must be 16-byte aligned; lse and the decode
  *    workspace 4- and 16-byte aligned respectively.
  *  * Head grouping (GQA/MQA): query head h reads KV head h / (Hq / Hkv);
@@ -154,18 +155,23 @@ attn_status_t attn_varlen_check(const int *cu_seqlens_host, int nseq, int total,
  * KV head, chunk) -- every query head of a KV group shares one pass over that
  * chunk of K and V -- and the chunks are merged:
  * LSE = M + log(sum_s exp(lse_s - M)), O = sum_s exp(lse_s - LSE) * O_s.
- * When the (sequence, KV head) groups spread evenly over the GPU's compute
- * units, each workgroup takes whole sequences instead: its four waves split
- * the keys and their results are merged the same way inside the kernel, and
- * the workspace is not touched; otherwise the chunks spread over the
- * workgroups and a second kernel merges partials kept in the workspace.
- * Either way the result is the same log-sum-exp merge (up to fp32 rounding
- * order), and it is deterministic for given sizes and num_splits.
- * num_splits <= 0 lets the library choose (attn_decode_pick_splits).
+ * A positive num_splits is honoured as given: with more than one chunk the
+ * chunks spread over the workgroups, each writes a normalised fp32 partial
+ * and its log-sum-exp into the workspace, and a second kernel merges them.
+ * With one chunk (num_splits == 1) each workgroup takes whole sequences: its
+ * four waves split the keys, their results are merged the same way inside
+ * the kernel, and no workspace is used.  Either way the result is the same
+ * log-sum-exp merge (up to fp32 rounding order), and it is deterministic for
+ * given sizes and num_splits.
+ * num_splits <= 0 lets the library choose (attn_decode_pick_splits): one
+ * chunk when the (sequence, KV head, block of 32 query heads) groups alone
+ * give each of an MI355X's 256 compute units a work item, else about one
+ * work item per compute unit with chunks of at least 512 keys.
  * workspace: DEVICE scratch of at least attn_decode_workspace_bytes(...)
  * bytes, 16-byte aligned, owned by the caller, may be reused between calls
- * on the same stream (not by calls that run concurrently).  With
- * num_splits == 1 no workspace is needed (may be NULL).
+ * on the same stream (not by calls that run concurrently).  When the split
+ * count resolves to 1 no workspace is needed (may be NULL); the size needed
+ * depends on the sizes and num_splits only.
  */
 attn_status_t attn_decode(const void *q, const void *k_cache, const void *v_cache, void *o,
                           float *lse, int B, int Hq, int Hkv, int Skv, int d, float scale,
@@ -277,7 +283,9 @@ size_t attn_decode_workspace_bytes(int B, int Hq, int Hkv, int Skv, int d, int n
 
 /* The number of KV chunks attn_decode uses when passed num_splits <= 0:
  * about one work item per compute unit of an MI355X (256 items over the
- * (sequence, KV head, head block) groups), but chunks of at least 512 keys. */
+ * (sequence, KV head, head block) groups), but chunks of at least 512 keys;
+ * so 1 (whole sequences, no workspace) when the groups alone number 256 or
+ * more. */
 int attn_decode_pick_splits(int B, int Hq, int Hkv, int Skv);
 
 /* Static text for a status code (never NULL). */

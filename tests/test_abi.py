@@ -13,6 +13,20 @@ import pytest
 import tiled_attention_transformer_amd as pkg
 from tiled_attention_transformer_amd import _lib
 
+
+def _gpu_visible() -> bool:
+    try:
+        import torch
+        return torch.cuda.device_count() > 0
+    except Exception:
+        return False
+
+
+# The fake device addresses below must never reach a kernel: on a machine
+# with a GPU a validation regression would launch on them, so these host
+# tests run only where no GPU is visible.
+pytestmark = pytest.mark.skipif(_gpu_visible(), reason="host-only ABI tests (fake device pointers)")
+
 ROOT = os.path.dirname(os.path.dirname(os.path.abspath(__file__)))
 HEADER = os.path.join(ROOT, "include", "attn.h")
 
@@ -260,3 +274,16 @@ def test_decode_split_choice(lib):
     assert lib.attn_decode_pick_splits(1, 3, 2, 100) == 0
     auto = lib.attn_decode_workspace_bytes(1, 32, 8, 4096, 128, 0)
     assert auto == lib.attn_decode_workspace_bytes(1, 32, 8, 4096, 128, 8)
+
+
+def test_decode_workspace_of_the_gqa_decode_workload(lib):
+    """B64 Hq32 Hkv8 Skv4096 d128: the library's choice is whole sequences
+    (512 groups fill the GPU) and needs no workspace; an explicit 8 chunks
+    is honoured and needs the partials (8 x 64 x 32 x (128 + 1) fp32)."""
+    assert lib.attn_decode_pick_splits(64, 32, 8, 4096) == 1
+    assert lib.attn_decode_workspace_bytes(64, 32, 8, 4096, 128, 0) == 0
+    assert lib.attn_decode_workspace_bytes(64, 32, 8, 4096, 128, 1) == 0
+    assert lib.attn_decode_workspace_bytes(64, 32, 8, 4096, 128, 8) == 8 * 64 * 32 * 129 * 4
+    # 8 chunks without a workspace are refused before any launch
+    assert lib.attn_decode(P, P, P, P, None, 64, 32, 8, 4096, 128, 0.088, 8, None, 0,
+                           None) == WS

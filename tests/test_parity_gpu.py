@@ -115,81 +115,161 @@ def test_wide_and_small_grid_paths_agree_bitwise(api, dev, causal):
     assert torch.equal(o_r[:S].view(torch.int16), o_one[0].view(torch.int16))
 
 
-def test_tiny_config_whole_and_golden(api, dev):
-    """Workload 1 (B1 H2 S256 d64, non-causal) compared in full."""
+def _golden(name):
+    import json
+    import os
+    path = os.path.join(os.path.dirname(os.path.abspath(__file__)), "golden", name)
+    return json.load(open(path))
+
+
+@pytest.mark.parametrize("causal", [False, True], ids=["full", "causal"])
+def test_tiny_config_whole_and_golden(api, dev, causal):
+    """Workload 1 (B1 H2 S256 d64) compared in full with the numpy oracle,
+    and the stored oracle rows of tests/golden/ compared with the kernel's."""
     spec, data = si.make_workload("tiny")
-    o, lse = run_fwd(api, dev, data, spec["scale"], False)
-    o_ref, lse_ref = ref.attention(*(si.bf16_to_f64(data[n]) for n in "qkv"), spec["scale"], False)
+    o, lse = run_fwd(api, dev, data, spec["scale"], causal)
+    o_ref, lse_ref = ref.attention(*(si.bf16_to_f64(data[n]) for n in "qkv"), spec["scale"],
+                                   causal)
     assert_close(o, o_ref, lse, lse_ref, "workload 1")
+    g = _golden("tiny_%s_rows.json" % ("causal" if causal else "noncausal"))
+    assert g["causal"] == causal and g["scale"] == spec["scale"]
+    rows = np.array(g["rows"], dtype=np.int64)
+    b, h, i = rows[:, 0], rows[:, 1], rows[:, 2]
+    assert_close(o[b, i, h], np.array(g["o"]), lse[b, h, i], np.array(g["lse"]), "golden rows")
 
 
 # -------------------------------------------------- the workloads at full size
 
-@pytest.mark.parametrize("n, name", [(2, "causal_prefill"), (3, "long_causal")], ids=["causal_prefill", "long_causal"])
-def test_full_size_prefill_sampled_rows(api, dev, n, name):
-    spec, data = si.make_workload(name)
-    o, lse = run_fwd(api, dev, data, spec["scale"], True)
-    rows = sample_rows(spec["B"], spec["Hq"], spec["Sq"], 160, seed=n,
-                       extra_rows=(spec["Sq"] // 2, spec["Sq"] // 2 - 1, 63, 64))
-    o_ref, lse_ref = cpu.attn_rows(data["q"], data["k"], data["v"], spec["scale"], True, rows)
-    b, h, i = rows[:, 0], rows[:, 1], rows[:, 2]
-    assert_close(o[b, i, h], o_ref, lse[b, h, i], lse_ref, "workload %d" % n)
-    # every output finite, and causal row 0 is exactly v_0 rounded to bf16
-    assert np.all(np.isfinite(o)) and np.all(np.isfinite(lse))
+def nan_outputs(dev, o_shape, lse_shape):
+    """Output buffers filled with NaN, so a row the kernels never write fails."""
+    import torch
+    o = torch.full(o_shape, float("nan"), dtype=torch.bfloat16, device=dev)
+    lse = torch.full(lse_shape, float("nan"), dtype=torch.float32, device=dev)
+    return o, lse
+
+
+def run_fwd_nan(api, dev, data, scale, causal):
+    import torch
+    q, k, v = (to_dev(data[n], dev) for n in "qkv")
+    B, Sq, Hq, _ = q.shape
+    o, lse = nan_outputs(dev, q.shape, (B, Hq, Sq))
+    api.attn_fwd(q, k, v, o=o, lse=lse, scale=scale, causal=causal)
+    torch.cuda.synchronize()
+    o, lse = bf16_to_np(o), f32_to_np(lse)
+    assert np.all(np.isfinite(o)) and np.all(np.isfinite(lse)), "rows left unwritten"
+    return o, lse
+
+
+def item_rows(B, Hq, Sq, tile, seed):
+    """One random row from every (batch, head, query tile of `tile` rows) work item."""
+    rng = np.random.default_rng(seed)
+    rows = []
+    for b in range(B):
+        for h in range(Hq):
+            for t0 in range(0, Sq, tile):
+                rows.append((b, h, int(rng.integers(t0, min(Sq, t0 + tile)))))
+    return np.array(rows, dtype=np.int64)
+
+
+def test_causal_prefill_workload_every_row(api, dev):
+    """Workload 2 (B4 H16 S2048 d128, causal) in the benchmark's launch
+    configuration, every output row against the C oracle (outputs start as
+    NaN, so a work item the persistent walk skipped would fail)."""
+    spec, data = si.make_workload("causal_prefill")
+    o, lse = run_fwd_nan(api, dev, data, spec["scale"], True)
+    o_ref, lse_ref = cpu.attn_full(data["q"], data["k"], data["v"], spec["scale"], True)
+    err = assert_close(o, o_ref, lse, lse_ref, "workload 2, every row")
+    print("workload 2 every row: max|dO| %.4g max|dLSE| %.3g" % err, flush=True)
     v = si.bf16_to_f64(data["v"])
     np.testing.assert_array_equal(o[:, 0], v[:, 0, :, :].repeat(spec["Hq"] // spec["Hkv"], axis=1))
+
+
+def test_long_causal_workload_whole_heads_and_every_item(api, dev):
+    """Workload 3 (B1 H32 S16384 d128, K of each head scaled by U(0.5, 2)):
+    four whole heads (the sharpest and flattest K scales and two others) and
+    one row of every 256-row work item of every head, against the C oracle."""
+    spec, data = si.make_workload("long_causal")
+    o, lse = run_fwd_nan(api, dev, data, spec["scale"], True)
+    c = data["k_head_scale"]
+    heads = sorted({int(np.argmax(c)), int(np.argmin(c)), 0, spec["Hq"] - 1})
+    S = spec["Sq"]
+    whole = np.array([(0, h, i) for h in heads for i in range(S)], dtype=np.int64)
+    rows = np.concatenate([whole, item_rows(1, spec["Hq"], S, 256, seed=3)])
+    o_ref, lse_ref = cpu.attn_rows(data["q"], data["k"], data["v"], spec["scale"], True, rows)
+    b, h, i = rows[:, 0], rows[:, 1], rows[:, 2]
+    err = assert_close(o[b, i, h], o_ref, lse[b, h, i], lse_ref, "workload 3")
+    print("workload 3 heads %s (K scales %s) + every item: max|dO| %.4g max|dLSE| %.3g"
+          % (heads, np.round(c[heads], 3).tolist(), *err), flush=True)
 
 
 @pytest.mark.parametrize("causal", [False, True], ids=["full", "causal"])
 def test_small_grid_long_items_sampled_rows(api, dev, causal):
     """B1 H8 S4096 d128: 128 items of 256 rows, fewer than the CUs, so the
     library runs 128-row items on 4-wave workgroups; each item walks up to
-    64 key tiles.  Sampled rows against the oracle, tile edges included."""
+    64 key tiles.  One row of every 128-row item, tile edges and random rows
+    against the oracle."""
     B, H, S, d = 1, 8, 4096, 128
     data = si.make_prefill(46, B, H, H, S, S, d)
     scale = si.default_scale(d)
-    o, lse = run_fwd(api, dev, data, scale, causal)
-    rows = sample_rows(B, H, S, 160, seed=46, extra_rows=(127, 128, 255, 256, 4095 - 128, 4095))
+    o, lse = run_fwd_nan(api, dev, data, scale, causal)
+    rows = np.concatenate([sample_rows(B, H, S, 160, seed=46,
+                                       extra_rows=(127, 128, 255, 256, 4095 - 128, 4095)),
+                           item_rows(B, H, S, 128, seed=47)])
     o_ref, lse_ref = cpu.attn_rows(data["q"], data["k"], data["v"], scale, causal, rows)
     b, h, i = rows[:, 0], rows[:, 1], rows[:, 2]
     assert_close(o[b, i, h], o_ref, lse[b, h, i], lse_ref, "B1 H8 S4096")
-    assert np.all(np.isfinite(o)) and np.all(np.isfinite(lse))
 
 
-def test_decode_workload_whole(api, dev):
+@pytest.mark.parametrize("splits", [8, 0], ids=["8chunks_merge_kernel", "library_choice"])
+def test_decode_workload_whole(api, dev, splits):
+    """Workload 4 (B64 Hq32 Hkv8 Skv4096 d128) in full: with the 8 chunks of
+    its recipe (split kernel, then the merge kernel over the partials) and
+    with the library's choice (whole sequences per workgroup, no workspace)."""
     import torch
     spec, data = si.make_workload("gqa_decode")
     q, k, v = (to_dev(data[x], dev) for x in "qkv")
-    o, lse = api.attn_decode(q, k, v, scale=spec["scale"], num_splits=spec["num_splits"])
+    o, lse = nan_outputs(dev, q.shape, q.shape[:2])
+    B, Hq, Hkv, Skv, d = (spec[x] for x in ("B", "Hq", "Hkv", "Skv", "d"))
+    assert (api.attn_decode_workspace_bytes(B, Hq, Hkv, Skv, d, splits) == 0) == (splits == 0)
+    api.attn_decode(q, k, v, o=o, lse=lse, scale=spec["scale"], num_splits=splits)
     torch.cuda.synchronize()
     o_ref, lse_ref = cpu.decode_full(data["q"], data["k"], data["v"], spec["scale"])
-    assert_close(bf16_to_np(o), o_ref, f32_to_np(lse), lse_ref, "workload 4")
+    err = assert_close(bf16_to_np(o), o_ref, f32_to_np(lse), lse_ref, "workload 4")
+    print("workload 4 (num_splits=%d): max|dO| %.4g max|dLSE| %.3g" % (splits, *err), flush=True)
 
 
-def test_varlen_workload_sampled_rows(api, dev):
+def test_varlen_workload_two_heads_and_every_item(api, dev):
+    """Workload 5 (16 ragged sequences, H32 d128, causal): every row of two
+    heads across all 16 sequences, and one row of every (sequence, head,
+    256-row tile) work item, against the C oracle; outputs start as NaN."""
     import torch
     spec, data = si.make_workload("ragged")
     cu = data["cu_seqlens"]
     maxlen = api.attn_varlen_check(cu, int(cu[-1]))
     q, k, v = (to_dev(data[x], dev) for x in "qkv")
     cu_d = torch.from_numpy(cu).to(dev)
-    o, lse = api.attn_fwd_varlen(q, k, v, cu_d, cu_d, maxlen, maxlen, scale=spec["scale"],
-                                 causal=True)
+    o, lse = nan_outputs(dev, q.shape, (spec["H"], q.shape[0]))
+    api.attn_fwd_varlen(q, k, v, cu_d, cu_d, maxlen, maxlen, o=o, lse=lse, scale=spec["scale"],
+                        causal=True)
     torch.cuda.synchronize()
     o, lse = bf16_to_np(o), f32_to_np(lse)
+    assert np.all(np.isfinite(o)) and np.all(np.isfinite(lse)), "rows left unwritten"
     rng = np.random.default_rng(5)
+    H = spec["H"]
     rows = []
     for s in range(spec["nseq"]):
         L = int(cu[s + 1] - cu[s])
-        for i in {0, L - 1, min(L - 1, 127), min(L - 1, 128), int(rng.integers(L)),
-                  int(rng.integers(L))}:
-            rows.append((s, int(rng.integers(spec["H"])), i))
+        for h in (3, H - 5):
+            rows.extend((s, h, i) for i in range(L))
+        for h in range(H):
+            for t0 in range(0, L, 256):
+                rows.append((s, h, int(rng.integers(t0, min(L, t0 + 256)))))
     rows = np.array(rows, dtype=np.int64)
     o_ref, lse_ref = cpu.varlen_rows(data["q"], data["k"], data["v"], cu, cu, spec["scale"],
                                      True, rows)
     gi = cu[rows[:, 0]] + rows[:, 2]
-    assert_close(o[gi, rows[:, 1]], o_ref, lse[rows[:, 1], gi], lse_ref, "workload 5")
-    assert np.all(np.isfinite(o)) and np.all(np.isfinite(lse))
+    err = assert_close(o[gi, rows[:, 1]], o_ref, lse[rows[:, 1], gi], lse_ref, "workload 5")
+    print("workload 5 two heads + every item: max|dO| %.4g max|dLSE| %.3g" % err, flush=True)
 
 
 # -------------------------------------------------------------------- decode
@@ -202,13 +282,17 @@ DECODE = [  # B, Hq, Hkv, Skv, d, splits
     (2, 32, 8, 4096, 128, 0),       # library picks the split count
     (1, 40, 8, 513, 64, 2),
     (4, 16, 2, 129, 128, 1),
-    # 256 or more (sequence, KV head) groups: a workgroup merges all chunks of
-    # its groups itself (uneven last chunk; chunks shorter than the load
-    # ring; empty chunks; d = 64)
+    # 256 or more (sequence, KV head) groups: an explicit split count is
+    # honoured (split kernel, then the merge kernel), while 0 or 1 gives
+    # whole sequences per workgroup, merged in the kernel (uneven last chunk;
+    # chunks shorter than the load ring; empty chunks; d = 64)
     (64, 8, 4, 1000, 128, 7),
+    (64, 8, 4, 1000, 128, 0),
     (64, 8, 4, 200, 128, 3),
+    (64, 8, 4, 200, 128, 1),
     (32, 16, 8, 100, 128, 64),
     (128, 4, 2, 777, 64, 3),
+    (128, 4, 2, 777, 64, 0),
     # few groups, many chunks: the merge kernel's unrolled loop and its tail
     (1, 32, 8, 5000, 128, 37),
     (2, 8, 2, 3000, 64, 100),       # six trailing chunks empty

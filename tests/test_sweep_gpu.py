@@ -9,10 +9,10 @@ Every output is compared with the fp64 oracle on the same bf16 inputs, to the
 same bars as the other parity tests (O max-abs 2e-2 against the unrounded
 oracle, LSE max-abs 1e-3; rows with no allowed key must be O = 0, LSE = -inf).
 
-The logits stay within twice the default spread (scale times query size at
-most 2 / sqrt(d)): the 2e-2 bar on bf16 outputs assumes weights that average
-several keys, and much sharper rows put a single bf16 value of V, rounded
-once more, into O.
+The random shapes keep the logits within twice the default spread (scale
+times query size at most 2 / sqrt(d)); a separate band takes them to 2-8x,
+where the weights concentrate on a few keys, and prints the max |dO| it
+reaches against the same bars.
 """
 import numpy as np
 import pytest
@@ -95,6 +95,48 @@ def test_random_prefill_and_splitkv(api, dev, case):
         dead = Sq - Skv
         for o in (o1, o2):
             assert torch.count_nonzero(o[:, :dead].float()).item() == 0
+
+
+def _draw_sharp(n, seed=2031):
+    """Shapes for the sharp-logit band: scale * |q| between 2 and 8 times
+    the default 1/sqrt(d), so rows are dominated by a few keys."""
+    rng = np.random.default_rng(seed)
+    cases = []
+    for i in range(n):
+        d = int(rng.choice([64, 128]))
+        Hkv = int(rng.choice([1, 2]))
+        Hq = Hkv * int(rng.choice([1, 4]))
+        B = int(rng.integers(1, 3))
+        Sq = _length(rng, 600)
+        Skv = Sq if rng.random() < 0.5 else _length(rng, 800)
+        causal = bool(rng.random() < 0.6)
+        spread = float(np.exp(rng.uniform(np.log(2.0), np.log(8.0))))
+        cases.append((i, B, Sq, Skv, Hq, Hkv, d, causal, round(spread, 3)))
+    return cases
+
+
+SHARP = _draw_sharp(12)
+
+
+@pytest.mark.parametrize("case", SHARP, ids=lambda c: "%d_B%d_Sq%d_Skv%d_Hq%d_Hkv%d_d%d_%s_x%.2f" % (
+    *c[:7], "causal" if c[7] else "full", c[8]))
+def test_sharp_logits_prefill(api, dev, case):
+    """Logits at 2-8x the default spread: weights concentrate on a few keys.
+
+    The same bars as everywhere (O 2e-2 max-abs, LSE 1e-3); the max |dO|
+    is printed so the margin left at these sharpnesses is on record.
+    """
+    import torch
+    i, B, Sq, Skv, Hq, Hkv, d, causal, spread = case
+    scale = float(np.float32(spread / np.sqrt(d)))
+    data = si.make_prefill(1200 + i, B, Hq, Hkv, Sq, Skv, d)
+    q, k, v = (to_dev(data[x], dev) for x in "qkv")
+    o, lse = api.attn_fwd(q, k, v, scale=scale, causal=causal)
+    torch.cuda.synchronize()
+    o_ref, lse_ref = cpu.attn_full(data["q"], data["k"], data["v"], scale, causal)
+    err = assert_close(bf16_to_np(o), o_ref, f32_to_np(lse), lse_ref, "sharp %s" % (case,))
+    print("sharp logits x%.2f %s: max|dO| %.4g max|dLSE| %.3g" % (spread, case[:8], *err),
+          flush=True)
 
 
 def _draw_varlen(n, seed=2028):

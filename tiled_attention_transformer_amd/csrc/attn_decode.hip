@@ -597,17 +597,12 @@ hipError_t launch_t(DecParams p, hipStream_t s) {
     int cus = 0;
     hipError_t e = current_cu_count(&cus);
     if (e != hipSuccess) return e;
-    // When the (sequence, KV head, head block) groups spread evenly over the
-    // CUs (at most 10 % idle), each workgroup takes whole sequences: its
-    // four waves split the keys and merge them, and the result goes out
-    // directly.  Otherwise the key ranges of a sequence spread over the
-    // workgroups and a second kernel merges their partials.
+    // The split count is the caller's (or the host-side choice): one key
+    // range per item means whole sequences per workgroup, whose four waves
+    // split the keys and merge them, and the result goes out directly;
+    // otherwise the key ranges of a sequence spread over the workgroups and
+    // a second kernel merges their partials.
     const int64_t groups = (int64_t)p.B * p.Hkv * p.ncb;
-    const int64_t rounds = (groups + cus - 1) / cus;
-    if (p.nsplit > 1 && groups >= cus && rounds * cus * 10 <= groups * 11) {
-        p.nsplit = 1;
-        p.chunk = p.Skv;
-    }
     const int64_t items = groups * p.nsplit;
     if (items > 0x7fffffff) return hipErrorInvalidConfiguration;
     const int blocks = (int)(items < cus ? items : cus);
