@@ -11,8 +11,15 @@ One step = one pass of the whole path over one batch of synthetic input:
 Inputs are seeded bf16 N(0,1) draws already resident in HBM when timing
 starts.  ``value`` is the prefill throughput in algorithmic TFLOP/s (4*d per
 allowed query/key pair); the decode rate in algorithmic GB/s (K and V read
-once, plus Q, O and LSE) is reported beside it.  Kernel durations come from
-HIP events on the stream the kernels are launched on.
+once, plus Q, O and LSE) is reported beside it.
+
+Timing: after the cold first calls, steps run back to back for ``--settle``
+seconds (the GPU clocks ramp up under load), then ``--warmup`` steps, then
+the K timed steps: their K prefill calls back to back, then their K decode
+calls, with HIP events on the launch stream before, between and after the
+two blocks (an event between every two kernels would add several
+microseconds of idle time per kernel).  Each kernel's average duration is its
+block's time / K.
 
 Prints ONE JSON line.  ``--gpus N`` with N > 1 is refused: the benchmark runs
 on one GPU.
@@ -67,9 +74,9 @@ def decode_bytes(B, Hq, Hkv, Skv, d, kv_elem_bytes=2):
 TRAFFIC_PATH = os.path.join(ROOT, "profiles", "traffic.json")
 # which kernels make up each reported path (substrings of the rocprofv3 names)
 TRAFFIC_KERNELS = {"prefill": ["attn_fwd_kernel<128, true, false, false, 8>"],
-                   "decode": ["attn_decode_split_kernel<128, false>",
+                   "decode": ["attn_decode_split_kernel<128, false, true>",
                               "attn_decode_combine_kernel<128>"],
-                   "decode_fp8": ["attn_decode_split_kernel<128, true>"],
+                   "decode_fp8": ["attn_decode_split_kernel<128, true, false>"],
                    "kmeans": ["kmeans_assign_kernel<128, 128>"]}
 # paths whose kernels only run with a context line (absent from a run without it)
 TRAFFIC_OPTIONAL = {"decode_fp8", "kmeans"}
@@ -150,6 +157,83 @@ def write_traffic(fetch_dir: str, write_dir: str):
     print(json.dumps(out))
 
 
+COUNTERS_PATH = os.path.join(ROOT, "profiles", "sq_counters.json")
+# One rocprofv3 --pmc pass each (at most 8 SQ counters and 2 GRBM per pass).
+COUNTER_PASSES = [
+    ["MfmaUtil", "VALUBusy", "GRBM_GUI_ACTIVE", "SQ_VALU_MFMA_BUSY_CYCLES",
+     "SQ_VALU_MFMA_COEXEC_CYCLES", "SQ_INSTS_VALU_MFMA_MOPS_BF16", "SQ_WAVE_CYCLES",
+     "SQ_WAIT_ANY", "SQ_INSTS_MFMA"],
+    ["GRBM_GUI_ACTIVE", "SQ_INSTS_VALU", "SQ_INSTS_SALU", "SQ_INSTS_LDS", "SQ_ACTIVE_INST_LDS",
+     "SQ_LDS_BANK_CONFLICT", "SQ_WAIT_INST_LDS", "SQ_INSTS_VMEM", "SQ_ACTIVE_INST_ANY"],
+]
+COUNTER_KERNELS = {"prefill": "attn_fwd_kernel<128, true, false, false, 8>",
+                   "decode": "attn_decode_split_kernel<128, false, true>",
+                   "decode_fp8": "attn_decode_split_kernel<128, true, false>",
+                   "kmeans": "kmeans_assign_kernel<128, 128>"}
+
+
+def write_counters(dirs):
+    """Turn ``rocprofv3 --pmc`` runs (one folder per pass of COUNTER_PASSES)
+    into per-kernel means per dispatch, plus:
+
+      mfma_util  = rocprofv3's MfmaUtil (MFMA-busy cycles over all SIMDs'
+                   active cycles), as a fraction
+      valu_busy  = rocprofv3's VALUBusy, as a fraction
+      coexec     = share of SIMD cycles in which the MFMA unit was busy and
+                   a plain VALU instruction issued (MfmaUtil scaled by
+                   SQ_VALU_MFMA_COEXEC_CYCLES / SQ_VALU_MFMA_BUSY_CYCLES)
+      wait_any   = SQ_WAIT_ANY / SQ_WAVE_CYCLES (share of wave time waiting)
+      mfma_flop  = SQ_INSTS_VALU_MFMA_MOPS_BF16 * 512 (matrix FLOP executed)
+    """
+    import csv
+    import glob
+    vals = {}
+    for d in dirs:
+        (path,) = glob.glob(os.path.join(d, "**", "*counter_collection.csv"), recursive=True)
+        per = {}
+        for r in csv.DictReader(open(path)):
+            key = (r["Kernel_Name"], r["Counter_Name"], r.get("Dispatch_Id", ""))
+            per[key] = per.get(key, 0.0) + float(r["Counter_Value"])
+        for (kn, cn, _), v in per.items():
+            vals.setdefault(kn, {}).setdefault(cn, []).append(v)
+    out = {"kernel_hash": kernel_hash(), "passes": COUNTER_PASSES, "kernels": {}}
+    for kind, name in COUNTER_KERNELS.items():
+        ks = [k for k in vals if name in k]
+        if len(ks) != 1:
+            continue
+        c = {cn: sum(v) / len(v) for cn, v in vals[ks[0]].items()}
+        der = {}
+        if "MfmaUtil" in c:
+            der["mfma_util"] = c["MfmaUtil"] / 100.0
+            if c.get("SQ_VALU_MFMA_BUSY_CYCLES"):
+                der["coexec"] = der["mfma_util"] * c.get("SQ_VALU_MFMA_COEXEC_CYCLES", 0.0) / \
+                    c["SQ_VALU_MFMA_BUSY_CYCLES"]
+        if "VALUBusy" in c:
+            der["valu_busy"] = c["VALUBusy"] / 100.0
+        if c.get("SQ_WAVE_CYCLES"):
+            der["wait_any"] = c.get("SQ_WAIT_ANY", 0.0) / c["SQ_WAVE_CYCLES"]
+        if "SQ_INSTS_VALU_MFMA_MOPS_BF16" in c:
+            der["mfma_flop"] = c["SQ_INSTS_VALU_MFMA_MOPS_BF16"] * 512
+        out["kernels"][kind] = {"name": ks[0], "dispatches": len(vals[ks[0]].get("GRBM_GUI_ACTIVE", [])),
+                                "counters": c,
+                                "derived": {k: round(v, 4) for k, v in der.items()}}
+    with open(COUNTERS_PATH, "w") as fh:
+        json.dump(out, fh, indent=1)
+        fh.write("\n")
+    print(json.dumps(out))
+
+
+def load_counters(kind: str):
+    """Derived unit utilisations of a kernel, if taken on these kernel sources."""
+    try:
+        t = json.load(open(COUNTERS_PATH))
+    except (OSError, ValueError):
+        return None
+    if t.get("kernel_hash") != kernel_hash() or kind not in t.get("kernels", {}):
+        return None
+    return t["kernels"][kind]["derived"]
+
+
 EXTRAS = ("decode_auto", "fp8", "kmeans", "long", "ragged")
 
 
@@ -173,8 +257,8 @@ def extra_workloads(api, dev, stream, which=EXTRAS, calls=20, dec_ms=None, dec_i
     def timed(fn, warm=0, n=calls, settle=0.2):
         # fresh buffers: the first calls also pay first-touch address
         # translation, and the clocks ramp up under load, so calls run back
-        # to back for `settle` seconds first; then n calls back to back with
-        # an event at every call boundary
+        # to back for `settle` seconds first; then n calls back to back
+        # between one pair of events
         t = time.perf_counter()
         while time.perf_counter() - t < settle:
             for _ in range(5):
@@ -182,13 +266,13 @@ def extra_workloads(api, dev, stream, which=EXTRAS, calls=20, dec_ms=None, dec_i
             torch.cuda.synchronize()
         for _ in range(warm):
             fn()
-        ev = [torch.cuda.Event(enable_timing=True) for _ in range(n + 1)]
-        ev[0].record(stream)
-        for i in range(n):
+        a, b = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+        a.record(stream)
+        for _ in range(n):
             fn()
-            ev[i + 1].record(stream)
+        b.record(stream)
         torch.cuda.synchronize()
-        return float(np.mean([ev[i].elapsed_time(ev[i + 1]) for i in range(n)]))
+        return a.elapsed_time(b) / n
 
     # the decode workload with the library's split choice (whole sequences
     # per workgroup, waves merged in the kernel, no workspace)
@@ -202,8 +286,8 @@ def extra_workloads(api, dev, stream, which=EXTRAS, calls=20, dec_ms=None, dec_i
             "ms": round(ms, 5), "GB/s": round(gbs, 1), "frac_of_8000": round(gbs / PEAK_HBM_GBS, 4),
             "num_splits": api.attn_decode_pick_splits(spec["B"], spec["Hq"], spec["Hkv"], spec["Skv"]),
             "algorithmic_bytes": nb, "traffic": load_traffic("decode_auto"),
-            "kernel": "attn_decode_split_kernel<128, false> (whole sequences per workgroup, "
-                      "the four waves merged in the kernel)"}
+            "kernel": "attn_decode_split_kernel<128, false, false> (whole sequences per "
+                      "workgroup, the four waves merged in the kernel)"}
     # decode with an fp8 KV cache (the decode workload's sizes)
     if "fp8" in which:
         fp8_decode(api, dev, stream, gen, d, timed, out, dec_ms)
@@ -241,8 +325,8 @@ def fp8_decode(api, dev, stream, gen, d, timed, out, dec_ms):
     out["decode_fp8_kv_B64_Hq32_Hkv8_Skv4096_d128"] = {
         "ms": round(ms, 5), "GB/s": round(gbs, 1), "frac_of_8000": round(gbs / PEAK_HBM_GBS, 4),
         "algorithmic_bytes": nb, "traffic": load_traffic("decode_fp8"),
-        "kernel": "attn_decode_split_kernel<128, true> (library's split choice: whole "
-                  "sequences per workgroup)",
+        "kernel": "attn_decode_split_kernel<128, true, false> (library's split choice: "
+                  "whole sequences per workgroup)",
         "speedup_vs_bf16_cache": None if dec_ms is None else round(dec_ms / ms, 3)}
     del q, codes, o, lse, ws
 
@@ -345,6 +429,11 @@ def main():
                     help="skip every context line (same as --extra none)")
     ap.add_argument("--cpu-pairs", type=float, default=2.0e8,
                     help="allowed query/key pairs in the CPU-baseline sample")
+    ap.add_argument("--write-counters", nargs="+", metavar="DIR",
+                    help="write profiles/sq_counters.json from rocprofv3 --pmc output folders "
+                         "(one per counter pass) and exit (no GPU use)")
+    ap.add_argument("--counter-pass", type=int, metavar="N",
+                    help="print the counters of pass N (for rocprofv3 --pmc) and exit")
     ap.add_argument("--copy-calibration", action="store_true",
                     help="also run a plain 1 GiB device copy (counter calibration)")
     ap.add_argument("--write-traffic", nargs=2, metavar=("FETCH_DIR", "WRITE_DIR"),
@@ -353,6 +442,12 @@ def main():
     args = ap.parse_args()
     if args.write_traffic:
         write_traffic(*args.write_traffic)
+        return
+    if args.write_counters:
+        write_counters(args.write_counters)
+        return
+    if args.counter_pass is not None:
+        print(" ".join(COUNTER_PASSES[args.counter_pass]))
         return
     if args.gpus != 1:
         print("bench.py runs on one GPU only; --gpus %d is not supported"
@@ -427,28 +522,31 @@ def main():
         torch.cuda.synchronize()
         del src, dst
 
-    # Timed region: K steps launched back to back, with one event at every
-    # kernel boundary (before prefill i, between prefill i and decode i,
-    # after decode i = before prefill i+1) on the launch stream.
+    # Timed region: the K steps' prefill calls launched back to back, then
+    # their K decode calls, with one event before, between and after the two
+    # blocks on the launch stream.  An event recorded between two kernels
+    # adds several microseconds of idle GPU time (measured ~5 us per event
+    # against a kernel trace), so events go only at the block boundaries;
+    # the kernels' averages are then block time / K, launch gaps included.
     K = args.steps
-    ev = [torch.cuda.Event(enable_timing=True) for _ in range(2 * K + 1)]
+    ev = [torch.cuda.Event(enable_timing=True) for _ in range(3)]
     torch.cuda.synchronize()
     t0 = time.perf_counter()
     ev[0].record(stream)
-    for i in range(K):
+    for _ in range(K):
         prefill()
-        ev[2 * i + 1].record(stream)
+    ev[1].record(stream)
+    for _ in range(K):
         decode()
-        ev[2 * i + 2].record(stream)
+    ev[2].record(stream)
     torch.cuda.synchronize()
     wall = time.perf_counter() - t0
-    pre_ms = np.array([ev[2 * i].elapsed_time(ev[2 * i + 1]) for i in range(K)])
-    dec_ms = np.array([ev[2 * i + 1].elapsed_time(ev[2 * i + 2]) for i in range(K)])
-    step_ms = ev[0].elapsed_time(ev[2 * K]) / K
+    pre_avg = ev[0].elapsed_time(ev[1]) / K
+    dec_avg = ev[1].elapsed_time(ev[2]) / K
+    step_ms = ev[0].elapsed_time(ev[2]) / K
 
     flops = prefill_flops(pspec["B"], pspec["Hq"], pspec["Sq"], pspec["Skv"], pspec["d"], True)
     nbytes = decode_bytes(dspec["B"], dspec["Hq"], dspec["Hkv"], dspec["Skv"], dspec["d"])
-    pre_avg, dec_avg = float(pre_ms.mean()), float(dec_ms.mean())
     tflops = flops / (pre_avg * 1e-3) / 1e12
     gbs = nbytes / (dec_avg * 1e-3) / 1e9
 
@@ -477,21 +575,21 @@ def main():
             "decode": {"B": 64, "Hq": 32, "Hkv": 8, "Skv": 4096, "d": 128, "num_splits": nsplit,
                        "seed": dspec["seed"], "algorithmic_bytes": nbytes},
         },
-        "prefill_ms": {"mean": round(pre_avg, 5), "median": round(float(np.median(pre_ms)), 5),
-                       "min": round(float(pre_ms.min()), 5), "cold": round(cold_prefill_ms, 5)},
+        "prefill_ms": {"mean": round(pre_avg, 5), "cold": round(cold_prefill_ms, 5)},
         "roofline": {"bound": "mfma", "achieved": round(tflops, 2), "peak": PEAK_BF16_TFLOPS,
                      "unit": "TFLOP/s", "frac": round(tflops / PEAK_BF16_TFLOPS, 4),
-                     "traffic": traffic, "kernel": "attn_fwd_kernel<128, true, false, false, 8>"},
+                     "traffic": traffic, "kernel": "attn_fwd_kernel<128, true, false, false, 8>",
+                     "counters": load_counters("prefill")},
         "decode": {
             "value": round(gbs, 1), "unit": "GB/s",
-            "ms": {"mean": round(dec_avg, 5), "median": round(float(np.median(dec_ms)), 5),
-                   "min": round(float(dec_ms.min()), 5), "cold": round(cold_decode_ms, 5)},
+            "ms": {"mean": round(dec_avg, 5), "cold": round(cold_decode_ms, 5)},
             "roofline": {"bound": "hbm", "achieved": round(gbs, 1), "peak": PEAK_HBM_GBS,
                          "unit": "GB/s", "frac": round(gbs / PEAK_HBM_GBS, 4),
-                         "traffic": load_traffic("decode"),
-                         "kernel": "attn_decode_split_kernel<128, false> (%d key chunks per "
-                                   "sequence) + attn_decode_combine_kernel<128> (LSE merge of "
-                                   "the chunks)" % nsplit},
+                         "traffic": load_traffic("decode"), "counters": load_counters("decode"),
+                         "kernel": "attn_decode_split_kernel<128, false, true> (%d key chunks "
+                                   "per sequence, one chunk per wave at a time) + "
+                                   "attn_decode_combine_kernel<128> (LSE merge of the chunks)"
+                                   % nsplit},
         },
         "kernel_hash": kernel_hash(),
     }

@@ -116,7 +116,12 @@ __device__ __forceinline__ bf16x8 fp8x8_to_bf16(uint32_t lo, uint32_t hi) {
     return __builtin_shufflevector(ab, cd, 0, 1, 2, 3, 4, 5, 6, 7);
 }
 
-template <int D, bool F8>
+// WI (wave items): every wave is a worker of its own that takes whole items
+// (each one key chunk of one group) and writes their partials itself: no
+// merge of the waves, no barrier.  Used for split counts that give every
+// wave of the grid work; otherwise (WI = false) the four waves of a
+// workgroup share each item's keys and merge their states through LDS.
+template <int D, bool F8, bool WI>
 __global__ __launch_bounds__(NT)
 void attn_decode_split_kernel(DecParams p) {
     using L = DecLay<D, F8>;
@@ -134,18 +139,19 @@ void attn_decode_split_kernel(DecParams p) {
     float *merge_l = merge_o + L::MERGE;
 
     // Work items are (group, key range), range fastest, with group =
-    // (sequence, KV head, block of query heads); workgroup w takes items
-    // w, w + grid, ...
-    const int G = gridDim.x;
+    // (sequence, KV head, block of query heads); worker w takes items
+    // w, w + workers, ...  A worker is a workgroup, or with WI a wave.
+    const int G = WI ? (int)gridDim.x * NWV : (int)gridDim.x;
+    const int worker = WI ? (int)blockIdx.x * NWV + wave : (int)blockIdx.x;
     const int nitems = p.B * p.Hkv * p.ncb * p.nsplit;
-    const int my_items = ((int)blockIdx.x < nitems) ? (nitems - (int)blockIdx.x + G - 1) / G : 0;
+    const int my_items = (worker < nitems) ? (nitems - worker + G - 1) / G : 0;
 
     struct Item {
         int b, hk, h0, ncols, sp, k_lo, nkeys, ntiles;
     };
     auto get_item = [&](int it) {
         Item r;
-        const int item = (int)blockIdx.x + G * it;
+        const int item = worker + G * it;
         r.sp = item % p.nsplit;
         int id = item / p.nsplit;
         const int cb = id % p.ncb;
@@ -164,8 +170,13 @@ void attn_decode_split_kernel(DecParams p) {
         r.h0 = r.hk * p.group + NCOL * cb;
         return r;
     };
-    // this wave's tiles of an item: w, w + NWV, ...
-    auto wave_tiles = [&](const Item &it) { return wave < it.ntiles ? (it.ntiles - wave + NWV - 1) / NWV : 0; };
+    // this wave's tiles of an item: w, w + NWV, ... (with WI: all of them)
+    auto wave_tiles = [&](const Item &it) {
+        if constexpr (WI) return it.ntiles;
+        return wave < it.ntiles ? (it.ntiles - wave + NWV - 1) / NWV : 0;
+    };
+    // the position of this wave's tile t within its item, in tiles
+    auto tile_pos = [&](int t) { return WI ? t : wave + NWV * t; };
 
     // Load plan: load m of a tensor (m < LOADS) fills bytes 1024m ..
     // 1024m+1023 of the tile; lane L's 16-byte slot is (row, physical
@@ -205,7 +216,7 @@ void attn_decode_split_kernel(DecParams p) {
     const unsigned char *vbase = static_cast<const unsigned char *>(p.v);
     auto issue_next = [&]() {
         if (li >= my_items) return;
-        const int key0 = litem.k_lo + TK * (wave + NWV * lt);
+        const int key0 = litem.k_lo + TK * tile_pos(lt);
         const int rows = min(TK, litem.k_lo + litem.nkeys - key0);
         __amdgpu_buffer_rsrc_t kr[L::NP], vr[L::NP];
 #pragma unroll
@@ -351,7 +362,7 @@ void attn_decode_split_kernel(DecParams p) {
                         s[kb] = mfma32x32x16(ld_lds_bf16x8((const __bf16 *)(sk + kof[t])), qf[t], s[kb]);
                 }
             }
-            const int kt = TK * (wave + NWV * tw);  // first key of the tile, within the item
+            const int kt = TK * tile_pos(tw);       // first key of the tile, within the item
             if (kt + TK > it.nkeys) {
 #pragma unroll
                 for (int kb = 0; kb < L::NB; ++kb)
@@ -413,6 +424,32 @@ void attn_decode_split_kernel(DecParams p) {
             ++ccnt;
         }
         if (nmine == 0 && ci + 1 < my_items) load_q(get_item(ci + 1), qn);
+
+        if constexpr (WI) {
+            // this wave's own item: its normalised partial and natural-log
+            // LSE go straight to the workspace (an empty chunk: O = 0,
+            // LSE = -inf, weight 0 in the merge)
+            const float lt2 = half_swap_sum(lsum);
+            // 1 / l, times the value scale of an fp8 cache
+            const float inv = lt2 > 0.f ? (F8 ? p.v_scale : 1.f) / lt2 : 0.f;
+            stores = true;
+            if (col < it.ncols) {
+                const int h = it.h0 + col;
+                float *op = p.ws_o + (((int64_t)it.sp * p.B + it.b) * p.Hq + h) * D + 4 * g;
+#pragma unroll
+                for (int db = 0; db < D / 32; ++db)
+#pragma unroll
+                    for (int rq = 0; rq < 4; ++rq) {
+                        const f32x4 v4 = {oacc[db][4 * rq] * inv, oacc[db][4 * rq + 1] * inv,
+                                          oacc[db][4 * rq + 2] * inv, oacc[db][4 * rq + 3] * inv};
+                        *reinterpret_cast<f32x4 *>(op + 32 * db + 8 * rq) = v4;
+                    }
+                if (g == 0)
+                    p.ws_lse[((int64_t)it.sp * p.B + it.b) * p.Hq + h] =
+                        lt2 > 0.f ? (m + fast_log2(lt2)) * kLn2 : -__builtin_inff();
+            }
+            continue;
+        }
 
         // Merge of the four waves' states: per query column, the waves'
         // log-sum-exp values give each wave's weight; the weighted outputs
@@ -594,6 +631,7 @@ __global__ __launch_bounds__(64 * CW) void attn_decode_combine_kernel(DecParams 
 
 template <int D, bool F8>
 hipError_t launch_t(DecParams p, hipStream_t s) {
+    static_assert(NWV == 4, "a workgroup is four waves");
     int cus = 0;
     hipError_t e = current_cu_count(&cus);
     if (e != hipSuccess) return e;
@@ -607,7 +645,13 @@ hipError_t launch_t(DecParams p, hipStream_t s) {
     if (items > 0x7fffffff) return hipErrorInvalidConfiguration;
     const int blocks = (int)(items < cus ? items : cus);
     if (blocks <= 0) return hipSuccess;
-    hipLaunchKernelGGL((attn_decode_split_kernel<D, F8>), dim3((unsigned)blocks), dim3(NT), 0, s, p);
+    // split items for every wave of the grid: waves take whole items
+    if (p.nsplit > 1 && items >= (int64_t)NWV * cus)
+        hipLaunchKernelGGL((attn_decode_split_kernel<D, F8, true>), dim3((unsigned)blocks), dim3(NT), 0,
+                           s, p);
+    else
+        hipLaunchKernelGGL((attn_decode_split_kernel<D, F8, false>), dim3((unsigned)blocks), dim3(NT),
+                           0, s, p);
     e = hipGetLastError();
     if (e != hipSuccess || p.nsplit == 1) return e;
     hipLaunchKernelGGL(attn_decode_combine_kernel<D>, dim3((unsigned)(p.B * p.Hq)), dim3(64 * CW), 0,
