@@ -62,8 +62,12 @@ typedef enum {
     ATTN_ERR_WORKSPACE = 6,      /* decode workspace missing or too small        */
     ATTN_ERR_SEQLENS = 7,        /* malformed cumulative sequence offsets        */
     ATTN_ERR_HIP = 8,            /* the HIP runtime reported an error on launch  */
-    ATTN_ERR_SCALE = 9           /* scale is not finite and > 0                  */
+    ATTN_ERR_SCALE = 9,          /* scale is not finite and > 0                  */
+    ATTN_ERR_SCRATCH_LIMIT = 10  /* the sizes need more than the fixed scratch   */
 } attn_status_t;
+
+/* Size of the fixed device scratch that attn_decode_noalloc uses (bytes). */
+#define ATTN_NOALLOC_SCRATCH_BYTES (16u << 20)
 
 /*
  * Prefill / full forward over a fixed batch.
@@ -275,6 +279,27 @@ attn_status_t attn_decode_fp8(const void *q, const void *k_cache, const void *v_
  */
 attn_status_t attn_kmeans_assign(const void *x, const void *c, int *idx, float *dist, int N, int K,
                                  int d, hipStream_t stream);
+
+/*
+ * attn_decode without a workspace argument and without any allocation, for
+ * callers that cannot allocate device memory: code under HIP graph capture,
+ * tight serving loops, harnesses that forbid hipMalloc.  Same arguments,
+ * layouts, split choice, result and errors as attn_decode, minus
+ * workspace / workspace_bytes.  The split partials live in a fixed array of
+ * ATTN_NOALLOC_SCRATCH_BYTES in device memory that the library holds on
+ * every GPU it runs on until the process ends (its address is looked up
+ * once per device, on the first call there).  Sizes whose partials need
+ * more (attn_decode_workspace_bytes(...) > ATTN_NOALLOC_SCRATCH_BYTES) are
+ * refused with ATTN_ERR_SCRATCH_LIMIT before any launch; with the split
+ * count resolving to 1 no scratch is used at all.  Every call on one GPU
+ * shares that GPU's array: calls that may overlap on one GPU (different
+ * streams, other host threads) race on it and must be serialised by the
+ * caller.  Nothing in the array needs clearing: every partial a call reads
+ * is written by the same call.
+ */
+attn_status_t attn_decode_noalloc(const void *q, const void *k_cache, const void *v_cache,
+                                  void *o, float *lse, int B, int Hq, int Hkv, int Skv, int d,
+                                  float scale, int num_splits, hipStream_t stream);
 
 /* Bytes of decode workspace for these sizes (0 when num_splits resolves to
  * 1; num_splits <= 0 means the library's choice, as in attn_decode).  Returns

@@ -30,7 +30,7 @@ pytestmark = pytest.mark.skipif(_gpu_visible(), reason="host-only ABI tests (fak
 ROOT = os.path.dirname(os.path.dirname(os.path.abspath(__file__)))
 HEADER = os.path.join(ROOT, "include", "attn.h")
 
-OK, NULLPTR, SHAPE, BAD_D, GQA, ALIGN, WS, SEQ, HIP, SCALE = range(10)
+OK, NULLPTR, SHAPE, BAD_D, GQA, ALIGN, WS, SEQ, HIP, SCALE, SCRATCH = range(11)
 P = 1 << 20          # a 16-byte aligned fake address (never dereferenced)
 
 
@@ -47,7 +47,7 @@ def lib():
 
 def test_library_exports_every_declared_symbol(lib):
     names = declared_functions()
-    assert len(names) == 13, names
+    assert len(names) == 14, names
     raw = ctypes.CDLL(_lib.LIB_PATH)
     for n in names:
         assert hasattr(raw, n), n
@@ -55,7 +55,7 @@ def test_library_exports_every_declared_symbol(lib):
 
 
 def test_status_strings(lib):
-    for s in range(10):
+    for s in range(11):
         text = lib.attn_status_string(s)
         assert text and text != b"unknown status"
     assert lib.attn_status_string(99) == b"unknown status"
@@ -287,3 +287,23 @@ def test_decode_workspace_of_the_gqa_decode_workload(lib):
     # 8 chunks without a workspace are refused before any launch
     assert lib.attn_decode(P, P, P, P, None, 64, 32, 8, 4096, 128, 0.088, 8, None, 0,
                            None) == WS
+
+
+def test_decode_noalloc_validation(lib):
+    """The no-allocation decode: attn_decode's checks in the same order, and
+    sizes whose split partials exceed the fixed 16 MiB scratch refused before
+    any launch (and before the scratch is looked up)."""
+    def nd(q=P, o=P, lse=None, B=2, Hq=8, Hkv=2, Skv=100, d=128, scale=0.1, splits=4):
+        return lib.attn_decode_noalloc(q, P, P, o, lse, B, Hq, Hkv, Skv, d, scale, splits, None)
+    assert nd(q=None) == NULLPTR
+    assert nd(B=0) == SHAPE
+    assert nd(d=80) == BAD_D
+    assert nd(Hq=6, Hkv=4) == GQA
+    assert nd(scale=float("inf")) == SCALE
+    assert nd(splits=70000) == SHAPE
+    assert nd(o=P + 4) == ALIGN
+    assert nd(lse=P + 2) == ALIGN
+    # B64 Hq32 Hkv8 d128: 8 chunks of partials take 8.45 MB, 16 chunks 16.9 MB
+    assert lib.attn_decode_workspace_bytes(64, 32, 8, 4096, 128, 16) > 16 << 20
+    assert nd(B=64, Hq=32, Hkv=8, Skv=4096, splits=16) == SCRATCH
+    assert nd(B=1024, Hq=64, Hkv=8, Skv=4096, splits=2) == SCRATCH

@@ -18,6 +18,7 @@ SIGNATURES = {
     "attn_fwd_splitkv_workspace_bytes": (_sz, [_i, _i, _i, _i, _i, _i, _i]),
     "attn_varlen_check": (_i, [_p, _i, _i, _p]),
     "attn_decode": (_i, [_p, _p, _p, _p, _p, _i, _i, _i, _i, _i, _f, _i, _p, _sz, _p]),
+    "attn_decode_noalloc": (_i, [_p, _p, _p, _p, _p, _i, _i, _i, _i, _i, _f, _i, _p]),
     "attn_decode_varlen": (_i, [_p, _p, _p, _p, _p, _p, _i, _i, _i, _i, _i, _f, _i, _p, _sz,
                                 _p]),
     "attn_decode_paged": (_i, [_p, _p, _p, _p, _p, _p, _p, _i, _i, _i, _i, _i, _i, _i, _f, _i,

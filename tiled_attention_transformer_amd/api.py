@@ -20,7 +20,7 @@ ATTN_OK = 0
 STATUS_NAMES = {
     0: "ATTN_OK", 1: "ATTN_ERR_NULLPTR", 2: "ATTN_ERR_SHAPE", 3: "ATTN_ERR_UNSUPPORTED_D",
     4: "ATTN_ERR_GQA_RATIO", 5: "ATTN_ERR_ALIGNMENT", 6: "ATTN_ERR_WORKSPACE",
-    7: "ATTN_ERR_SEQLENS", 8: "ATTN_ERR_HIP", 9: "ATTN_ERR_SCALE",
+    7: "ATTN_ERR_SEQLENS", 8: "ATTN_ERR_HIP", 9: "ATTN_ERR_SCALE", 10: "ATTN_ERR_SCRATCH_LIMIT",
 }
 
 
@@ -201,6 +201,33 @@ def attn_decode(q, k_cache, v_cache, o=None, lse=None, scale=None, num_splits=0,
     """
     return _decode(q, k_cache, v_cache, None, o, lse, scale, num_splits, workspace, want_lse,
                    stream)
+
+
+def attn_decode_noalloc(q, k_cache, v_cache, o=None, lse=None, scale=None, num_splits=0,
+                        want_lse=True, stream=None):
+    """:func:`attn_decode` through the entry point that allocates nothing (its
+    split partials live in the library's fixed device scratch); returns
+    ``(o, lse)``.  Outputs are allocated here only if not given."""
+    _need(q, "q", torch.bfloat16, 3)
+    _need(k_cache, "k_cache", torch.bfloat16, 4)
+    _need(v_cache, "v_cache", torch.bfloat16, 4)
+    B, Hq, d = q.shape
+    Skv, Hkv = k_cache.shape[1], k_cache.shape[2]
+    if tuple(v_cache.shape) != tuple(k_cache.shape) or k_cache.shape[0] != B or \
+            k_cache.shape[3] != d:
+        raise ValueError("shape mismatch")
+    if o is None:
+        o = torch.empty_like(q)
+    _need(o, "o", torch.bfloat16, 3)
+    if lse is None and want_lse:
+        lse = torch.empty((B, Hq), dtype=torch.float32, device=q.device)
+    if lse is not None:
+        _need(lse, "lse", torch.float32, 2)
+    st = _lib.load().attn_decode_noalloc(_ptr(q), _ptr(k_cache), _ptr(v_cache), _ptr(o), _ptr(lse),
+                                         B, Hq, Hkv, Skv, d, _scale(scale, d), int(num_splits),
+                                         _stream(stream))
+    _check(st, "attn_decode_noalloc")
+    return o, lse
 
 
 def attn_decode_varlen(q, k_cache, v_cache, seqlens_k, o=None, lse=None, scale=None,

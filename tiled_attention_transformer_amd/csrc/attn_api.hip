@@ -3,8 +3,16 @@
 #include <math.h>
 #include <stdint.h>
 
+#include <mutex>
+
 #include "../../include/attn.h"
 #include "kernels.h"
+
+// Split partials of attn_decode_noalloc: a fixed array in device memory (one
+// copy per GPU), so that entry point allocates nothing.  Host code never
+// passes `scratch` itself (on the host the name is only a stand-in): the
+// device address comes from hipGetSymbolAddress, once per device.
+static __device__ __align__(256) unsigned char scratch[ATTN_NOALLOC_SCRATCH_BYTES];
 
 namespace {
 
@@ -106,6 +114,7 @@ const char *attn_status_string(attn_status_t s) {
         case ATTN_ERR_SEQLENS: return "malformed cumulative sequence offsets";
         case ATTN_ERR_HIP: return "HIP runtime error at launch";
         case ATTN_ERR_SCALE: return "scale must be finite and > 0";
+        case ATTN_ERR_SCRATCH_LIMIT: return "the split partials need more than the fixed scratch of attn_decode_noalloc";
     }
     return "unknown status";
 }
@@ -260,11 +269,11 @@ struct Fp8Cache {
     float k_scale, v_scale;
 };
 
-attn_status_t decode_impl(const void *q, const void *k_cache, const void *v_cache, void *o,
-                          float *lse, const int *seqlens, int B, int Hq, int Hkv, int Skv, int d,
-                          float scale, int num_splits, void *workspace, size_t workspace_bytes,
-                          hipStream_t stream, const PagedCache *paged = nullptr,
-                          const Fp8Cache *fp8 = nullptr) {
+// The argument checks of every decode entry point, in their fixed order
+// (everything but the workspace).
+attn_status_t decode_args_status(const void *q, const void *k_cache, const void *v_cache,
+                                 const void *o, const float *lse, int B, int Hq, int Hkv, int Skv,
+                                 int d, float scale, int num_splits, const Fp8Cache *fp8) {
     if (!q || !k_cache || !v_cache || !o) return ATTN_ERR_NULLPTR;
     if (!decode_sizes_ok(B, Hq, Hkv, Skv, d)) return ATTN_ERR_SHAPE;
     if (!d_ok(d)) return ATTN_ERR_UNSUPPORTED_D;
@@ -277,6 +286,17 @@ attn_status_t decode_impl(const void *q, const void *k_cache, const void *v_cach
     if (!aligned(q, 16) || !aligned(k_cache, 16) || !aligned(v_cache, 16) || !aligned(o, 16) ||
         (lse && !aligned(lse, 4)))
         return ATTN_ERR_ALIGNMENT;
+    return ATTN_OK;
+}
+
+attn_status_t decode_impl(const void *q, const void *k_cache, const void *v_cache, void *o,
+                          float *lse, const int *seqlens, int B, int Hq, int Hkv, int Skv, int d,
+                          float scale, int num_splits, void *workspace, size_t workspace_bytes,
+                          hipStream_t stream, const PagedCache *paged = nullptr,
+                          const Fp8Cache *fp8 = nullptr) {
+    const attn_status_t st = decode_args_status(q, k_cache, v_cache, o, lse, B, Hq, Hkv, Skv, d,
+                                                scale, num_splits, fp8);
+    if (st != ATTN_OK) return st;
     const DecodeShape sh = decode_shape(B, Hq, Hkv, Skv, num_splits);
     const size_t need = decode_ws_bytes(B, Hq, d, sh.nsplit);
     if (need > 0) {
@@ -330,6 +350,36 @@ attn_status_t attn_decode(const void *q, const void *k_cache, const void *v_cach
                           hipStream_t stream) {
     return decode_impl(q, k_cache, v_cache, o, lse, nullptr, B, Hq, Hkv, Skv, d, scale,
                        num_splits, workspace, workspace_bytes, stream);
+}
+
+attn_status_t attn_decode_noalloc(const void *q, const void *k_cache, const void *v_cache,
+                                  void *o, float *lse, int B, int Hq, int Hkv, int Skv, int d,
+                                  float scale, int num_splits, hipStream_t stream) {
+    const attn_status_t st = decode_args_status(q, k_cache, v_cache, o, lse, B, Hq, Hkv, Skv, d,
+                                                scale, num_splits, nullptr);
+    if (st != ATTN_OK) return st;
+    // the partials must fit the fixed scratch
+    const size_t need = decode_ws_bytes(B, Hq, d, decode_shape(B, Hq, Hkv, Skv, num_splits).nsplit);
+    if (need > ATTN_NOALLOC_SCRATCH_BYTES) return ATTN_ERR_SCRATCH_LIMIT;
+    void *ws = nullptr;
+    if (need > 0) {
+        // the device address of this GPU's copy of `scratch`, looked up on
+        // the first call on the device (with it current) and kept
+        static std::mutex mu;
+        static void *addr[64] = {};
+        int dev = 0;
+        if (hipGetDevice(&dev) != hipSuccess || dev < 0 || dev >= 64) return ATTN_ERR_HIP;
+        std::lock_guard<std::mutex> lock(mu);
+        if (addr[dev] == nullptr) {
+            void *p = nullptr;
+            if (hipGetSymbolAddress(&p, HIP_SYMBOL(scratch)) != hipSuccess || p == nullptr)
+                return ATTN_ERR_HIP;
+            addr[dev] = p;
+        }
+        ws = addr[dev];
+    }
+    return decode_impl(q, k_cache, v_cache, o, lse, nullptr, B, Hq, Hkv, Skv, d, scale,
+                       num_splits, ws, ws ? (size_t)ATTN_NOALLOC_SCRATCH_BYTES : 0, stream);
 }
 
 attn_status_t attn_decode_varlen(const void *q, const void *k_cache, const void *v_cache,
