@@ -31,6 +31,14 @@ def _run(cmd, verbose):
         print(out, flush=True)
 
 
+# Host-only C++ (the ABI's argument checks): built with the host compiler,
+# so the same file also builds under the host sanitizers in the tests.
+HOST_SOURCES = ["host_checks.cpp"]
+CXX = os.environ.get("CXX", "g++")
+HOST_FLAGS = ["-O2", "-std=c++17", "-fPIC", "-Wall", "-D__HIP_PLATFORM_AMD__",
+              "-I/opt/rocm/include"]
+
+
 def build(verbose: bool = False, extra_flags=()) -> str:
     """Compile every kernel source and link ``libattn.so``; returns its path."""
     os.makedirs(BUILD, exist_ok=True)
@@ -40,6 +48,10 @@ def build(verbose: bool = False, extra_flags=()) -> str:
         obj = os.path.join(BUILD, src.replace(".hip", ".o"))
         objs.append(obj)
         cmds.append([HIPCC, *FLAGS, *extra_flags, "-c", os.path.join(CSRC, src), "-o", obj])
+    for src in HOST_SOURCES:
+        obj = os.path.join(BUILD, src.replace(".cpp", ".o"))
+        objs.append(obj)
+        cmds.append([CXX, *HOST_FLAGS, "-c", os.path.join(CSRC, src), "-o", obj])
     with ThreadPoolExecutor(max_workers=len(cmds)) as ex:
         list(ex.map(lambda c: _run(c, verbose), cmds))
     tmp = LIB + ".tmp"

@@ -72,6 +72,8 @@
 //    are known only on the device, and the hardware dispatcher balances them
 //    (unless every sequence is at most 512 tokens: items of one or two tiles
 //    keep a static walk balanced, and the persistent grid is used).
+#include <type_traits>
+
 #include "kernels.h"
 #include "tile_common.h"
 
@@ -712,6 +714,468 @@ void attn_fwd_kernel(FwdParams p) {
     wait_vmcnt<0>();                 // no load may outlive the workgroup
 }
 
+// Ping-pong prefill (8 waves, fixed or ragged batches, no key split).
+//
+// The waves form two groups of four, waves 0-3 and 4-7; a SIMD holds one
+// wave of each.  Every key tile takes each wave through two phases, one
+// workgroup barrier after each:
+//  * an MFMA phase M(n): the scores of stream tile n+1 (S^T = K Q^T) and
+//    O += P_n V_n, with the operand reads of each group of MFMAs issued one
+//    group ahead;
+//  * a softmax phase S(n+1): mask, row max, exponentials and the weights
+//    P_{n+1} (bf16), on the vector ALUs only.
+// Group B runs one phase behind group A, so on every SIMD one wave's
+// exponentials run while the other wave's MFMAs run: the matrix products of
+// one tile hide the softmax of another (lecompute.fr, "FlashAttention-4 :
+// limites du calcul matriciel", section "Faire avancer plusieurs tuiles sans
+// écraser leurs données", where two tiles alternate between the units).
+//
+// Tile loads go out and complete inside the softmax phases (details at the
+// walk below), so the operand reads of the MFMA phases never run beside
+// loads into LDS.
+template <int D, bool CAUSAL, bool VARLEN, int NS_, bool POISON>
+__global__ __launch_bounds__(512) __attribute__((amdgpu_waves_per_eu(2, 2)))
+void attn_fwd_pp_kernel(FwdParams p) {
+    static_assert(NS_ >= 3 && NS_ <= 4, "the schedule needs tiles n, n+1 and a free stage");
+    constexpr int NW = 8;
+    constexpr int BR = 32 * NW;
+    using L = FwdLay<D, NW>;
+    __shared__ __attribute__((aligned(16))) __bf16 lds[NS_ * L::STAGE];
+
+    const int tid = threadIdx.x;
+    const int lane = tid & 63;
+    const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
+    const bool grp_b = wave >= 4;
+    // the item's 32-row blocks alternate between the groups, so both groups
+    // meet the causal diagonal alike
+    const int rblk = grp_b ? 2 * (wave - 4) + 1 : 2 * wave;
+    const int g = lane >> 5;
+    const int col = lane & 31;
+    const int64_t hd_q = (int64_t)p.Hq * D;
+    const int64_t hd_k = (int64_t)p.Hkv * D;
+
+    auto item = [&](int r) { return fwd_item<CAUSAL, VARLEN, false, BR>(p, fwd_item_at(p, r)); };
+    auto next_tiled = [&](int r) -> int {
+        for (int s = r + 1;; ++s) {
+            const int it = fwd_item_at(p, s);
+            if (it < 0) return -1;
+            if (fwd_item<CAUSAL, VARLEN, false, BR>(p, it).nt > 0) return s;
+        }
+    };
+
+    // ---- the load stream (as in attn_fwd_kernel): every tile of every item
+    // of this workgroup, tile n into stage n % NS_
+    auto load_index = [&](int pp, bool &isv) -> int {
+        if (pp < L::KW) { isv = false; return wave + NW * pp; }
+        if (pp < L::KW + L::VW) { isv = true; return wave + NW * (pp - L::KW); }
+        if (wave < L::KR) { isv = false; return NW * L::KW + wave; }
+        isv = true;
+        if (wave < L::KR + L::VR) return NW * L::VW + wave - L::KR;
+        return wave + NW * (L::VW - 1);
+    };
+    uint32_t goff[L::PER_WAVE];
+    int ldo[L::PER_WAVE];
+#pragma unroll
+    for (int pp = 0; pp < L::PER_WAVE; ++pp) {
+        bool isv;
+        const int n = load_index(pp, isv);
+        const int slot = 64 * n + lane;
+        const int row = isv ? slot / L::VS : slot / L::KS;
+        const int colx = min(slot - row * (isv ? L::VS : L::KS), L::DS - 1) * 8;
+        goff[pp] = (uint32_t)(row * hd_k + colx) * 2u;
+        ldo[pp] = (isv ? L::K_ELEMS : 0) + 512 * n;
+    }
+    const bool last_is_v = wave >= L::KR;
+    int l_r = -1, l_tiles = 0, l_keys = 0, l_stage = 0;
+    int64_t l_off = 0;
+    auto load_item = [&](int r) {
+        l_r = r;
+        if (r >= 0) {
+            const FwdItem x = item(r);
+            l_tiles = x.nt;
+            l_keys = x.Skv;
+            l_off = x.krow0 * hd_k + (int64_t)(x.h / p.group) * D;
+        }
+    };
+    // The next tile of the stream: issue_begin() advances the stream and
+    // makes the tile's descriptors, issue_part(pp) issues this wave's load
+    // pp of it (PER_WAVE loads per tile); issue_next() does both at once.
+    __amdgpu_buffer_rsrc_t t_kr, t_vr;
+    __bf16 *t_dst = lds;
+    // (issue_begin touches no memory, so it may run before the barrier
+    // that frees the stage; issue_part only after it)
+    auto issue_begin = [&]() {
+        t_dst = lds + l_stage;
+        const __bf16 *kb = p.k, *vb = p.v;
+        int nbytes = 0;
+        if (l_r >= 0) {
+            const int rows = min(BC, l_keys);
+            nbytes = (int)(((int64_t)(rows - 1) * hd_k + D) * 2);
+            kb = p.k + l_off;
+            vb = p.v + l_off;
+            l_off += BC * hd_k;
+            l_keys -= BC;
+            if (--l_tiles == 0) load_item(next_tiled(l_r));
+        }
+        t_kr = buffer_rsrc(kb, nbytes);
+        t_vr = buffer_rsrc(vb, nbytes);
+        l_stage = l_stage == (NS_ - 1) * L::STAGE ? 0 : l_stage + L::STAGE;
+    };
+    auto issue_part = [&](int pp) {
+        if constexpr (POISON) {
+            if (pp == 0) {
+                // debug: fill what this wave's loads are about to overwrite
+                // with NaN first, so a read of a stage before its loads land
+                // (or after it was handed back to the loads) gives NaN
+                // instead of old data
+                const u32x4 nan4 = {0x7FC07FC0u, 0x7FC07FC0u, 0x7FC07FC0u, 0x7FC07FC0u};
+#pragma unroll
+                for (int q = 0; q < L::PER_WAVE; ++q) st_lds16(t_dst + ldo[q] + 8 * lane, nan4);
+                wait_lgkmcnt0();
+            }
+        }
+        const bool isv = pp == L::PER_WAVE - 1 ? last_is_v : pp >= L::KW;
+        buffer_lds_dma16(isv ? t_vr : t_kr, goff[pp], t_dst + ldo[pp]);
+    };
+    auto issue_next = [&]() {
+        issue_begin();
+#pragma unroll
+        for (int pp = 0; pp < L::PER_WAVE; ++pp) issue_part(pp);
+    };
+
+    // ---- query rows (B operand of S^T = K Q^T): qf for the item whose
+    // scores the MFMA phases compute, qn loaded ahead for the next item.  qf
+    // is only ever written by a register copy from qn, so no MFMA phase
+    // waits for a load
+    bf16x8 qf[D / 16], qn[D / 16];
+    auto load_q = [&](const FwdItem &x, bf16x8 (&q)[D / 16]) {
+        const int wr0 = x.q0 + 32 * rblk;
+        const int rows = min(32, x.Sq - wr0);
+        const __bf16 *qb = p.q + (x.qrow0 + wr0) * hd_q + (int64_t)x.h * D;
+        const int nbytes = rows > 0 ? (int)(((int64_t)(rows - 1) * hd_q + D) * 2) : 0;
+        const __amdgpu_buffer_rsrc_t rq = buffer_rsrc(rows > 0 ? qb : p.q, nbytes);
+        const uint32_t off0 = (uint32_t)((col * hd_q + 8 * g) * 2);
+#pragma unroll
+        for (int t = 0; t < D / 16; ++t)
+            q[t] = __builtin_bit_cast(bf16x8, __builtin_amdgcn_raw_buffer_load_b128(rq, off0 + 32 * t, 0, 0));
+    };
+
+    auto lane_base = [&](int n, int lane_off) -> int {
+        int o = (n % NS_) * L::STAGE + lane_off;
+        asm volatile("" : "+v"(o));
+        return o;
+    };
+    const int k_lane = col * L::KP + 8 * g;
+    const int tr_e = (lane & 15) >> 2, tr_s = lane & 3, tr_dh = (lane >> 4) & 1;
+    const int v_lane = L::K_ELEMS + (4 * g + tr_e) * L::VP + 16 * tr_dh + 4 * tr_s;
+
+    f32x16 oacc[D / 32];
+    f32x16 s[BC / 32];               // scores of the tile whose softmax comes next
+    bf16x8 pk[BC / 16];              // weights of the tile whose P V comes next
+    float m = -__builtin_inff(), lsum = 0.f;
+    const float c = p.c;
+
+    // ---- per-wave view of the item of tile n (the one being softmaxed and
+    // then multiplied with V) and of the item of tile n+1
+    struct View {
+        int r;                // item position in this workgroup's walk (-1: none)
+        int nt, ntw;          // its key tiles, and those this wave computes
+        int Skv, off, wrow0, qr;
+    };
+    auto wave_tiles = [&](const FwdItem &x) -> int {
+        const int w0 = x.q0 + 32 * rblk;
+        if (w0 >= x.Sq || x.nt == 0) return 0;
+        int wk = x.Skv;
+        if (CAUSAL) wk = min(x.Skv, min(w0 + 32, x.Sq) + (x.Skv - x.Sq));
+        return wk > 0 ? min(x.nt, (wk + BC - 1) / BC) : 0;
+    };
+    auto make_view = [&](int r) {
+        View v;
+        v.r = r;
+        v.nt = v.ntw = v.Skv = v.off = v.wrow0 = v.qr = 0;
+        if (r >= 0) {
+            const FwdItem x = item(r);
+            v.nt = x.nt;
+            v.ntw = wave_tiles(x);
+            v.Skv = x.Skv;
+            v.off = x.Skv - x.Sq;
+            v.wrow0 = x.q0 + 32 * rblk;
+            v.qr = v.wrow0 + col;
+        }
+        return v;
+    };
+
+    // items after position r0 and before r1 (-1: to the end) with rows but
+    // no keys: O = 0, LSE = -inf
+    bool stores = false;
+    auto write_rows = [&](const FwdItem &x, bool zero) {
+        const int wr0 = x.q0 + 32 * rblk;
+        if (wr0 >= x.Sq) return;
+        const int rows = min(32, x.Sq - wr0);
+        const float lt = zero ? 0.f : half_swap_sum(lsum);
+        const float inv = lt > 0.f ? 1.f / lt : 0.f;
+        const __bf16 *ob = p.o + (x.qrow0 + wr0) * hd_q + (int64_t)x.h * D;
+        const __amdgpu_buffer_rsrc_t ro = buffer_rsrc(ob, (int)(((int64_t)(rows - 1) * hd_q + D) * 2));
+        const uint32_t oo = (uint32_t)((col * hd_q + 8 * g) * 2);
+#pragma unroll
+        for (int db = 0; db < D / 32; ++db)
+#pragma unroll
+            for (int k = 0; k < 2; ++k) {
+                const f32x16 &a = oacc[db];
+                const int r = 8 * k;
+                const bf16x4 lo = zero ? bf16x4{} :
+                    to_bf16x4(a[r] * inv, a[r + 1] * inv, a[r + 2] * inv, a[r + 3] * inv);
+                const bf16x4 hi = zero ? bf16x4{} :
+                    to_bf16x4(a[r + 4] * inv, a[r + 5] * inv, a[r + 6] * inv, a[r + 7] * inv);
+                const u32x2 ul = __builtin_bit_cast(u32x2, lo), uh = __builtin_bit_cast(u32x2, hi);
+                const auto s0 = __builtin_amdgcn_permlane32_swap(ul[0], uh[0], false, false);
+                const auto s1 = __builtin_amdgcn_permlane32_swap(ul[1], uh[1], false, false);
+                const u32x4 v = {(uint32_t)s0[0], (uint32_t)s1[0], (uint32_t)s0[1], (uint32_t)s1[1]};
+                __builtin_amdgcn_raw_buffer_store_b128(v, ro, oo + (32 * db + 16 * k) * 2, 0, 0);
+            }
+        if (p.lse != nullptr) {
+            int64_t l0;
+            if constexpr (VARLEN) l0 = (int64_t)x.h * p.total_q + x.qrow0 + wr0;
+            else l0 = ((int64_t)x.b * p.Hq + x.h) * x.Sq + wr0;
+            const __amdgpu_buffer_rsrc_t rl = buffer_rsrc(p.lse + l0, rows * 4);
+            const float v = lt > 0.f ? (m + fast_log2(lt)) * kLn2 : -__builtin_inff();
+            __builtin_amdgcn_raw_buffer_store_b32(__builtin_bit_cast(uint32_t, v), rl,
+                                                  g == 0 ? (uint32_t)(col * 4) : 0x80000000u, 0, 0);
+        }
+        stores = true;
+    };
+    auto write_empty = [&](int r0, int r1) {
+        for (int r = r0 + 1; r1 < 0 || r < r1; ++r) {
+            const int it = fwd_item_at(p, r);
+            if (it < 0) break;
+            const FwdItem x = fwd_item<CAUSAL, VARLEN, false, BR>(p, it);
+            if (x.q0 < x.Sq && x.nt == 0) write_rows(x, true);
+        }
+    };
+
+    // The MFMA phase as one fixed sequence of 2*NOPS operations, score and
+    // P V MFMAs alternating; every operand fragment is read RING operations
+    // ahead into a ring of fragment registers, so each read has RING-1 MFMAs
+    // of time to land.  Score op i: key block i % 2, d-slice i / 2 (the same
+    // accumulation order as a plain loop over d); P V op i: key slice
+    // i / (D / 32), output block i % (D / 32).
+    constexpr int NSOP = 2 * (D / 16);           // score MFMAs (two key blocks)
+    constexpr int NPOP = (BC / 16) * (D / 32);   // P V MFMAs
+    static_assert(NSOP == NPOP, "score and P V MFMAs alternate one for one");
+    constexpr int NOPS = NSOP;
+    constexpr int RING = 8;
+    // the tile loads of a softmax phase: one every LD_EVERY exponentials
+    constexpr int LD_EVERY = 32 / L::PER_WAVE;
+    static_assert(LD_EVERY * L::PER_WAVE <= 32, "every load finds its exponential");
+    auto mphase_t = [&](auto ds, auto dpv, int n) {
+        constexpr bool DS = decltype(ds)::value, DPV = decltype(dpv)::value;
+        __builtin_amdgcn_s_setprio(1);
+        const __bf16 *ks = lds + lane_base(n + 1, k_lane);
+        const __bf16 *vs = lds + lane_base(n, v_lane);
+        // operation o of the sequence: o even -> score op o/2, odd -> P V op o/2
+        auto valid = [&](int o) { return (o & 1) ? DPV : DS; };
+        bf16x8 fr[RING];
+        auto read = [&](int o) {
+            const int i = o >> 1;
+            if (o & 1) {
+                const int kk = i / (D / 32), db = i % (D / 32);
+                fr[o % RING] = concat_tr(lds_read_tr(vs + 16 * kk * L::VP + 32 * db),
+                                         lds_read_tr(vs + (16 * kk + 8) * L::VP + 32 * db));
+            } else {
+                const int kb = i & 1, t = i >> 1;
+                fr[o % RING] = ld_lds_bf16x8(ks + 32 * kb * L::KP + 16 * t);
+            }
+        };
+        if constexpr (DS) {
+#pragma unroll
+            for (int kb = 0; kb < 2; ++kb) s[kb] = f32x16{};
+        }
+#pragma unroll
+        for (int o = 0; o < RING; ++o)
+            if (valid(o)) read(o);
+#pragma unroll
+        for (int o = 0; o < 2 * NOPS; ++o) {
+            __builtin_amdgcn_sched_barrier(0);
+            const int i = o >> 1;
+            if (valid(o)) {
+                if (o & 1) {
+                    const int kk = i / (D / 32), db = i % (D / 32);
+                    oacc[db] = mfma32x32x16(fr[o % RING], pk[kk], oacc[db]);
+                } else {
+                    const int kb = i & 1, t = i >> 1;
+                    s[kb] = mfma32x32x16(fr[o % RING], qf[t], s[kb]);
+                }
+            }
+            if (o + RING < 2 * NOPS && valid(o + RING)) read(o + RING);
+        }
+        __builtin_amdgcn_sched_barrier(0);
+        __builtin_amdgcn_s_setprio(0);
+    };
+    typedef std::integral_constant<bool, true> T_;
+    typedef std::integral_constant<bool, false> F_;
+
+    // ---- the softmax phase of tile n (item-local index j of view v)
+    auto sphase = [&](const View &v, int j, auto &&between) {
+        const int key0 = j * BC;
+        if (key0 + BC > v.Skv || (CAUSAL && key0 + BC - 1 > v.wrow0 + v.off)) {
+            int lim = v.Skv - 1;
+            if (CAUSAL) lim = min(lim, v.qr + v.off);
+            lim -= key0 + 4 * g;
+            asm volatile("" : "+v"(lim));
+            const float ninf = -__builtin_inff();
+#pragma unroll
+            for (int kb = 0; kb < 2; ++kb)
+#pragma unroll
+                for (int r = 0; r < 16; ++r) {
+                    float x = s[kb][r];
+                    asm volatile("v_cmp_gt_i32_e32 vcc, %2, %1\n\tv_cndmask_b32_e32 %0, %0, %3, vcc"
+                                 : "+v"(x)
+                                 : "v"(lim), "i"(32 * kb + 8 * (r >> 2) + (r & 3)), "v"(ninf)
+                                 : "vcc");
+                    s[kb][r] = x;
+                }
+        }
+        float mx = -__builtin_inff();
+#pragma unroll
+        for (int kb = 0; kb < 2; ++kb)
+#pragma unroll
+            for (int r = 0; r < 16; ++r) mx = fmaxf(mx, s[kb][r]);
+        const float mt = half_swap_max(mx) * c;
+        const bool raise = mt > m + kRescaleSlack;
+        if (__builtin_amdgcn_ballot_w64(raise)) {
+            const float m_new = raise ? mt : m;
+            const float alpha = m_new == -__builtin_inff() ? 1.f : fast_exp2(m - m_new);
+            lsum *= alpha;
+#pragma unroll
+            for (int db = 0; db < D / 32; ++db)
+#pragma unroll
+                for (int r = 0; r < 16; ++r) oacc[db][r] *= alpha;
+            m = m_new;
+        }
+        const float m_use = m == -__builtin_inff() ? 0.f : m;
+        float rs = 0.f;
+#pragma unroll
+        for (int f = 0; f < 32; ++f) {
+            const int kb = f >> 4, r = f & 15;
+            between(f);
+            s[kb][r] = fast_exp2(__builtin_fmaf(s[kb][r], c, -m_use));
+            rs += s[kb][r];
+        }
+#pragma unroll
+        for (int kk = 0; kk < BC / 16; ++kk) pk[kk] = pack_p8(s[kk >> 1], 8 * (kk & 1));
+        lsum += rs;
+    };
+
+    // ---- walk.  Every wave runs the same sequence S(n), M(n) over the
+    // stream's tiles n, with a barrier after each; group B starts one
+    // barrier late (it idles through A's first MFMA phase) and group A ends
+    // one barrier late.  cur is the item of tile n, nx the next one with key
+    // tiles.
+    //
+    // Tile loads: every wave issues its share of the next tile of the stream
+    // during each softmax phase, spread between the exponentials (issued
+    // together, the loads of four waves queue at the address units), and
+    // waits for the previous softmax phase's loads at its end.  Group A's
+    // S(m) issues tile m+NS_-2 and group B's S(m) tile m+NS_-1 (global
+    // phases 2m-1 and 2m): each into the stage of a tile whose last reader,
+    // B's M(m-NS_+2) or M(m-1), ran in an earlier phase.  A waits for tile
+    // m+NS_-2 at the end of S(m+1) (phase 2m+1), B for tile m+NS_-1 at the
+    // end of S(m+1) (phase 2m+2); they are first read by A's M(m+NS_-3) and
+    // M(m+NS_-2), at phases 2m+2 and 2m+4 (NS_ = 4).  With NS_ = 3 the
+    // tiles are first read one phase earlier, so each softmax phase waits
+    // for its own loads.
+    // Rows: qf holds those of the item whose tiles the MFMA phases score,
+    // qn those of sq1, the next item with key tiles.  Once the scores of the
+    // former's last tile are issued, qf takes qn's rows and qn is refilled.
+    int sq1 = -1;
+    auto rows_advance = [&]() {
+#pragma unroll
+        for (int t = 0; t < D / 16; ++t) qf[t] = qn[t];
+        sq1 = sq1 >= 0 ? next_tiled(sq1) : -1;
+        if (sq1 >= 0) load_q(item(sq1), qn);
+    };
+
+    const int r0 = next_tiled(-1);
+    write_empty(-1, r0);
+    if (r0 < 0) {
+        wait_vmcnt<0>();
+        return;
+    }
+    View cur = make_view(r0);
+    View nx = make_view(next_tiled(r0));
+    sq1 = nx.r;
+    load_q(item(r0), qf);
+    if (sq1 >= 0) load_q(item(sq1), qn);
+    load_item(r0);
+    // the tiles ahead of the first softmax phase: 0 .. NS_-3 (group A) or
+    // 0 .. NS_-2 (group B), all complete before the first barrier (the
+    // first softmax phase then waits for no earlier loads)
+    const int ahead = grp_b ? NS_ - 1 : NS_ - 2;
+    for (int i = 0; i < ahead; ++i) issue_next();
+    wait_vmcnt<0>();
+    stores = false;
+#pragma unroll
+    for (int db = 0; db < D / 32; ++db) oacc[db] = f32x16{};
+    lds_barrier();
+    if (grp_b) lds_barrier();            // B idles through A's M(-1)
+    // M(-1): the scores of tile 0
+    mphase_t(T_{}, F_{}, -1);
+    if (cur.nt == 1) rows_advance();     // tile 0 was r0's last
+    lds_barrier();
+
+    int jn = 0;                          // index of tile n in cur
+    for (int n = 0;; ++n) {
+        // S(n): the weights of tile n (zero weights for a tile past this
+        // wave's rows, so the P V below adds exactly nothing), with the next
+        // tile's loads spread between its exponentials; then the loads of
+        // the previous softmax phase complete
+        issue_begin();
+        const bool same = jn + 1 < cur.nt;
+        if (jn < cur.ntw) {
+            sphase(cur, jn, [&](int f) {
+                if (f % LD_EVERY == 0 && f / LD_EVERY < L::PER_WAVE) issue_part(f / LD_EVERY);
+            });
+        } else {
+#pragma unroll
+            for (int pp = 0; pp < L::PER_WAVE; ++pp) issue_part(pp);
+#pragma unroll
+            for (int kk = 0; kk < BC / 16; ++kk) pk[kk] = bf16x8{};
+        }
+        // (a 3-stage ring has no room for a tile in flight across a phase:
+        // there the phase waits for its own loads too)
+        if (stores || NS_ == 3) wait_vmcnt<0>();
+        else wait_vmcnt<L::PER_WAVE>();
+        stores = false;
+        lds_barrier();
+        // M(n): the scores of tile n+1 and O += P_n V_n (one branch-free
+        // body: scores nobody needs are computed anyway, and a P V of zero
+        // weights adds nothing)
+        mphase_t(T_{}, T_{}, n);
+        // tile n+1, just scored, the last of its item: the next MFMA phase
+        // scores the next item's first tile
+        if (same ? jn + 2 == cur.nt : nx.nt == 1) rows_advance();
+        lds_barrier();
+        // on to tile n+1: past the end of cur, write its output (its last
+        // P V was this wave's M(n)) and enter the next item
+        if (same) {
+            ++jn;
+        } else {
+            write_rows(item(cur.r), false);
+            write_empty(cur.r, nx.r);
+            if (nx.r < 0) break;
+            cur = nx;
+            jn = 0;
+            m = -__builtin_inff();
+            lsum = 0.f;
+#pragma unroll
+            for (int db = 0; db < D / 32; ++db) oacc[db] = f32x16{};
+            nx = make_view(next_tiled(cur.r));
+        }
+    }
+    if (!grp_b) lds_barrier();           // A's barrier for B's last phase
+    wait_vmcnt<0>();                     // no load may outlive the workgroup
+}
+
 // Merge of the split-KV shares, one wave per query row: LSE = M + log(sum_s
 // exp(lse_s - M)), O = sum_s exp(lse_s - LSE) O_s (the decode merge, per row).
 template <int D>
@@ -785,8 +1249,21 @@ hipError_t launch_t(const FwdParams &p_in, hipStream_t s) {
         }
         if (cus > 0 && grid > cus) grid = cus;
     }
-    hipLaunchKernelGGL((attn_fwd_kernel<D, CAUSAL, VARLEN, SPLIT, NW>), dim3((unsigned)grid),
-                       dim3(64 * NW), 0, s, p);
+    if constexpr (NW == 8 && !SPLIT) {
+        // debug builds of the fixed-batch path (see the C ABI's ATTN_DEBUG):
+        // NaN-poisoned stages, or the shallowest ring the pipeline allows
+        if (!VARLEN && (p.debug & 4))
+            hipLaunchKernelGGL((attn_fwd_pp_kernel<D, CAUSAL, false, 3, false>),
+                               dim3((unsigned)grid), dim3(64 * NW), 0, s, p);
+        else if (!VARLEN && (p.debug & 2))
+            hipLaunchKernelGGL((attn_fwd_pp_kernel<D, CAUSAL, false, NS, true>),
+                               dim3((unsigned)grid), dim3(64 * NW), 0, s, p);
+        else
+            hipLaunchKernelGGL((attn_fwd_pp_kernel<D, CAUSAL, VARLEN, NS, false>),
+                               dim3((unsigned)grid), dim3(64 * NW), 0, s, p);
+    } else
+        hipLaunchKernelGGL((attn_fwd_kernel<D, CAUSAL, VARLEN, SPLIT, NW>), dim3((unsigned)grid),
+                           dim3(64 * NW), 0, s, p);
     hipError_t e = hipGetLastError();
     if (!SPLIT || e != hipSuccess) return e;
     const int64_t rows = (int64_t)p.nbatch * p.Hq * p.Sq;

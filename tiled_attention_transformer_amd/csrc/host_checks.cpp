@@ -1,0 +1,194 @@
+// Host-side argument checks and sizing of the C ABI (see host_checks.h).
+// Plain C++: built into libattn.so, and on its own under the host
+// sanitizers by the tests.
+#include "host_checks.h"
+
+#include <math.h>
+
+#include "tile_config.h"
+
+namespace attn {
+namespace host {
+
+bool aligned(const void *p, uintptr_t a) { return ((uintptr_t)p & (a - 1)) == 0; }
+
+bool d_ok(int d) { return d == 64 || d == 128; }
+
+bool scale_ok(float s) { return isfinite(s) && s > 0.f; }
+
+// a / b rounded up, for a >= 0 and b >= 1 (no intermediate a + b - 1,
+// which overflows for a near INT_MAX)
+int ceil_div(int a, int b) { return a / b + (a % b != 0); }
+
+int pick_splits(int B, int Hq, int Hkv, int Skv) {
+    // About one work item per compute unit (an MI355X has 256), but chunks of
+    // at least 512 keys.  Measured on the decode kernels: more, shorter
+    // chunks spend their time in per-item setup and in the merge of the
+    // partials, fewer leave compute units idle.
+    const int ncb = ceil_div(Hq / Hkv, kDecCols);
+    const int64_t base = (int64_t)B * Hkv * ncb;
+    int64_t s = (256 + base - 1) / base;
+    const int max_by_len = ceil_div(Skv, 512);
+    if (s > max_by_len) s = max_by_len;
+    if (s < 1) s = 1;
+    return (int)s;
+}
+
+DecodeShape decode_shape(int B, int Hq, int Hkv, int Skv, int num_splits) {
+    DecodeShape sh;
+    sh.nsplit = num_splits > 0 ? num_splits : pick_splits(B, Hq, Hkv, Skv);
+    // chunks start on 32-key boundaries, so a kernel tile (32 keys, read as
+    // two 16-key halves) never straddles a 16-key boundary -- in a paged
+    // cache, never a page boundary; trailing chunks may be empty
+    sh.chunk = ceil_div(ceil_div(Skv, sh.nsplit), 32) * 32;
+    sh.ncb = ceil_div(Hq / Hkv, kDecCols);
+    return sh;
+}
+
+size_t decode_ws_bytes(int B, int Hq, int d, int nsplit) {
+    if (nsplit <= 1) return 0;
+    const size_t o_bytes = (size_t)nsplit * B * Hq * d * sizeof(float);
+    const size_t l_bytes = (size_t)nsplit * B * Hq * sizeof(float);
+    return o_bytes + l_bytes;
+}
+
+bool decode_sizes_ok(int B, int Hq, int Hkv, int Skv, int d) {
+    // Skv leaves room for the chunk rounding to 32 keys in an int
+    return B >= 1 && Hq >= 1 && Hkv >= 1 && Skv >= 1 && d >= 1 && Skv <= 0x7fffffff - 64 &&
+           (int64_t)B * Skv * Hkv * d <= kMaxElems && (int64_t)B * Hq * d <= kMaxElems;
+}
+
+attn_status_t decode_args_status(const void *q, const void *k_cache, const void *v_cache,
+                                 const void *o, const float *lse, int B, int Hq, int Hkv, int Skv,
+                                 int d, float scale, int num_splits, const Fp8Scales *fp8) {
+    if (!q || !k_cache || !v_cache || !o) return ATTN_ERR_NULLPTR;
+    if (!decode_sizes_ok(B, Hq, Hkv, Skv, d)) return ATTN_ERR_SHAPE;
+    if (!d_ok(d)) return ATTN_ERR_UNSUPPORTED_D;
+    if (Hq % Hkv) return ATTN_ERR_GQA_RATIO;
+    if (!scale_ok(scale)) return ATTN_ERR_SCALE;
+    if (fp8 && (!scale_ok(fp8->k_scale) || !scale_ok(fp8->v_scale) ||
+                !scale_ok(scale * fp8->k_scale)))
+        return ATTN_ERR_SCALE;
+    if (num_splits > 65536) return ATTN_ERR_SHAPE;
+    if (!aligned(q, 16) || !aligned(k_cache, 16) || !aligned(v_cache, 16) || !aligned(o, 16) ||
+        (lse && !aligned(lse, 4)))
+        return ATTN_ERR_ALIGNMENT;
+    const DecodeShape sh = decode_shape(B, Hq, Hkv, Skv, num_splits);
+    if ((int64_t)B * Hkv * sh.ncb * sh.nsplit > 0x7fffffff) return ATTN_ERR_SHAPE;
+    return ATTN_OK;
+}
+
+attn_status_t workspace_status(const void *workspace, size_t workspace_bytes, size_t need) {
+    if (need == 0) return ATTN_OK;
+    if (!workspace || workspace_bytes < need) return ATTN_ERR_WORKSPACE;
+    if (!aligned(workspace, 16)) return ATTN_ERR_ALIGNMENT;
+    return ATTN_OK;
+}
+
+// Split-KV prefill: about one work item per compute unit (an MI355X has
+// 256), but shares that average at least 1024 keys: the shares' partial
+// outputs cost a write and a read of fp32 rows, which only pays when each
+// share still streams many key tiles.  Measured (d = 128): a 512-token chunk
+// against 8192 keys splits 4 ways (2.3x faster), 256 tokens against 16384
+// keys 8 ways (4.4x), a causal 4096-token prefill with 8 heads 2 ways
+// (1.4x); a 1024-token prefill with 32 heads is faster unsplit, causal or
+// not.
+int fwd_pick_splits(int B, int Hq, int Sq, int Skv, bool causal) {
+    const int64_t base = (int64_t)B * Hq * ceil_div(Sq, kFwdBr);
+    int64_t s = (256 + base - 1) / base;
+    // keys a query row sees on average (bottom-right causal alignment)
+    int64_t avg = Skv;
+    if (causal) avg = Sq <= Skv ? Skv - Sq / 2 : (int64_t)Skv * Skv / (2 * (int64_t)Sq);
+    const int64_t cap = avg / 1024;
+    if (s > cap) s = cap;
+    return s < 1 ? 1 : (int)s;
+}
+
+size_t fwd_ws_bytes(int B, int Hq, int Sq, int d, int nsplit) {
+    if (nsplit <= 1) return 0;
+    return (size_t)nsplit * B * Hq * Sq * (d + 1) * sizeof(float);
+}
+
+attn_status_t fwd_args_status(const void *q, const void *k, const void *v, const void *o,
+                              const float *lse, int B, int Hq, int Hkv, int Sq, int Skv, int d,
+                              float scale, int *ntiles) {
+    if (!q || !k || !v || !o) return ATTN_ERR_NULLPTR;
+    if (B < 1 || Hq < 1 || Hkv < 1 || Sq < 1 || Skv < 1 || d < 1) return ATTN_ERR_SHAPE;
+    if ((int64_t)B * Sq * Hq * d > kMaxElems || (int64_t)B * Skv * Hkv * d > kMaxElems)
+        return ATTN_ERR_SHAPE;
+    if (!d_ok(d)) return ATTN_ERR_UNSUPPORTED_D;
+    if (Hq % Hkv) return ATTN_ERR_GQA_RATIO;
+    if (!scale_ok(scale)) return ATTN_ERR_SCALE;
+    if (!aligned(q, 16) || !aligned(k, 16) || !aligned(v, 16) || !aligned(o, 16) ||
+        (lse && !aligned(lse, 4)))
+        return ATTN_ERR_ALIGNMENT;
+    const int nt = ceil_div(Sq, kFwdBr);
+    if ((int64_t)nt * B * Hq > 0x7fffffff) return ATTN_ERR_SHAPE;
+    *ntiles = nt;
+    return ATTN_OK;
+}
+
+attn_status_t varlen_args_status(const void *q, const void *k, const void *v, const void *o,
+                                 const float *lse, const int *cu_q, const int *cu_k, int nseq,
+                                 int total_q, int total_k, int max_seqlen_q, int max_seqlen_k,
+                                 int Hq, int Hkv, int d, float scale, int *ntiles) {
+    if (!q || !k || !v || !o || !cu_q || !cu_k) return ATTN_ERR_NULLPTR;
+    if (nseq < 1 || total_q < 1 || total_k < 1 || max_seqlen_q < 1 || max_seqlen_k < 1 ||
+        Hq < 1 || Hkv < 1 || d < 1)
+        return ATTN_ERR_SHAPE;
+    if (nseq == 0x7fffffff) return ATTN_ERR_SHAPE;   // nseq + 1 offsets must fit an int
+    if (max_seqlen_q > total_q || max_seqlen_k > total_k) return ATTN_ERR_SEQLENS;
+    if ((int64_t)total_q * Hq * d > kMaxElems || (int64_t)total_k * Hkv * d > kMaxElems)
+        return ATTN_ERR_SHAPE;
+    if (!d_ok(d)) return ATTN_ERR_UNSUPPORTED_D;
+    if (Hq % Hkv) return ATTN_ERR_GQA_RATIO;
+    if (!scale_ok(scale)) return ATTN_ERR_SCALE;
+    if (!aligned(q, 16) || !aligned(k, 16) || !aligned(v, 16) || !aligned(o, 16) ||
+        (lse && !aligned(lse, 4)) || !aligned(cu_q, 4) || !aligned(cu_k, 4))
+        return ATTN_ERR_ALIGNMENT;
+    const int nt = ceil_div(max_seqlen_q, kFwdBr);
+    if ((int64_t)nt * nseq * Hq > 0x7fffffff) return ATTN_ERR_SHAPE;
+    *ntiles = nt;
+    return ATTN_OK;
+}
+
+attn_status_t varlen_check(const int *cu, int nseq, int total, int *max_seqlen) {
+    if (!cu) return ATTN_ERR_NULLPTR;
+    if (nseq < 1 || nseq == 0x7fffffff || total < 0 || cu[0] != 0 || cu[nseq] != total)
+        return ATTN_ERR_SEQLENS;
+    int mx = 0;
+    for (int s = 0; s < nseq; ++s) {
+        if (cu[s + 1] < cu[s]) return ATTN_ERR_SEQLENS;
+        // non-decreasing from 0, so the difference cannot overflow
+        if (cu[s + 1] - cu[s] > mx) mx = cu[s + 1] - cu[s];
+    }
+    if (max_seqlen) *max_seqlen = mx;
+    return ATTN_OK;
+}
+
+attn_status_t paged_args_status(const int *block_table, const int *seqlens_k, int B, int Hkv,
+                                int d, int page_size, int max_pages_per_seq, int num_pages) {
+    if (!block_table || !seqlens_k) return ATTN_ERR_NULLPTR;
+    if (page_size < 16 || page_size % 16 || max_pages_per_seq < 1 || num_pages < 1)
+        return ATTN_ERR_SHAPE;
+    if ((int64_t)max_pages_per_seq * page_size > 0x7fffffff - 64 ||
+        (int64_t)num_pages * page_size * Hkv * d > kMaxElems ||
+        (int64_t)B * max_pages_per_seq > 0x7fffffff)
+        return ATTN_ERR_SHAPE;
+    if (!aligned(block_table, 4) || !aligned(seqlens_k, 4)) return ATTN_ERR_ALIGNMENT;
+    return ATTN_OK;
+}
+
+attn_status_t kmeans_args_status(const void *x, const void *c, const int *idx, const float *dist,
+                                 int N, int K, int d) {
+    if (!x || !c || !idx) return ATTN_ERR_NULLPTR;
+    if (N < 1 || K < 1 || (int64_t)N * d > kMaxElems || (int64_t)K * d > kMaxElems)
+        return ATTN_ERR_SHAPE;
+    if (!d_ok(d)) return ATTN_ERR_UNSUPPORTED_D;
+    if (!aligned(x, 16) || !aligned(c, 16) || !aligned(idx, 4) || (dist && !aligned(dist, 4)))
+        return ATTN_ERR_ALIGNMENT;
+    return ATTN_OK;
+}
+
+}  // namespace host
+}  // namespace attn

@@ -8,6 +8,8 @@
 
 #include <atomic>
 
+#include "tile_config.h"
+
 namespace attn {
 
 constexpr float kLn2 = 0.69314718055994530942f;
@@ -16,18 +18,6 @@ constexpr float kLog2e = 1.44269504088896340736f;
 // Slack (log2 units) before the online softmax moves its reference max:
 // weights exp2(s*c - m) stay <= 2^8, far from fp32/bf16 overflow.
 constexpr float kRescaleSlack = 8.0f;
-
-// Prefill tile shape: 8 waves x 32 query rows, 64 keys per K/V tile (the
-// host counts query tiles of kFwdBr rows; the launcher halves the tile, on
-// 4-wave workgroups, for fixed batches with fewer tiles than CUs).
-constexpr int kFwdWaves = 8;
-constexpr int kFwdBr = 32 * kFwdWaves;
-constexpr int kFwdBc = 64;
-
-// Decode: 4 waves per workgroup; one work item serves up to 32 query heads
-// of one KV head.
-constexpr int kDecThreads = 256;
-constexpr int kDecCols = 32;
 
 // Compute units of the current device.  Cached per device after the first
 // query: the attribute query costs host time on every launch otherwise,
@@ -71,6 +61,9 @@ struct FwdParams {
     // natural-log LSE to ws_o [nsplit, B, Hq, Sq, d] and ws_lse [nsplit, B, Hq, Sq]
     int nsplit;
     float *ws_o, *ws_lse;
+    // debug bits (host only, chosen at launch): 2 = NaN-poison retired LDS
+    // stages, 4 = 3-stage K/V ring (fixed-batch prefill)
+    int debug;
 };
 
 struct DecParams {
