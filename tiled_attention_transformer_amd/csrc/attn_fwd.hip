@@ -730,9 +730,8 @@ void attn_fwd_kernel(FwdParams p) {
 // limites du calcul matriciel", section "Faire avancer plusieurs tuiles sans
 // écraser leurs données", where two tiles alternate between the units).
 //
-// Tile loads go out and complete inside the softmax phases (details at the
-// walk below), so the operand reads of the MFMA phases never run beside
-// loads into LDS.
+// Tile loads go out spread over the MFMA phases, where the vector ALUs are
+// idle, and are waited for a whole step later (details at the walk below).
 template <int D, bool CAUSAL, bool VARLEN, int NS_, bool POISON>
 __global__ __launch_bounds__(512) __attribute__((amdgpu_waves_per_eu(2, 2)))
 void attn_fwd_pp_kernel(FwdParams p) {
@@ -964,11 +963,13 @@ void attn_fwd_pp_kernel(FwdParams p) {
     static_assert(NSOP == NPOP, "score and P V MFMAs alternate one for one");
     constexpr int NOPS = NSOP;
     constexpr int RING = 8;
-    // the tile loads of a softmax phase: one every LD_EVERY exponentials
-    constexpr int LD_EVERY = 32 / L::PER_WAVE;
-    static_assert(LD_EVERY * L::PER_WAVE <= 32, "every load finds its exponential");
-    auto mphase_t = [&](auto ds, auto dpv, int n) {
+    // the tile loads of an MFMA phase (ld = PER_WAVE, or 0 for none): one
+    // every LD_EVERY operations
+    constexpr int LD_EVERY = (2 * NOPS) / L::PER_WAVE;
+    static_assert(LD_EVERY >= 1, "every load finds its operation");
+    auto mphase_t = [&](auto ds, auto dpv, int n, auto ld) {
         constexpr bool DS = decltype(ds)::value, DPV = decltype(dpv)::value;
+        constexpr int NLD = decltype(ld)::value;
         __builtin_amdgcn_s_setprio(1);
         const __bf16 *ks = lds + lane_base(n + 1, k_lane);
         const __bf16 *vs = lds + lane_base(n, v_lane);
@@ -1006,6 +1007,7 @@ void attn_fwd_pp_kernel(FwdParams p) {
                     s[kb] = mfma32x32x16(fr[o % RING], qf[t], s[kb]);
                 }
             }
+            if (NLD > 0 && o % LD_EVERY == 0 && o / LD_EVERY < NLD) issue_part(o / LD_EVERY);
             if (o + RING < 2 * NOPS && valid(o + RING)) read(o + RING);
         }
         __builtin_amdgcn_sched_barrier(0);
@@ -1013,9 +1015,11 @@ void attn_fwd_pp_kernel(FwdParams p) {
     };
     typedef std::integral_constant<bool, true> T_;
     typedef std::integral_constant<bool, false> F_;
+    typedef std::integral_constant<int, 0> LD0_;
+    typedef std::integral_constant<int, L::PER_WAVE> LDW_;
 
     // ---- the softmax phase of tile n (item-local index j of view v)
-    auto sphase = [&](const View &v, int j, auto &&between) {
+    auto sphase = [&](const View &v, int j) {
         const int key0 = j * BC;
         if (key0 + BC > v.Skv || (CAUSAL && key0 + BC - 1 > v.wrow0 + v.off)) {
             int lim = v.Skv - 1;
@@ -1057,7 +1061,6 @@ void attn_fwd_pp_kernel(FwdParams p) {
 #pragma unroll
         for (int f = 0; f < 32; ++f) {
             const int kb = f >> 4, r = f & 15;
-            between(f);
             s[kb][r] = fast_exp2(__builtin_fmaf(s[kb][r], c, -m_use));
             rs += s[kb][r];
         }
@@ -1072,18 +1075,21 @@ void attn_fwd_pp_kernel(FwdParams p) {
     // one barrier late.  cur is the item of tile n, nx the next one with key
     // tiles.
     //
-    // Tile loads: every wave issues its share of the next tile of the stream
-    // during each softmax phase, spread between the exponentials (issued
-    // together, the loads of four waves queue at the address units), and
-    // waits for the previous softmax phase's loads at its end.  Group A's
-    // S(m) issues tile m+NS_-2 and group B's S(m) tile m+NS_-1 (global
-    // phases 2m-1 and 2m): each into the stage of a tile whose last reader,
-    // B's M(m-NS_+2) or M(m-1), ran in an earlier phase.  A waits for tile
-    // m+NS_-2 at the end of S(m+1) (phase 2m+1), B for tile m+NS_-1 at the
-    // end of S(m+1) (phase 2m+2); they are first read by A's M(m+NS_-3) and
-    // M(m+NS_-2), at phases 2m+2 and 2m+4 (NS_ = 4).  With NS_ = 3 the
-    // tiles are first read one phase earlier, so each softmax phase waits
-    // for its own loads.
+    // Phases: group A runs S(n) in phase 2n+1 and M(n) in phase 2n+2, group
+    // B one phase later.  Tile t is read by the MFMA phases M(t-1) (its keys)
+    // and M(t) (its values): first in phase 2t (A's M(t-1)), last in phase
+    // 2t+3 (B's M(t)).
+    // Tile loads: the first NS_-1 tiles go out before the first barrier; then
+    // every wave issues its share of tile n+NS_-1 during its M(n), spread
+    // over the MFMAs, into the stage of tile n-1, whose last reader, B's
+    // M(n-1), ran in phase 2n+1, before A's M(n) (phase 2n+2) and B's (2n+3).
+    // The descriptors are made at the end of the softmax phase before (the
+    // scalar unit is idle there).  At the end of M(n) a wave waits for all
+    // its loads but tile n+NS_-1's, i.e. for tile n+NS_-2 (issued in
+    // M(n-1)), which is first read in phase 2n+2*NS_-4: after the barrier
+    // that ends B's M(n) (phase 2n+3) when NS_ = 4.  With NS_ = 3 it is tile
+    // n+2 itself, first read in phase 2n+4, so there the wait takes every
+    // load.
     // Rows: qf holds those of the item whose tiles the MFMA phases score,
     // qn those of sq1, the next item with key tiles.  Once the scores of the
     // former's last tile are issued, qf takes qn's rows and qn is refilled.
@@ -1107,11 +1113,8 @@ void attn_fwd_pp_kernel(FwdParams p) {
     load_q(item(r0), qf);
     if (sq1 >= 0) load_q(item(sq1), qn);
     load_item(r0);
-    // the tiles ahead of the first softmax phase: 0 .. NS_-3 (group A) or
-    // 0 .. NS_-2 (group B), all complete before the first barrier (the
-    // first softmax phase then waits for no earlier loads)
-    const int ahead = grp_b ? NS_ - 1 : NS_ - 2;
-    for (int i = 0; i < ahead; ++i) issue_next();
+    // tiles 0 .. NS_-2, complete before the first barrier
+    for (int i = 0; i < NS_ - 1; ++i) issue_next();
     wait_vmcnt<0>();
     stores = false;
 #pragma unroll
@@ -1119,38 +1122,33 @@ void attn_fwd_pp_kernel(FwdParams p) {
     lds_barrier();
     if (grp_b) lds_barrier();            // B idles through A's M(-1)
     // M(-1): the scores of tile 0
-    mphase_t(T_{}, F_{}, -1);
+    mphase_t(T_{}, F_{}, -1, LD0_{});
     if (cur.nt == 1) rows_advance();     // tile 0 was r0's last
     lds_barrier();
 
     int jn = 0;                          // index of tile n in cur
     for (int n = 0;; ++n) {
         // S(n): the weights of tile n (zero weights for a tile past this
-        // wave's rows, so the P V below adds exactly nothing), with the next
-        // tile's loads spread between its exponentials; then the loads of
-        // the previous softmax phase complete
-        issue_begin();
+        // wave's rows, so the P V below adds exactly nothing); then the
+        // descriptors of tile n+NS_-1
         const bool same = jn + 1 < cur.nt;
         if (jn < cur.ntw) {
-            sphase(cur, jn, [&](int f) {
-                if (f % LD_EVERY == 0 && f / LD_EVERY < L::PER_WAVE) issue_part(f / LD_EVERY);
-            });
+            sphase(cur, jn);
         } else {
-#pragma unroll
-            for (int pp = 0; pp < L::PER_WAVE; ++pp) issue_part(pp);
 #pragma unroll
             for (int kk = 0; kk < BC / 16; ++kk) pk[kk] = bf16x8{};
         }
-        // (a 3-stage ring has no room for a tile in flight across a phase:
-        // there the phase waits for its own loads too)
-        if (stores || NS_ == 3) wait_vmcnt<0>();
-        else wait_vmcnt<L::PER_WAVE>();
-        stores = false;
+        issue_begin();
         lds_barrier();
         // M(n): the scores of tile n+1 and O += P_n V_n (one branch-free
         // body: scores nobody needs are computed anyway, and a P V of zero
-        // weights adds nothing)
-        mphase_t(T_{}, T_{}, n);
+        // weights adds nothing), with the loads of tile n+NS_-1; then tile
+        // n+NS_-2 completes (every load, after output stores, which share
+        // the counter)
+        mphase_t(T_{}, T_{}, n, LDW_{});
+        if (stores || NS_ == 3) wait_vmcnt<0>();
+        else wait_vmcnt<L::PER_WAVE>();
+        stores = false;
         // tile n+1, just scored, the last of its item: the next MFMA phase
         // scores the next item's first tile
         if (same ? jn + 2 == cur.nt : nx.nt == 1) rows_advance();
