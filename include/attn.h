@@ -36,11 +36,25 @@
  *    LSE = -inf.
  *  * lse may be NULL, in which case it is not written.
  *  * Every call is asynchronous on `stream` (0 = the null stream) and never
- *    synchronises.  Arguments are validated on the host BEFORE any launch; on
+ *    synchronises (outside debug mode 1, below).  Arguments are validated on the host BEFORE any launch; on
  *    a nonzero status nothing was launched and no output was written.  A
  *    launch failure returns ATTN_ERR_HIP (outputs then undefined).
  *  * Results are deterministic: the same inputs give bitwise the same
  *    outputs (fixed tile order, no atomics).
+ *
+ * Debug modes (environment variable ATTN_DEBUG, an integer of bit flags,
+ * read at every call; unset or 0 in production)
+ * ------------------------------------------------------------------------
+ *  * 1: every call synchronises its stream before it returns and reports a
+ *    kernel fault as ATTN_ERR_HIP, so a fault is charged to the call that
+ *    caused it.
+ *  * 2: fixed-batch prefill fills each LDS stage of the K/V ring with NaN
+ *    before its tile loads are issued, so a read of a stage before its loads
+ *    complete (or after the stage was handed back) turns the output NaN.
+ *  * 4: fixed-batch prefill runs the shallowest K/V ring its pipeline allows
+ *    (3 stages instead of 4), which leaves no slack for a missing wait.
+ *  Modes 2 and 4 (and 6, both) change no arithmetic: correct kernels give the
+ *  normal mode's outputs bit for bit, only slower.
  */
 #ifndef ATTN_H
 #define ATTN_H

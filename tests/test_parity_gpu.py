@@ -717,6 +717,105 @@ def test_varlen_cross_lengths_match_oracle(api, dev, case, causal):
         assert np.all(o[a:a + dead] == 0) and np.all(np.isneginf(lse[:, a:a + dead]))
 
 
+# Ragged batches with at least as many (sequence, head, 256-row tile) items
+# as compute units run on a persistent grid whose workgroups each list their
+# items, cost-sorted, in LDS; up to 256 sequences and 1024 query tiles,
+# beyond that in the launcher's own order.
+def _compact_rows(rng, lq, Hq, heads=(0,), per_item=1):
+    """Every row of the given heads, and per_item random rows of every
+    (sequence, head, 256-row tile)."""
+    rows = []
+    for s, L in enumerate(lq):
+        for h in heads:
+            rows.extend((s, h, i) for i in range(L))
+        for h in range(Hq):
+            for t0 in range(0, L, 256):
+                for _ in range(per_item):
+                    rows.append((s, h, int(rng.integers(t0, min(L, t0 + 256)))))
+    return np.array(rows, dtype=np.int64)
+
+
+def test_varlen_listed_schedule_equals_separate_calls_bitwise(api, dev):
+    """A ragged batch on the listed schedule (7 sequences x 32 heads x up to 8
+    query tiles) gives bit for bit what one call per sequence gives."""
+    import torch
+    lengths = [1, 130, 7, 2000, 128, 513, 300]
+    data = si.make_varlen(31, len(lengths), 1, 2000, H=32, d=128, Hkv=8, lengths=lengths)
+    cu = data["cu_seqlens"]
+    q, k, v = (to_dev(data[x], dev) for x in "qkv")
+    cu_d = torch.from_numpy(cu).to(dev)
+    for causal in (False, True):
+        print("listed schedule vs separate calls, causal=%d" % causal, flush=True)
+        o, lse = api.attn_fwd_varlen(q, k, v, cu_d, cu_d, max(lengths), max(lengths),
+                                     scale=0.09, causal=causal)
+        torch.cuda.synchronize()
+        o, lse = bf16_to_np(o), f32_to_np(lse)
+        for s, L in enumerate(lengths):
+            a, b = cu[s], cu[s + 1]
+            sub = {x: data[x][a:b][None] for x in "qkv"}
+            os_, ls_ = run_fwd(api, dev, sub, 0.09, causal)
+            assert np.array_equal(o[a:b], os_[0]) and np.array_equal(lse[:, a:b], ls_[0]), s
+
+
+@pytest.mark.parametrize("causal", [False, True], ids=["full", "causal"])
+def test_varlen_listed_schedule_cross_lengths(api, dev, causal):
+    """The listed schedule with query and key lengths that differ (either may
+    be 0, empty sequences included): sampled rows against the oracle; rows
+    with no keys exactly O = 0, LSE = -inf; outputs start as NaN."""
+    import torch
+    rng = np.random.default_rng(77)
+    n = 40
+    lq = [int(x) for x in rng.integers(0, 700, n)]
+    lk = [int(x) for x in rng.integers(0, 900, n)]
+    lq[3], lk[5], lq[7], lk[7] = 0, 0, 0, 0
+    lk[9] = lq[9] // 3                       # more queries than keys
+    Hq, Hkv, d = 16, 4, 128
+    data = si.make_varlen_cross(78, lq, lk, H=Hq, d=d, Hkv=Hkv)
+    cq, ck = data["cu_seqlens_q"], data["cu_seqlens_k"]
+    q, k, v = (to_dev(data[x], dev) for x in "qkv")
+    o, lse = nan_outputs(dev, q.shape, (Hq, q.shape[0]))
+    print("listed schedule cross lengths causal=%d" % causal, flush=True)
+    api.attn_fwd_varlen(q, k, v, torch.from_numpy(cq).to(dev), torch.from_numpy(ck).to(dev),
+                        max(lq), max(lk), o=o, lse=lse, scale=si.default_scale(d), causal=causal)
+    torch.cuda.synchronize()
+    o, lse = bf16_to_np(o), f32_to_np(lse)
+    assert not np.isnan(o).any() and not np.isnan(lse).any(), "rows left unwritten"
+    rows = _compact_rows(rng, lq, Hq, heads=(0, Hq - 1), per_item=2)
+    o_ref, lse_ref = cpu.varlen_rows(data["q"], data["k"], data["v"], cq, ck,
+                                     si.default_scale(d), causal, rows)
+    tok = cq[rows[:, 0]] + rows[:, 2]
+    assert_close(o[tok, rows[:, 1]], o_ref, lse[rows[:, 1], tok], lse_ref, "listed cross")
+    for s in range(n):
+        dead = lq[s] if lk[s] == 0 else (max(0, lq[s] - lk[s]) if causal else 0)
+        a = cq[s]
+        assert np.all(o[a:a + dead] == 0) and np.all(np.isneginf(lse[:, a:a + dead])), s
+
+
+def test_varlen_more_sequences_than_the_list_holds(api, dev):
+    """300 sequences (past the listed schedule's 256): the launcher's order on
+    a persistent grid; sampled rows of every item against the oracle."""
+    import torch
+    rng = np.random.default_rng(79)
+    lengths = [int(x) for x in rng.integers(1, 400, 300)]
+    Hq, d = 4, 64
+    data = si.make_varlen(80, len(lengths), 1, 400, H=Hq, d=d, Hkv=2, lengths=lengths)
+    cu = data["cu_seqlens"]
+    q, k, v = (to_dev(data[x], dev) for x in "qkv")
+    o, lse = nan_outputs(dev, q.shape, (Hq, q.shape[0]))
+    print("300 sequences, causal", flush=True)
+    api.attn_fwd_varlen(q, k, v, torch.from_numpy(cu).to(dev), torch.from_numpy(cu).to(dev),
+                        max(lengths), max(lengths), o=o, lse=lse, scale=si.default_scale(d),
+                        causal=True)
+    torch.cuda.synchronize()
+    o, lse = bf16_to_np(o), f32_to_np(lse)
+    assert np.all(np.isfinite(o)) and np.all(np.isfinite(lse)), "rows left unwritten"
+    rows = _compact_rows(rng, lengths, Hq, heads=(1,), per_item=1)
+    o_ref, lse_ref = cpu.varlen_rows(data["q"], data["k"], data["v"], cu, cu,
+                                     si.default_scale(d), True, rows)
+    gi = cu[rows[:, 0]] + rows[:, 2]
+    assert_close(o[gi, rows[:, 1]], o_ref, lse[rows[:, 1], gi], lse_ref, "300 sequences")
+
+
 def test_lse_optional(api, dev):
     import torch
     data = si.make_prefill(19, 1, 2, 2, 200, 200, 64)

@@ -122,8 +122,10 @@ struct FwdItem {
     int64_t qrow0, krow0;   // first query / key row of the sequence
 };
 
+// (cu_l: for a ragged batch, an LDS copy of the offsets, cu_seqlens_q at
+// cu_l[0 .. nseq] and cu_seqlens_k at cu_l[kSchedSeqs + 1 ..], else null)
 template <bool CAUSAL, bool VARLEN, bool SPLIT, int BR>
-__device__ __forceinline__ FwdItem fwd_item(const FwdParams &p, int it) {
+__device__ __forceinline__ FwdItem fwd_item(const FwdParams &p, int it, const int *cu_l = nullptr) {
     FwdItem x;
     const int BH = p.nbatch * p.Hq;
     const int rs = it / BH;
@@ -138,9 +140,19 @@ __device__ __forceinline__ FwdItem fwd_item(const FwdParams &p, int it) {
         // constant address space, so they are scalar loads into SGPRs (and
         // take no part in the vector-load counter the tile waits rely on)
         typedef const __attribute__((address_space(4))) int cint;
-        cint *cq = (cint *)p.cu_q, *ck = (cint *)p.cu_k;
-        const int qs = cq[x.b], qe = cq[x.b + 1];
-        const int ks = ck[x.b], ke = ck[x.b + 1];
+        int qs, qe, ks, ke;
+        if (cu_l != nullptr) {
+            qs = __builtin_amdgcn_readfirstlane(cu_l[x.b]);
+            qe = __builtin_amdgcn_readfirstlane(cu_l[x.b + 1]);
+            ks = __builtin_amdgcn_readfirstlane(cu_l[kSchedSeqs + 1 + x.b]);
+            ke = __builtin_amdgcn_readfirstlane(cu_l[kSchedSeqs + 2 + x.b]);
+        } else {
+            cint *cq = (cint *)p.cu_q, *ck = (cint *)p.cu_k;
+            qs = cq[x.b];
+            qe = cq[x.b + 1];
+            ks = ck[x.b];
+            ke = ck[x.b + 1];
+        }
         const bool ok = qs >= 0 && qe >= qs && qe <= p.total_q && ks >= 0 && ke >= ks &&
                         ke <= p.total_k;
         x.Sq = ok ? qe - qs : 0;
@@ -169,19 +181,111 @@ __device__ __forceinline__ FwdItem fwd_item(const FwdParams &p, int it) {
     return x;
 }
 
-// The r-th item of this workgroup, or -1: its items are one per row of
-// gridDim.x items (boustrophedon: position w in even rows, the mirror
-// position, in steps of 8 so the item's head stays on this XCD, in odd
-// rows), taken from the last row to the first.
-__device__ __forceinline__ int fwd_item_at(const FwdParams &p, int r) {
+// The r-th of this workgroup's positions in a sequence of N items, or -1:
+// one per row of gridDim.x positions (boustrophedon: position w in even rows,
+// the mirror position, in steps of 8 so the item's head stays on this XCD,
+// in odd rows), taken from the last row to the first.  fwd_walk_len is the
+// number of them.
+__device__ __forceinline__ int fwd_walk_len(int N) {
     const int G = gridDim.x, w = blockIdx.x;
     const int mirror = (G % 8 == 0) ? (G / 8 - 1 - w / 8) * 8 + (w % 8) : G - 1 - w;
-    const int R = (p.nitems + G - 1) / G;                  // rows of G items
-    const bool last_ok = (int64_t)(R - 1) * G + (((R - 1) & 1) ? mirror : w) < p.nitems;
-    const int nv = last_ok ? R : R - 1;                   // rows holding an item of w
+    const int R = (N + G - 1) / G;                        // rows of G positions
+    const bool last_ok = (int64_t)(R - 1) * G + (((R - 1) & 1) ? mirror : w) < N;
+    return last_ok ? R : R - 1;                           // rows holding a position of w
+}
+__device__ __forceinline__ int fwd_walk_pos(int N, int r) {
+    const int G = gridDim.x, w = blockIdx.x;
+    const int mirror = (G % 8 == 0) ? (G / 8 - 1 - w / 8) * 8 + (w % 8) : G - 1 - w;
+    const int nv = fwd_walk_len(N);
     if (r >= nv) return -1;
     const int row = nv - 1 - r;                           // the rows in reverse order
     return row * G + ((row & 1) ? mirror : w);
+}
+// The r-th item of this workgroup in the launcher's item order, or -1.
+__device__ __forceinline__ int fwd_item_at(const FwdParams &p, int r) {
+    return fwd_walk_pos(p.nitems, r);
+}
+
+// Ragged batch: this workgroup's items, in the order of its walk, listed in
+// LDS (sm: kSchedSeqs + kSchedSeqs + kSchedLevels + kSchedItems ints; on
+// return the kSchedLevels ints at sm + 2 * kSchedSeqs hold the offsets as
+// fwd_item's cu_l).  The
+// items with rows, (sequence, head, query tile j), are put in one order of
+// falling cost: by j from the highest down (the causal key range of a tile
+// ends at its last row, and only long sequences have high tiles), within
+// one j the sequences with more query tiles first (ties by index), then the
+// heads.  The positions of that order are dealt out as by fwd_walk_pos, so
+// the persistent workgroups get nearly equal work however the lengths mix
+// (the launcher's own order holds a slot for every tile of the longest
+// sequence in every sequence).  Returns the number of items listed, or -1
+// when they do not fit (then the launcher's order applies).  Every thread
+// of the workgroup takes part; the list is complete on return.
+template <bool CAUSAL, int BR>
+__device__ int fwd_sched_build(const FwdParams &p, int *sm) {
+    int *s_t = sm, *s_perm = sm + kSchedSeqs, *s_lev = sm + 2 * kSchedSeqs;
+    int *s_list = s_lev + kSchedLevels;
+    const int tid = threadIdx.x, nth = blockDim.x;
+    const int nseq = p.nbatch, nlev = p.ntiles, H = p.Hq;
+    // query tiles of each sequence (bad offsets: none, as fwd_item has it)
+    for (int b = tid; b < nseq; b += nth) {
+        const int qs = p.cu_q[b], qe = p.cu_q[b + 1], ks = p.cu_k[b], ke = p.cu_k[b + 1];
+        const bool ok = qs >= 0 && qe >= qs && qe <= p.total_q && ks >= 0 && ke >= ks &&
+                        ke <= p.total_k;
+        s_t[b] = ok ? min((qe - qs + BR - 1) / BR, nlev) : 0;
+    }
+    __syncthreads();
+    // the sequences by falling tile count (a rank sort), and per level j the
+    // items of the levels above it, H * sum_b max(0, T_b - j - 1)
+    for (int b = tid; b < nseq; b += nth) {
+        const int t = s_t[b];
+        int rank = 0;
+        for (int c = 0; c < nseq; ++c) rank += (s_t[c] > t || (s_t[c] == t && c < b)) ? 1 : 0;
+        s_perm[rank] = b;
+    }
+    for (int j = tid; j < nlev; j += nth) {
+        int above = 0;
+        for (int c = 0; c < nseq; ++c) above += max(0, s_t[c] - j - 1);
+        s_lev[j] = above * H;
+    }
+    // N = H * sum_b T_b, summed by every wave alike
+    int tiles = 0;
+    for (int b = (int)(threadIdx.x & 63); b < nseq; b += 64) tiles += s_t[b];
+#pragma unroll
+    for (int sh = 32; sh >= 1; sh >>= 1) tiles += __shfl_xor(tiles, sh, 64);
+    const int N = __builtin_amdgcn_readfirstlane(tiles) * H;
+    const int cnt = fwd_walk_len(N);
+    __syncthreads();
+    // (one decision for every workgroup: the longest list, one per row)
+    if ((N + (int)gridDim.x - 1) / (int)gridDim.x > kSchedItems) return -1;
+    for (int r = tid; r < cnt; r += nth) {
+        const int q = fwd_walk_pos(N, r);
+        // level of position q: the lowest j with s_lev[j] <= q (s_lev falls
+        // with j; s_lev[nlev - 1] = 0)
+        int lo = 0, hi = nlev - 1;
+        while (lo < hi) {
+            const int mid = (lo + hi) >> 1;
+            if (s_lev[mid] <= q) hi = mid;
+            else lo = mid + 1;
+        }
+        const int i = q - s_lev[lo];
+        const int k = i / H, h = i - k * H;
+        // the launcher's item id, as fwd_item decodes it: rank, then
+        // (sequence, head), where the rank is the query tile (from the last,
+        // under the causal mask)
+        const int rank = CAUSAL ? nlev - 1 - lo : lo;
+        s_list[r] = rank * (nseq * H) + s_perm[k] * H + h;
+    }
+    __syncthreads();
+    // the level table is done with: it now keeps a copy of the offsets for
+    // the walk's item lookups (LDS reads instead of chains of scalar loads
+    // at every item change), in the layout fwd_item takes
+    static_assert(kSchedLevels >= 2 * (kSchedSeqs + 1), "room for both offset arrays");
+    for (int b = tid; b <= nseq; b += nth) {
+        s_lev[b] = p.cu_q[b];
+        s_lev[kSchedSeqs + 1 + b] = p.cu_k[b];
+    }
+    __syncthreads();
+    return cnt;
 }
 
 template <int D, bool CAUSAL, bool VARLEN, bool SPLIT, int NW>
@@ -739,12 +843,32 @@ void attn_fwd_pp_kernel(FwdParams p) {
     constexpr int NW = 8;
     constexpr int BR = 32 * NW;
     using L = FwdLay<D, NW>;
-    __shared__ __attribute__((aligned(16))) __bf16 lds[NS_ * L::STAGE];
+    // the K/V ring, then (ragged batches) the item list: one LDS object, so
+    // the compiler keeps no alias scopes that would make it wait for every
+    // tile load before the next LDS read (the walk orders those itself)
+    constexpr int SCHED_INTS = VARLEN ? 2 * kSchedSeqs + kSchedLevels + kSchedItems : 0;
+    __shared__ __attribute__((aligned(16))) __bf16 lds[NS_ * L::STAGE + 2 * SCHED_INTS];
+    int *const sched = reinterpret_cast<int *>(lds + NS_ * L::STAGE);
 
     const int tid = threadIdx.x;
     const int lane = tid & 63;
     const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
     const bool grp_b = wave >= 4;
+    // the r-th item of this workgroup: from its LDS list (a ragged batch on
+    // a persistent grid), else in the launcher's order
+    int n_listed = -1;
+    if constexpr (VARLEN) {
+        if (p.compact) n_listed = fwd_sched_build<CAUSAL, BR>(p, sched);
+    }
+    const int *const listed = sched + 2 * kSchedSeqs + kSchedLevels;
+    const int *const cu_l = VARLEN && n_listed >= 0 ? sched + 2 * kSchedSeqs : nullptr;
+    auto at = [&](int r) -> int {
+        if constexpr (VARLEN) {
+            if (n_listed >= 0) return r < n_listed ? listed[r] : -1;
+        }
+        return fwd_item_at(p, r);
+    };
+    auto item_of = [&](int it) { return fwd_item<CAUSAL, VARLEN, false, BR>(p, it, cu_l); };
     // the item's 32-row blocks alternate between the groups, so both groups
     // meet the causal diagonal alike
     const int rblk = grp_b ? 2 * (wave - 4) + 1 : 2 * wave;
@@ -753,12 +877,12 @@ void attn_fwd_pp_kernel(FwdParams p) {
     const int64_t hd_q = (int64_t)p.Hq * D;
     const int64_t hd_k = (int64_t)p.Hkv * D;
 
-    auto item = [&](int r) { return fwd_item<CAUSAL, VARLEN, false, BR>(p, fwd_item_at(p, r)); };
+    auto item = [&](int r) { return item_of(at(r)); };
     auto next_tiled = [&](int r) -> int {
         for (int s = r + 1;; ++s) {
-            const int it = fwd_item_at(p, s);
+            const int it = at(s);
             if (it < 0) return -1;
-            if (fwd_item<CAUSAL, VARLEN, false, BR>(p, it).nt > 0) return s;
+            if (item_of(it).nt > 0) return s;
         }
     };
 
@@ -906,7 +1030,6 @@ void attn_fwd_pp_kernel(FwdParams p) {
 
     // items after position r0 and before r1 (-1: to the end) with rows but
     // no keys: O = 0, LSE = -inf
-    bool stores = false;
     auto write_rows = [&](const FwdItem &x, bool zero) {
         const int wr0 = x.q0 + 32 * rblk;
         if (wr0 >= x.Sq) return;
@@ -941,13 +1064,12 @@ void attn_fwd_pp_kernel(FwdParams p) {
             __builtin_amdgcn_raw_buffer_store_b32(__builtin_bit_cast(uint32_t, v), rl,
                                                   g == 0 ? (uint32_t)(col * 4) : 0x80000000u, 0, 0);
         }
-        stores = true;
     };
     auto write_empty = [&](int r0, int r1) {
         for (int r = r0 + 1; r1 < 0 || r < r1; ++r) {
-            const int it = fwd_item_at(p, r);
+            const int it = at(r);
             if (it < 0) break;
-            const FwdItem x = fwd_item<CAUSAL, VARLEN, false, BR>(p, it);
+            const FwdItem x = item_of(it);
             if (x.q0 < x.Sq && x.nt == 0) write_rows(x, true);
         }
     };
@@ -1116,7 +1238,6 @@ void attn_fwd_pp_kernel(FwdParams p) {
     // tiles 0 .. NS_-2, complete before the first barrier
     for (int i = 0; i < NS_ - 1; ++i) issue_next();
     wait_vmcnt<0>();
-    stores = false;
 #pragma unroll
     for (int db = 0; db < D / 32; ++db) oacc[db] = f32x16{};
     lds_barrier();
@@ -1143,12 +1264,13 @@ void attn_fwd_pp_kernel(FwdParams p) {
         // M(n): the scores of tile n+1 and O += P_n V_n (one branch-free
         // body: scores nobody needs are computed anyway, and a P V of zero
         // weights adds nothing), with the loads of tile n+NS_-1; then tile
-        // n+NS_-2 completes (every load, after output stores, which share
-        // the counter)
+        // n+NS_-2 completes.  Loads complete in the order they were issued,
+        // so at most PER_WAVE outstanding operations means every load but
+        // the last PER_WAVE done; output stores in between share the
+        // counter, but only ever add to it.
         mphase_t(T_{}, T_{}, n, LDW_{});
-        if (stores || NS_ == 3) wait_vmcnt<0>();
+        if (NS_ == 3) wait_vmcnt<0>();
         else wait_vmcnt<L::PER_WAVE>();
-        stores = false;
         // tile n+1, just scored, the last of its item: the next MFMA phase
         // scores the next item's first tile
         if (same ? jn + 2 == cur.nt : nx.nt == 1) rows_advance();
@@ -1228,10 +1350,18 @@ hipError_t launch_t(const FwdParams &p_in, hipStream_t s) {
         const hipError_t e = current_cu_count(&cus);
         if (e != hipSuccess) return e;
         if (cus > 0 && items < cus) return launch_t<D, CAUSAL, VARLEN, SPLIT, 4>(p_in, s);
+        // a persistent grid, one workgroup per CU, whose load stream runs
+        // across items instead of a workgroup per item: over a cost-sorted
+        // list of the items with rows where it fits the LDS bounds, else for
         // short sequences only (at most two tiles per item, so a static walk
-        // stays balanced): a persistent grid, one workgroup per CU, whose
-        // load stream runs across items instead of a workgroup per item
-        if (cus > 0 && p.max_len <= 512) grid = cus;
+        // over the launcher's order stays balanced)
+        if (cus > 0 && p.nbatch <= kSchedSeqs && p.ntiles <= kSchedLevels &&
+            items <= (int64_t)kSchedItems * cus) {
+            grid = cus;
+            p.compact = 1;
+        } else if (cus > 0 && p.max_len <= 512) {
+            grid = cus;
+        }
     }
     if constexpr (!VARLEN) {
         // one workgroup per CU (the LDS ring allows no more), each walking
@@ -1249,8 +1379,12 @@ hipError_t launch_t(const FwdParams &p_in, hipStream_t s) {
     }
     if constexpr (NW == 8 && !SPLIT) {
         // debug builds of the fixed-batch path (see the C ABI's ATTN_DEBUG):
-        // NaN-poisoned stages, or the shallowest ring the pipeline allows
-        if (!VARLEN && (p.debug & 4))
+        // NaN-poisoned stages, the shallowest ring the pipeline allows, or
+        // both
+        if (!VARLEN && (p.debug & 6) == 6)
+            hipLaunchKernelGGL((attn_fwd_pp_kernel<D, CAUSAL, false, 3, true>),
+                               dim3((unsigned)grid), dim3(64 * NW), 0, s, p);
+        else if (!VARLEN && (p.debug & 4))
             hipLaunchKernelGGL((attn_fwd_pp_kernel<D, CAUSAL, false, 3, false>),
                                dim3((unsigned)grid), dim3(64 * NW), 0, s, p);
         else if (!VARLEN && (p.debug & 2))

@@ -5,6 +5,8 @@
 
 #include <math.h>
 
+#include <initializer_list>
+
 #include "tile_config.h"
 
 namespace attn {
@@ -19,6 +21,22 @@ bool scale_ok(float s) { return isfinite(s) && s > 0.f; }
 // a / b rounded up, for a >= 0 and b >= 1 (no intermediate a + b - 1,
 // which overflows for a near INT_MAX)
 int ceil_div(int a, int b) { return a / b + (a % b != 0); }
+
+// Whether the product of non-negative factors is at most lim (lim >= 0),
+// without forming any product above lim: four int factors near INT_MAX
+// would overflow even int64.
+bool prod_le(int64_t lim, std::initializer_list<int64_t> factors) {
+    for (const int64_t f : factors)
+        if (f < 0) return false;
+    for (const int64_t f : factors)
+        if (f == 0) return true;
+    int64_t acc = 1;
+    for (const int64_t f : factors) {
+        if (acc > lim / f) return false;
+        acc *= f;
+    }
+    return true;
+}
 
 int pick_splits(int B, int Hq, int Hkv, int Skv) {
     // About one work item per compute unit (an MI355X has 256), but chunks of
@@ -55,7 +73,7 @@ size_t decode_ws_bytes(int B, int Hq, int d, int nsplit) {
 bool decode_sizes_ok(int B, int Hq, int Hkv, int Skv, int d) {
     // Skv leaves room for the chunk rounding to 32 keys in an int
     return B >= 1 && Hq >= 1 && Hkv >= 1 && Skv >= 1 && d >= 1 && Skv <= 0x7fffffff - 64 &&
-           (int64_t)B * Skv * Hkv * d <= kMaxElems && (int64_t)B * Hq * d <= kMaxElems;
+           prod_le(kMaxElems, {B, Skv, Hkv, d}) && prod_le(kMaxElems, {B, Hq, d});
 }
 
 attn_status_t decode_args_status(const void *q, const void *k_cache, const void *v_cache,
@@ -74,7 +92,7 @@ attn_status_t decode_args_status(const void *q, const void *k_cache, const void 
         (lse && !aligned(lse, 4)))
         return ATTN_ERR_ALIGNMENT;
     const DecodeShape sh = decode_shape(B, Hq, Hkv, Skv, num_splits);
-    if ((int64_t)B * Hkv * sh.ncb * sh.nsplit > 0x7fffffff) return ATTN_ERR_SHAPE;
+    if (!prod_le(0x7fffffff, {B, Hkv, sh.ncb, sh.nsplit})) return ATTN_ERR_SHAPE;
     return ATTN_OK;
 }
 
@@ -114,7 +132,7 @@ attn_status_t fwd_args_status(const void *q, const void *k, const void *v, const
                               float scale, int *ntiles) {
     if (!q || !k || !v || !o) return ATTN_ERR_NULLPTR;
     if (B < 1 || Hq < 1 || Hkv < 1 || Sq < 1 || Skv < 1 || d < 1) return ATTN_ERR_SHAPE;
-    if ((int64_t)B * Sq * Hq * d > kMaxElems || (int64_t)B * Skv * Hkv * d > kMaxElems)
+    if (!prod_le(kMaxElems, {B, Sq, Hq, d}) || !prod_le(kMaxElems, {B, Skv, Hkv, d}))
         return ATTN_ERR_SHAPE;
     if (!d_ok(d)) return ATTN_ERR_UNSUPPORTED_D;
     if (Hq % Hkv) return ATTN_ERR_GQA_RATIO;
@@ -123,7 +141,7 @@ attn_status_t fwd_args_status(const void *q, const void *k, const void *v, const
         (lse && !aligned(lse, 4)))
         return ATTN_ERR_ALIGNMENT;
     const int nt = ceil_div(Sq, kFwdBr);
-    if ((int64_t)nt * B * Hq > 0x7fffffff) return ATTN_ERR_SHAPE;
+    if (!prod_le(0x7fffffff, {nt, B, Hq})) return ATTN_ERR_SHAPE;
     *ntiles = nt;
     return ATTN_OK;
 }
@@ -138,7 +156,7 @@ attn_status_t varlen_args_status(const void *q, const void *k, const void *v, co
         return ATTN_ERR_SHAPE;
     if (nseq == 0x7fffffff) return ATTN_ERR_SHAPE;   // nseq + 1 offsets must fit an int
     if (max_seqlen_q > total_q || max_seqlen_k > total_k) return ATTN_ERR_SEQLENS;
-    if ((int64_t)total_q * Hq * d > kMaxElems || (int64_t)total_k * Hkv * d > kMaxElems)
+    if (!prod_le(kMaxElems, {total_q, Hq, d}) || !prod_le(kMaxElems, {total_k, Hkv, d}))
         return ATTN_ERR_SHAPE;
     if (!d_ok(d)) return ATTN_ERR_UNSUPPORTED_D;
     if (Hq % Hkv) return ATTN_ERR_GQA_RATIO;
@@ -147,7 +165,7 @@ attn_status_t varlen_args_status(const void *q, const void *k, const void *v, co
         (lse && !aligned(lse, 4)) || !aligned(cu_q, 4) || !aligned(cu_k, 4))
         return ATTN_ERR_ALIGNMENT;
     const int nt = ceil_div(max_seqlen_q, kFwdBr);
-    if ((int64_t)nt * nseq * Hq > 0x7fffffff) return ATTN_ERR_SHAPE;
+    if (!prod_le(0x7fffffff, {nt, nseq, Hq})) return ATTN_ERR_SHAPE;
     *ntiles = nt;
     return ATTN_OK;
 }
@@ -171,9 +189,9 @@ attn_status_t paged_args_status(const int *block_table, const int *seqlens_k, in
     if (!block_table || !seqlens_k) return ATTN_ERR_NULLPTR;
     if (page_size < 16 || page_size % 16 || max_pages_per_seq < 1 || num_pages < 1)
         return ATTN_ERR_SHAPE;
-    if ((int64_t)max_pages_per_seq * page_size > 0x7fffffff - 64 ||
-        (int64_t)num_pages * page_size * Hkv * d > kMaxElems ||
-        (int64_t)B * max_pages_per_seq > 0x7fffffff)
+    if (!prod_le(0x7fffffff - 64, {max_pages_per_seq, page_size}) ||
+        !prod_le(kMaxElems, {num_pages, page_size, Hkv, d}) ||
+        !prod_le(0x7fffffff, {B, max_pages_per_seq}))
         return ATTN_ERR_SHAPE;
     if (!aligned(block_table, 4) || !aligned(seqlens_k, 4)) return ATTN_ERR_ALIGNMENT;
     return ATTN_OK;
@@ -182,7 +200,7 @@ attn_status_t paged_args_status(const int *block_table, const int *seqlens_k, in
 attn_status_t kmeans_args_status(const void *x, const void *c, const int *idx, const float *dist,
                                  int N, int K, int d) {
     if (!x || !c || !idx) return ATTN_ERR_NULLPTR;
-    if (N < 1 || K < 1 || (int64_t)N * d > kMaxElems || (int64_t)K * d > kMaxElems)
+    if (N < 1 || K < 1 || !prod_le(kMaxElems, {N, d}) || !prod_le(kMaxElems, {K, d}))
         return ATTN_ERR_SHAPE;
     if (!d_ok(d)) return ATTN_ERR_UNSUPPORTED_D;
     if (!aligned(x, 16) || !aligned(c, 16) || !aligned(idx, 4) || (dist && !aligned(dist, 4)))

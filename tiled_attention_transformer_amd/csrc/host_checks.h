@@ -6,6 +6,8 @@
 #include <stddef.h>
 #include <stdint.h>
 
+#include <initializer_list>
+
 #include "../../include/attn.h"
 
 namespace attn {
@@ -17,6 +19,8 @@ bool aligned(const void *p, uintptr_t a);
 bool d_ok(int d);
 bool scale_ok(float s);
 int ceil_div(int a, int b);
+// product of non-negative factors <= lim, decided without overflow
+bool prod_le(int64_t lim, std::initializer_list<int64_t> factors);
 
 // Decode: split count, chunk length (keys) and blocks of <= 32 query heads.
 struct DecodeShape {

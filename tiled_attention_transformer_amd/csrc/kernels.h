@@ -62,8 +62,11 @@ struct FwdParams {
     int nsplit;
     float *ws_o, *ws_lse;
     // debug bits (host only, chosen at launch): 2 = NaN-poison retired LDS
-    // stages, 4 = 3-stage K/V ring (fixed-batch prefill)
+    // stages, 4 = 3-stage K/V ring, 6 = both (fixed-batch prefill)
     int debug;
+    // ragged batch on a persistent grid with a cost-sorted item list (set by
+    // the launcher when the list fits the kSched* bounds)
+    int compact;
 };
 
 struct DecParams {

@@ -12,6 +12,14 @@ constexpr int kFwdWaves = 8;
 constexpr int kFwdBr = 32 * kFwdWaves;
 constexpr int kFwdBc = 64;
 
+// Ragged-batch prefill on a persistent grid: each workgroup lists its items
+// in LDS at start, from a cost-sorted order of every (sequence, head, query
+// tile) that has rows.  Bounds of that list: sequences, query tiles of the
+// longest sequence, and items per workgroup.
+constexpr int kSchedSeqs = 256;
+constexpr int kSchedLevels = 1024;
+constexpr int kSchedItems = 1024;
+
 // Decode: 4 waves per workgroup; one work item serves up to 32 query heads
 // of one KV head.
 constexpr int kDecThreads = 256;
