@@ -235,7 +235,7 @@ def load_counters(kind: str):
     return t["kernels"][kind]["derived"]
 
 
-EXTRAS = ("decode_auto", "fp8", "kmeans", "long", "ragged")
+EXTRAS = ("decode_auto", "fp8", "skewed", "kmeans", "long", "ragged")
 
 
 def extra_workloads(api, dev, stream, which=EXTRAS, calls=20, dec_ms=None, dec_inputs=None):
@@ -248,8 +248,9 @@ def extra_workloads(api, dev, stream, which=EXTRAS, calls=20, dec_ms=None, dec_i
     inputs); K of the long workload is scaled per head by U(0.5, 2) as in its
     test recipe; the fp8 cache holds the codes of x / (max|x| / 448) per
     tensor, as the test recipe does; the k-means points and centroids follow
-    the test recipe's mixture.  ``which`` names the lines to run (a subset of
-    EXTRAS)."""
+    the test recipe's mixture; the skewed decode has the decode workload's
+    heads with one sequence of 32768 keys among 63 of 256 (cache capacity
+    32768).  ``which`` names the lines to run (a subset of EXTRAS)."""
     import torch
     out = {}
     gen = torch.Generator(device=dev)
@@ -292,6 +293,8 @@ def extra_workloads(api, dev, stream, which=EXTRAS, calls=20, dec_ms=None, dec_i
     # decode with an fp8 KV cache (the decode workload's sizes)
     if "fp8" in which:
         fp8_decode(api, dev, stream, gen, d, timed, out, dec_ms)
+    if "skewed" in which:
+        skewed_decode(api, dev, stream, gen, d, timed, out)
     if "kmeans" in which:
         kmeans_assign(api, dev, stream, gen, d, timed, out)
     if "long" in which:
@@ -330,6 +333,39 @@ def fp8_decode(api, dev, stream, gen, d, timed, out, dec_ms):
                   "whole sequences per workgroup)",
         "speedup_vs_bf16_cache": None if dec_ms is None else round(dec_ms / ms, 3)}
     del q, codes, o, lse, ws
+
+
+def skewed_decode(api, dev, stream, gen, d, timed, out):
+    """ragged decode (per-sequence key counts on the device) with one long
+    sequence: the library's split choice, which sizes the split from the
+    cache capacity (the host never sees the lengths), against an explicit
+    16-way split"""
+    import torch
+    gen.manual_seed(6)
+    B, Hq, Hkv, cap = 64, 32, 8, 32768
+    lens = [256] * 17 + [cap] + [256] * 46
+    k, v = (torch.randn((B, cap, Hkv, d), generator=gen, device=dev, dtype=torch.float32)
+            .to(torch.bfloat16) for _ in range(2))
+    q = torch.randn((B, Hq, d), generator=gen, device=dev, dtype=torch.float32).to(torch.bfloat16)
+    sl = torch.tensor(lens, dtype=torch.int32, device=dev)
+    o = torch.empty_like(q)
+    lse = torch.empty((B, Hq), dtype=torch.float32, device=dev)
+    nb = sum(lens) * Hkv * d * 2 * 2 + 2 * B * Hq * d * 2 + B * Hq * 4
+    line = {"algorithmic_bytes": nb, "lengths": "17 x 256, 1 x 32768, 46 x 256"}
+    for ns in (0, 16):
+        ws = torch.empty(max(1, api.attn_decode_workspace_bytes(B, Hq, Hkv, cap, d, ns)),
+                         dtype=torch.uint8, device=dev)
+        ms = timed(lambda: api.attn_decode_varlen(q, k, v, sl, o=o, lse=lse, scale=d ** -0.5,
+                                                  num_splits=ns, workspace=ws, stream=stream),
+                   n=50)
+        gbs = nb / (ms * 1e-3) / 1e9
+        eff = api.attn_decode_pick_splits(B, Hq, Hkv, cap) if ns == 0 else ns
+        line["library_choice" if ns == 0 else "splits_16"] = {
+            "num_splits": eff, "ms": round(ms, 5), "GB/s": round(gbs, 1),
+            "frac_of_8000": round(gbs / PEAK_HBM_GBS, 4)}
+        del ws
+    out["decode_varlen_skewed_B64_Hq32_Hkv8_cap32768_d128"] = line
+    del k, v, q, o, lse, sl
 
 
 def kmeans_assign(api, dev, stream, gen, d, timed, out):
