@@ -74,7 +74,7 @@ def decode_bytes(B, Hq, Hkv, Skv, d, kv_elem_bytes=2):
 
 TRAFFIC_PATH = os.path.join(ROOT, "profiles", "traffic.json")
 # which kernels make up each reported path (substrings of the rocprofv3 names)
-TRAFFIC_KERNELS = {"prefill": ["attn_fwd_kernel<128, true, false, false, 8>"],
+TRAFFIC_KERNELS = {"prefill": ["attn_fwd_pp_kernel<128, true, false, 4, false>"],
                    "decode": ["attn_decode_split_kernel<128, false, true>",
                               "attn_decode_combine_kernel<128>"],
                    "decode_fp8": ["attn_decode_split_kernel<128, true, false>"],
@@ -167,7 +167,7 @@ COUNTER_PASSES = [
     ["GRBM_GUI_ACTIVE", "SQ_INSTS_VALU", "SQ_INSTS_SALU", "SQ_INSTS_LDS", "SQ_ACTIVE_INST_LDS",
      "SQ_LDS_BANK_CONFLICT", "SQ_WAIT_INST_LDS", "SQ_INSTS_VMEM", "SQ_ACTIVE_INST_ANY"],
 ]
-COUNTER_KERNELS = {"prefill": "attn_fwd_kernel<128, true, false, false, 8>",
+COUNTER_KERNELS = {"prefill": "attn_fwd_pp_kernel<128, true, false, 4, false>",
                    "decode": "attn_decode_split_kernel<128, false, true>",
                    "decode_fp8": "attn_decode_split_kernel<128, true, false>",
                    "kmeans": "kmeans_assign_kernel<128, 128>"}
@@ -473,6 +473,10 @@ def main():
                     help="print the counters of pass N (for rocprofv3 --pmc) and exit")
     ap.add_argument("--copy-calibration", action="store_true",
                     help="also run a plain 1 GiB device copy (counter calibration)")
+    ap.add_argument("--extra-only", action="store_true",
+                    help="time only the context workloads named by --extra (no headline step, "
+                         "no CPU baseline) and print them as one JSON line: for profiling one "
+                         "workload at a time")
     ap.add_argument("--write-traffic", nargs=2, metavar=("FETCH_DIR", "WRITE_DIR"),
                     help="write profiles/traffic.json from two rocprofv3 --pmc output folders "
                          "and exit (no GPU use)")
@@ -501,6 +505,13 @@ def main():
 
     dev = torch.device("cuda:0")
     api._lib.load()
+    if args.extra_only:
+        which = EXTRAS if args.extra == "all" else tuple(x for x in args.extra.split(",") if x)
+        which = tuple(x for x in which if x != "decode_auto")   # needs the headline's inputs
+        print(json.dumps({"extra": extra_workloads(api, dev, torch.cuda.current_stream(),
+                                                   which=which), "kernel_hash": kernel_hash()}),
+              flush=True)
+        return
 
     def to_dev(bits):
         return torch.from_numpy(np.ascontiguousarray(bits).view(np.int16)).view(torch.bfloat16).to(dev)
@@ -615,7 +626,7 @@ def main():
         "prefill_ms": {"mean": round(pre_avg, 5), "cold": round(cold_prefill_ms, 5)},
         "roofline": {"bound": "mfma", "achieved": round(tflops, 2), "peak": PEAK_BF16_TFLOPS,
                      "unit": "TFLOP/s", "frac": round(tflops / PEAK_BF16_TFLOPS, 4),
-                     "traffic": traffic, "kernel": "attn_fwd_kernel<128, true, false, false, 8>",
+                     "traffic": traffic, "kernel": "attn_fwd_pp_kernel<128, true, false, 4, false>",
                      "counters": load_counters("prefill")},
         "decode": {
             "value": round(gbs, 1), "unit": "GB/s",
