@@ -1377,7 +1377,11 @@ hipError_t launch_t(const FwdParams &p_in, hipStream_t s) {
         }
         if (cus > 0 && grid > cus) grid = cus;
     }
-    if constexpr (NW == 8 && !SPLIT) {
+    // the ping-pong kernel, except for fixed batches at d = 64, where a phase
+    // has half the MFMAs to hide the same barrier and descriptor work and the
+    // single-group kernel measured faster on short causal shapes (3-10 %,
+    // within 1.5 % the other way on long or non-causal ones; the same bits)
+    if constexpr (NW == 8 && !SPLIT && (D == 128 || VARLEN)) {
         // debug builds of the fixed-batch path (see the C ABI's ATTN_DEBUG):
         // NaN-poisoned stages, the shallowest ring the pipeline allows, or
         // both
