@@ -816,6 +816,52 @@ def test_varlen_more_sequences_than_the_list_holds(api, dev):
     assert_close(o[gi, rows[:, 1]], o_ref, lse[rows[:, 1], gi], lse_ref, "300 sequences")
 
 
+def _varlen_sampled(api, dev, lengths, H, Hkv, d, seed, heads, per_item, label):
+    """One causal ragged call (outputs start as NaN), every row of the given
+    heads and per_item random rows of every (sequence, head, 256-row tile)
+    against the oracle."""
+    import torch
+    rng = np.random.default_rng(seed)
+    data = si.make_varlen(seed, len(lengths), 1, max(lengths), H=H, d=d, Hkv=Hkv, lengths=lengths)
+    cu = data["cu_seqlens"]
+    q, k, v = (to_dev(data[x], dev) for x in "qkv")
+    o, lse = nan_outputs(dev, q.shape, (H, q.shape[0]))
+    print(label, flush=True)
+    api.attn_fwd_varlen(q, k, v, torch.from_numpy(cu).to(dev), torch.from_numpy(cu).to(dev),
+                        max(lengths), max(lengths), o=o, lse=lse, scale=si.default_scale(d),
+                        causal=True)
+    torch.cuda.synchronize()
+    o, lse = bf16_to_np(o), f32_to_np(lse)
+    assert np.all(np.isfinite(o)) and np.all(np.isfinite(lse)), "rows left unwritten"
+    rows = _compact_rows(rng, lengths, H, heads=heads, per_item=per_item)
+    o_ref, lse_ref = cpu.varlen_rows(data["q"], data["k"], data["v"], cu, cu,
+                                     si.default_scale(d), True, rows)
+    gi = cu[rows[:, 0]] + rows[:, 2]
+    return assert_close(o[gi, rows[:, 1]], o_ref, lse[rows[:, 1], gi], lse_ref, label)
+
+
+def test_varlen_listed_schedule_at_its_bounds(api, dev):
+    """256 sequences (the list's sequence bound), the longest 262,144 tokens
+    (1024 query tiles: the level bound) and 1 head: 262,144 item slots, the
+    launcher's bound for the list on 256 CUs (1024 per workgroup)."""
+    rng = np.random.default_rng(81)
+    lengths = [int(x) for x in rng.integers(1, 300, 256)]
+    lengths[100] = 262144
+    err = _varlen_sampled(api, dev, lengths, 1, 1, 64, 82, heads=(), per_item=1,
+                          label="listed schedule at its bounds")
+    print("max|dO| %.4g max|dLSE| %.3g" % err, flush=True)
+
+
+def test_varlen_one_workgroup_per_item(api, dev):
+    """257 sequences, some past 512 tokens: past the list's sequence bound and
+    the short-sequence rule, so one workgroup per item."""
+    rng = np.random.default_rng(83)
+    lengths = [int(x) for x in rng.integers(1, 1200, 257)]
+    err = _varlen_sampled(api, dev, lengths, 2, 1, 128, 84, heads=(1,), per_item=1,
+                          label="one workgroup per item, 257 sequences")
+    print("max|dO| %.4g max|dLSE| %.3g" % err, flush=True)
+
+
 def test_lse_optional(api, dev):
     import torch
     data = si.make_prefill(19, 1, 2, 2, 200, 200, 64)
