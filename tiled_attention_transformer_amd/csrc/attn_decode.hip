@@ -35,6 +35,10 @@
 //    reads are free of bank conflicts.  An fp8 (e4m3fn) cache stays fp8 in
 //    LDS and is widened to bf16 in registers (v_cvt_scalef32_pk_bf16_fp8,
 //    exact) right before the MFMAs; V then comes through ds_read_b64_tr_b8;
+//  * when the split items number at least four per CU, every wave is a
+//    worker of its own instead (template parameter WI): it takes whole items
+//    and writes each one's partial itself, with no merge of the waves and
+//    no barrier;
 //  * at the end of an item the four waves merge their states through LDS
 //    (log-sum-exp weights, then a fixed-order sum, so results are
 //    deterministic) and the result goes out: bf16 O and LSE when the item is

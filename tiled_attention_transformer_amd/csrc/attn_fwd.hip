@@ -8,13 +8,22 @@
 // contributions (section "Déplacer une partie des exponentielles").  The
 // page's point that the exponentials and sums, not the matrix units, become
 // the limit (section "Blackwell déplace la limite vers les autres unités") is
-// what the schedule below is built around: the softmax of one key tile runs
-// on the vector ALUs while the matrix cores already compute the scores of the
-// next tile (section "Faire avancer plusieurs tuiles sans écraser leurs
-// données" describes the same overlap with thread-group roles on SM100; here
-// one wave interleaves both streams).
+// what the schedules below are built around: the softmax of one key tile runs
+// on the vector ALUs while the matrix cores compute the scores of another
+// (section "Faire avancer plusieurs tuiles sans écraser leurs données"
+// describes the same overlap with thread-group roles on SM100).  Two kernels
+// do it two ways:
+//  * attn_fwd_pp_kernel (batches with at least one 256-row item per CU,
+//    except fixed batches at d = 64): the two waves of each SIMD belong to
+//    two wave groups that take turns, one running a tile's MFMAs while the
+//    other runs a tile's softmax, a workgroup barrier after each phase;
+//  * attn_fwd_kernel (smaller grids, the split-KV prefill, fixed batches at
+//    d = 64): each wave interleaves both streams itself.
+// Ragged batches on the persistent grid walk a cost-sorted list of their
+// items that every workgroup builds in LDS from the offsets
+// (fwd_sched_build).
 //
-// gfx950 mapping:
+// gfx950 mapping (shared by both kernels unless noted):
 //  * one work item = 256 query rows of one (batch, head); a workgroup of 8
 //    waves runs one item at a time, one workgroup per CU (two waves per
 //    SIMD); each wave owns 32 rows and keeps its Q fragment, running max/sum
@@ -45,8 +54,9 @@
 //    from the score accumulators straight into the B operand of the second
 //    product (converted to bf16) without touching LDS.  V stays row-major in
 //    LDS and is read as the A operand with ds_read_b64_tr_b16;
-//  * software pipeline inside each wave: iteration j issues the MFMAs of
-//    S_{j+1} and of P_j * V_j, interleaved with the softmax of S_j: group g
+//  * attn_fwd_kernel's software pipeline inside each wave: iteration j
+//    issues the MFMAs of S_{j+1} and of P_j * V_j, interleaved with the
+//    softmax of S_j: group g
 //    holds the score MFMAs of two d-slices, weight chunk g and the P * V
 //    MFMAs of the key slices whose weights chunk g-1 made.  Groups are split
 //    by scheduling barriers, and every LDS operand read is issued one group
@@ -68,10 +78,11 @@
 //    per-item overheads then fall where the next item's loads hide them
 //    rather than in the kernel's tail (measured ~5 % faster on the causal
 //    B4 H16 S2048 prefill than the reverse order, same HBM traffic).
-//    Ragged batches launch one workgroup per item instead: their item sizes
-//    are known only on the device, and the hardware dispatcher balances them
-//    (unless every sequence is at most 512 tokens: items of one or two tiles
-//    keep a static walk balanced, and the persistent grid is used).
+//    Ragged batches on the persistent grid use a list of their own, sorted
+//    by cost on the device (their item sizes are known only there); past
+//    that list's bounds they keep this order, persistent when every
+//    sequence is at most 512 tokens (items of one or two tiles keep a
+//    static walk balanced), else one workgroup per item.
 #include <type_traits>
 
 #include "kernels.h"
