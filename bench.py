@@ -337,9 +337,11 @@ def fp8_decode(api, dev, stream, gen, d, timed, out, dec_ms):
 
 def skewed_decode(api, dev, stream, gen, d, timed, out):
     """ragged decode (per-sequence key counts on the device) with one long
-    sequence: the library's split choice, which sizes the split from the
-    cache capacity (the host never sees the lengths), against an explicit
-    16-way split"""
+    sequence: the split by the lengths (the library's choice with a
+    workspace of attn_decode_varlen_workspace_bytes: the kernel reads the
+    lengths and gives every wave an equal run of key tiles), the split by the
+    capacity (the library's choice with the smaller workspace: the host never
+    sees the lengths) and an explicit 16-way split"""
     import torch
     gen.manual_seed(6)
     B, Hq, Hkv, cap = 64, 32, 8, 32768
@@ -352,17 +354,20 @@ def skewed_decode(api, dev, stream, gen, d, timed, out):
     lse = torch.empty((B, Hq), dtype=torch.float32, device=dev)
     nb = sum(lens) * Hkv * d * 2 * 2 + 2 * B * Hq * d * 2 + B * Hq * 4
     line = {"algorithmic_bytes": nb, "lengths": "17 x 256, 1 x 32768, 46 x 256"}
-    for ns in (0, 16):
-        ws = torch.empty(max(1, api.attn_decode_workspace_bytes(B, Hq, Hkv, cap, d, ns)),
-                         dtype=torch.uint8, device=dev)
+    runs = (("split_by_lengths", 0, api.attn_decode_varlen_workspace_bytes(B, Hq, Hkv, cap, d)),
+            ("split_by_capacity", 0, api.attn_decode_workspace_bytes(B, Hq, Hkv, cap, d, 0)),
+            ("splits_16", 16, api.attn_decode_workspace_bytes(B, Hq, Hkv, cap, d, 16)))
+    for name, ns, nbytes in runs:
+        ws = torch.empty(max(16, nbytes), dtype=torch.uint8, device=dev)
         ms = timed(lambda: api.attn_decode_varlen(q, k, v, sl, o=o, lse=lse, scale=d ** -0.5,
                                                   num_splits=ns, workspace=ws, stream=stream),
                    n=50)
         gbs = nb / (ms * 1e-3) / 1e9
-        eff = api.attn_decode_pick_splits(B, Hq, Hkv, cap) if ns == 0 else ns
-        line["library_choice" if ns == 0 else "splits_16"] = {
-            "num_splits": eff, "ms": round(ms, 5), "GB/s": round(gbs, 1),
-            "frac_of_8000": round(gbs / PEAK_HBM_GBS, 4)}
+        r = {"ms": round(ms, 5), "GB/s": round(gbs, 1), "frac_of_8000": round(gbs / PEAK_HBM_GBS, 4),
+             "workspace_bytes": nbytes}
+        if name != "split_by_lengths":
+            r["num_splits"] = api.attn_decode_pick_splits(B, Hq, Hkv, cap) if ns == 0 else ns
+        line[name] = r
         del ws
     out["decode_varlen_skewed_B64_Hq32_Hkv8_cap32768_d128"] = line
     del k, v, q, o, lse, sl

@@ -207,6 +207,21 @@ attn_status_t attn_decode(const void *q, const void *k_cache, const void *v_cach
  * no memory.  Serving keeps one KV cache per sequence, each filled to its
  * own length (lecompute.fr, "Flapping Airplanes, ThunderKittens and
  * megakernels", section "A benchmark that could test the broader promise").
+ * Split by the lengths: with num_splits <= 0 and a workspace of at least
+ * attn_decode_varlen_workspace_bytes(B, Hq, Hkv, Skv_max, d) bytes, the
+ * kernel reads the lengths, lays the 32-key tiles of every (sequence, KV
+ * head, block of 32 query heads) group end to end and gives each of the
+ * 1024 waves of its grid an equal run of ceil(tiles / 1024) tiles (at least
+ * 4), so a batch of mixed lengths (one long sequence among short ones)
+ * spreads evenly over the whole GPU.  A group inside one run gets its result
+ * directly; the runs of the others are merged as above.  With a smaller
+ * workspace (attn_decode_workspace_bytes) or a positive num_splits the split
+ * is by the capacity Skv_max, as in attn_decode.  The same holds for
+ * attn_decode_paged and for attn_decode_fp8 with seqlens_k.  The runs depend
+ * on the lengths, so the fp32 rounding order (not the result beyond it) may
+ * change with them.  Up to 2048 sequences, and sequences x ceil(Skv_max / 32)
+ * x Hkv x query-head blocks below 2^31 - 2^20; larger batches split by the
+ * capacity.
  */
 attn_status_t attn_decode_varlen(const void *q, const void *k_cache, const void *v_cache,
                                  void *o, float *lse, const int *seqlens_k, int B, int Hq,
@@ -319,6 +334,18 @@ attn_status_t attn_decode_noalloc(const void *q, const void *k_cache, const void
  * 1; num_splits <= 0 means the library's choice, as in attn_decode).  Returns
  * 0 for invalid sizes. */
 size_t attn_decode_workspace_bytes(int B, int Hq, int Hkv, int Skv, int d, int num_splits);
+
+/* Bytes of workspace for the split by the lengths of attn_decode_varlen,
+ * attn_decode_paged and attn_decode_fp8 with seqlens_k (num_splits <= 0):
+ * a header (16 bytes, then B + 1 ints, padded to 16 bytes: the run length
+ * and each sequence's first tile, which the kernel writes), then fp32
+ * partials with their log-sum-exp (d + 1 values each) in a row per
+ * (sequence, query head) and min(Hq / Hkv, 32) rows per wave of the
+ * 1024-wave grid.  Independent of Skv_max.  For sizes where that split is
+ * not available (see attn_decode_varlen) this is
+ * attn_decode_workspace_bytes(B, Hq, Hkv, Skv_max, d, 0), and the call
+ * splits by the capacity.  Returns 0 for invalid sizes. */
+size_t attn_decode_varlen_workspace_bytes(int B, int Hq, int Hkv, int Skv_max, int d);
 
 /* The number of KV chunks attn_decode uses when passed num_splits <= 0:
  * about one work item per compute unit of an MI355X (256 items over the

@@ -49,3 +49,18 @@ def sample_rows(B, Hq, Sq, n, seed, extra_rows=()):
     for _ in range(n):
         rows.add((int(rng.integers(B)), int(rng.integers(Hq)), int(rng.integers(Sq))))
     return np.array(sorted(rows), dtype=np.int64)
+
+
+def decode_varlen_ref(data, lengths, scale):
+    """The oracle's decode of sequence b over its first lengths[b] keys
+    (O = 0, LSE = -inf for an empty sequence)."""
+    from oracle import cpu
+    B, Hq, d = data["q"].shape
+    o = np.zeros((B, Hq, d))
+    lse = np.full((B, Hq), -np.inf)
+    for b, L in enumerate(lengths):
+        if L > 0:
+            ob, lb = cpu.decode_full(data["q"][b:b + 1], data["k"][b:b + 1, :L],
+                                     data["v"][b:b + 1, :L], scale)
+            o[b], lse[b] = ob[0], lb[0]
+    return o, lse

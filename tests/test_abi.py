@@ -47,7 +47,7 @@ def lib():
 
 def test_library_exports_every_declared_symbol(lib):
     names = declared_functions()
-    assert len(names) == 14, names
+    assert len(names) == 15, names
     raw = ctypes.CDLL(_lib.LIB_PATH)
     for n in names:
         assert hasattr(raw, n), n
@@ -287,6 +287,28 @@ def test_decode_workspace_of_the_gqa_decode_workload(lib):
     # 8 chunks without a workspace are refused before any launch
     assert lib.attn_decode(P, P, P, P, None, 64, 32, 8, 4096, 128, 0.088, 8, None, 0,
                            None) == WS
+
+
+def test_decode_varlen_workspace_bytes(lib):
+    """The split by the lengths: a header (16 bytes, then one int per sequence
+    and one more, padded to 16 bytes), then fp32 partials with their
+    log-sum-exp (d + 1 values) in a row per (sequence, query head) and
+    min(Hq / Hkv, 32) rows per wave of the 1024-wave grid; past 2048
+    sequences the capacity split's size."""
+    vw = lib.attn_decode_varlen_workspace_bytes
+    hdr = lambda B: 16 + -(-4 * (B + 1) // 16) * 16
+    assert vw(64, 32, 8, 32768, 128) == hdr(64) + (64 * 32 + 1024 * 4) * 129 * 4
+    assert vw(2, 8, 2, 1000, 64) == hdr(2) + (2 * 8 + 1024 * 4) * 65 * 4
+    assert vw(1, 64, 1, 300, 128) == hdr(1) + (64 + 1024 * 32) * 129 * 4   # two blocks of 32
+    assert vw(3, 6, 2, 5, 128) == hdr(3) + (18 + 1024 * 3) * 129 * 4
+    assert vw(2049, 8, 8, 4096, 128) == lib.attn_decode_workspace_bytes(2049, 8, 8, 4096, 128, 0)
+    assert vw(2048, 8, 8, 4096, 128) == hdr(2048) + (2048 * 8 + 1024) * 129 * 4
+    # tile positions past an int: the capacity split
+    big = 0x7fffffff // 32
+    assert vw(2048, 8, 1, big, 64) == lib.attn_decode_workspace_bytes(2048, 8, 1, big, 64, 0)
+    assert vw(2, 8, 3, 100, 128) == 0      # bad ratio
+    assert vw(2, 8, 2, 100, 96) == 0       # bad d
+    assert vw(0, 8, 2, 100, 128) == 0      # no sequences
 
 
 def test_decode_noalloc_validation(lib):

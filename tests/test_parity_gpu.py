@@ -11,7 +11,8 @@ import pytest
 
 import synth_inputs as si
 from oracle import cpu, ref
-from tests.gpu_util import (assert_close, bf16_to_np, f32_to_np, sample_rows, to_dev)
+from tests.gpu_util import (assert_close, bf16_to_np, decode_varlen_ref, f32_to_np, sample_rows,
+                            to_dev)
 
 pytestmark = pytest.mark.gpu
 
@@ -322,16 +323,7 @@ DECODE_VARLEN = [  # B, Hq, Hkv, Skv_max, d, splits, lengths (None: random in [0
 ]
 
 
-def _decode_varlen_ref(data, lengths, scale):
-    B, Hq, d = data["q"].shape
-    o = np.zeros((B, Hq, d))
-    lse = np.full((B, Hq), -np.inf)
-    for b, L in enumerate(lengths):
-        if L > 0:
-            ob, lb = cpu.decode_full(data["q"][b:b + 1], data["k"][b:b + 1, :L],
-                                     data["v"][b:b + 1, :L], scale)
-            o[b], lse[b] = ob[0], lb[0]
-    return o, lse
+_decode_varlen_ref = decode_varlen_ref
 
 
 @pytest.mark.parametrize("case", DECODE_VARLEN,
@@ -374,6 +366,7 @@ DECODE_PAGED = [  # B, Hq, Hkv, d, page_size, max_pages, splits, lengths (None: 
     (2, 32, 4, 128, 256, 4, 3, [1024, 700]),
     (64, 8, 2, 128, 128, 4, 8, None),                 # groups fill the GPU: whole sequences
     (3, 4, 1, 128, 48, 7, 2, [336, 47, 100]),         # page size a multiple of 16, not of 32
+    (6, 16, 4, 128, 32, 64, 0, [2048, 100, 0, 1500, 33, 2047]),   # split by the lengths
 ]
 
 

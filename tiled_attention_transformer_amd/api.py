@@ -187,6 +187,18 @@ def attn_decode_workspace_bytes(B, Hq, Hkv, Skv, d, num_splits=0) -> int:
     return int(_lib.load().attn_decode_workspace_bytes(B, Hq, Hkv, Skv, d, num_splits))
 
 
+def attn_decode_varlen_workspace_bytes(B, Hq, Hkv, Skv_max, d) -> int:
+    return int(_lib.load().attn_decode_varlen_workspace_bytes(B, Hq, Hkv, Skv_max, d))
+
+
+def _decode_ws_bytes(B, Hq, Hkv, Skv, d, num_splits, with_lengths):
+    # with per-sequence lengths and the library's choice: the workspace of the
+    # split by the lengths, so the kernel spreads mixed lengths over the GPU
+    if with_lengths and num_splits <= 0:
+        return attn_decode_varlen_workspace_bytes(B, Hq, Hkv, Skv, d)
+    return attn_decode_workspace_bytes(B, Hq, Hkv, Skv, d, num_splits)
+
+
 def attn_decode_pick_splits(B, Hq, Hkv, Skv) -> int:
     return int(_lib.load().attn_decode_pick_splits(B, Hq, Hkv, Skv))
 
@@ -236,7 +248,10 @@ def attn_decode_varlen(q, k_cache, v_cache, seqlens_k, o=None, lse=None, scale=N
 
     As :func:`attn_decode`, with ``seqlens_k`` an int32 GPU tensor ``[B]``:
     sequence b attends to its first ``seqlens_k[b]`` cache rows (clamped to
-    the cache capacity on the device).
+    the cache capacity on the device).  With ``num_splits <= 0`` the
+    workspace allocated here (or one of at least
+    :func:`attn_decode_varlen_workspace_bytes` bytes) lets the kernel split
+    the batch by the lengths themselves.
     """
     _need(seqlens_k, "seqlens_k", torch.int32, 1)
     if seqlens_k.shape[0] != q.shape[0]:
@@ -273,7 +288,7 @@ def attn_decode_paged(q, k_pages, v_pages, block_table, seqlens_k, o=None, lse=N
         lse = torch.empty((B, Hq), dtype=torch.float32, device=q.device)
     if lse is not None:
         _need(lse, "lse", torch.float32, 2)
-    nbytes = attn_decode_workspace_bytes(B, Hq, Hkv, max_pages * page_size, d, num_splits)
+    nbytes = _decode_ws_bytes(B, Hq, Hkv, max_pages * page_size, d, num_splits, True)
     if workspace is None and nbytes > 0:
         workspace = torch.empty(nbytes, dtype=torch.uint8, device=q.device)
     ws_bytes = 0 if workspace is None else workspace.numel() * workspace.element_size()
@@ -319,7 +334,7 @@ def attn_decode_fp8(q, k_cache, v_cache, k_scale, v_scale, seqlens_k=None, o=Non
         lse = torch.empty((B, Hq), dtype=torch.float32, device=q.device)
     if lse is not None:
         _need(lse, "lse", torch.float32, 2)
-    nbytes = attn_decode_workspace_bytes(B, Hq, Hkv, Skv, d, num_splits)
+    nbytes = _decode_ws_bytes(B, Hq, Hkv, Skv, d, num_splits, seqlens_k is not None)
     if workspace is None and nbytes > 0:
         workspace = torch.empty(nbytes, dtype=torch.uint8, device=q.device)
     ws_bytes = 0 if workspace is None else workspace.numel() * workspace.element_size()
@@ -376,7 +391,7 @@ def _decode(q, k_cache, v_cache, seqlens_k, o, lse, scale, num_splits, workspace
         lse = torch.empty((B, Hq), dtype=torch.float32, device=q.device)
     if lse is not None:
         _need(lse, "lse", torch.float32, 2)
-    nbytes = attn_decode_workspace_bytes(B, Hq, Hkv, Skv, d, num_splits)
+    nbytes = _decode_ws_bytes(B, Hq, Hkv, Skv, d, num_splits, seqlens_k is not None)
     if workspace is None and nbytes > 0:
         workspace = torch.empty(nbytes, dtype=torch.uint8, device=q.device)
     ws_bytes = 0 if workspace is None else workspace.numel() * workspace.element_size()

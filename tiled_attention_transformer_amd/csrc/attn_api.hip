@@ -94,8 +94,16 @@ attn_status_t decode_impl(const void *q, const void *k_cache, const void *v_cach
     const attn_status_t st = decode_args_status(q, k_cache, v_cache, o, lse, B, Hq, Hkv, Skv, d,
                                                 scale, num_splits, fp8);
     if (st != ATTN_OK) return st;
-    const DecodeShape sh = decode_shape(B, Hq, Hkv, Skv, num_splits);
-    const size_t need = decode_ws_bytes(B, Hq, d, sh.nsplit);
+    DecodeShape sh = decode_shape(B, Hq, Hkv, Skv, num_splits);
+    size_t need = decode_ws_bytes(B, Hq, d, sh.nsplit);
+    // Per-sequence key counts with the library's choice and a workspace
+    // large enough: the kernel splits by the counts themselves (the groups'
+    // key tiles end to end, an equal run per wave).  Otherwise the split is
+    // by the capacity.
+    const bool listed = seqlens != nullptr && num_splits <= 0 && decode_list_ok(B, Hq, Hkv, Skv) &&
+                        workspace != nullptr &&
+                        workspace_bytes >= decode_list_ws_bytes(B, Hq, Hkv, d);
+    if (listed) need = decode_list_ws_bytes(B, Hq, Hkv, d);
     const attn_status_t ws = workspace_status(workspace, workspace_bytes, need);
     if (ws != ATTN_OK) return ws;
     attn::DecParams p{};
@@ -111,7 +119,16 @@ attn_status_t decode_impl(const void *q, const void *k_cache, const void *v_cach
         p.max_pages = paged->max_pages;
         p.num_pages = paged->num_pages;
     }
-    if (need > 0) {
+    if (listed) {
+        // header (run length, per-sequence tile offsets), then the partials:
+        // a row per (sequence, query head), then ncm rows per wave
+        p.listed = 1;
+        p.ncm = Hq / Hkv < attn::kDecCols ? Hq / Hkv : attn::kDecCols;
+        p.ws_hdr = (int *)workspace;
+        p.ws_o = (float *)((char *)workspace + decode_list_hdr_bytes(B));
+        p.ws_lse = p.ws_o + ((size_t)B * Hq + (size_t)attn::kDecListWGs * 4 * p.ncm) * d;
+        sh.nsplit = 0;
+    } else if (need > 0) {
         p.ws_o = (float *)workspace;
         p.ws_lse = p.ws_o + (size_t)sh.nsplit * B * Hq * d;
     }
@@ -222,6 +239,12 @@ size_t attn_decode_workspace_bytes(int B, int Hq, int Hkv, int Skv, int d, int n
     if (!decode_sizes_ok(B, Hq, Hkv, Skv, d) || Hq % Hkv || !d_ok(d)) return 0;
     const DecodeShape sh = decode_shape(B, Hq, Hkv, Skv, num_splits);
     return decode_ws_bytes(B, Hq, d, sh.nsplit);
+}
+
+size_t attn_decode_varlen_workspace_bytes(int B, int Hq, int Hkv, int Skv_max, int d) {
+    if (!decode_sizes_ok(B, Hq, Hkv, Skv_max, d) || Hq % Hkv || !d_ok(d)) return 0;
+    if (decode_list_ok(B, Hq, Hkv, Skv_max)) return decode_list_ws_bytes(B, Hq, Hkv, d);
+    return decode_ws_bytes(B, Hq, d, decode_shape(B, Hq, Hkv, Skv_max, 0).nsplit);
 }
 
 attn_status_t attn_decode(const void *q, const void *k_cache, const void *v_cache, void *o,

@@ -78,8 +78,12 @@ struct DecLay {
     static constexpr int RING = STAGES * STAGE;        // the wave's ring
     static constexpr int MERGE = NCOL * D;             // fp32 output block for the merge
     static constexpr int LSE = NWV * NCOL;             // per-wave LSEs (fp32)
-    // LDS bytes: the rings, then the fp32 merge areas
+    // LDS bytes: the rings, then the fp32 merge areas, then the item list of
+    // a batch split by its key counts (one LDS object, so the compiler
+    // keeps no alias scopes that would make it wait for every tile load
+    // before the next LDS read)
     static constexpr int TOTAL = NWV * RING + 4 * (MERGE + LSE);
+    static constexpr int LIST = 4 * (kDecListSeqs + 1 + NWV);
     static_assert((CPR & (CPR - 1)) == 0 && 32 % CPR == 0, "chunk swizzle needs a power of two");
     static_assert(T_BYTES % 1024 == 0, "a tile must be whole wave loads");
     static_assert(16 % (1024 / RB) == 0, "a load must stay within a 16-key part");
@@ -120,17 +124,73 @@ __device__ __forceinline__ bf16x8 fp8x8_to_bf16(uint32_t lo, uint32_t hi) {
     return __builtin_shufflevector(ab, cd, 0, 1, 2, 3, 4, 5, 6, 7);
 }
 
+// Decode split by the per-sequence key counts.  The 32-key tiles of every
+// group (sequence b, KV head, query-head block) are laid end to end, the
+// groups in (b, KV head, block) order, sequence b's `per` groups holding
+// ceil(len_b / 32) tiles each; list[b] = the position of sequence b's first
+// tile, list[B] = the tile count Wt.  Every wave w of the `workers` takes the
+// run of tiles [w Ct, (w+1) Ct) (clipped to Wt), with Ct = ceil(Wt /
+// workers), at least kDecListMinTiles; returns Ct.  list holds
+// kDecListSeqs + 1 + NWV ints in LDS, the last NWV scratch.  Every thread of
+// the workgroup takes part; the list is complete on return, and every
+// workgroup computes the same one.
+__device__ int decode_list_build(const DecParams &p, int *list, int workers) {
+    const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
+    const int nt = (int)blockDim.x;
+    int *const wave_tot = list + kDecListSeqs + 1;
+    typedef const __attribute__((address_space(1))) int gint;
+    const int per = p.Hkv * p.ncb;                   // groups per sequence
+    // the tiles of one group of each sequence (lengths clamped to
+    // [0, capacity]) into list[]
+    for (int b = tid; b < p.B; b += nt)
+        list[b] = (min(max(((gint *)p.seqlens)[b], 0), p.Skv) + 31) / 32;
+    __syncthreads();
+    // sequence tiles, an exclusive scan over the workgroup: thread t owns
+    // the sequences t*K .. t*K+K-1 (K = ceil(B / threads)), in order
+    const int K = (p.B + nt - 1) / nt;
+    int mine = 0;
+    for (int i = 0; i < K; ++i) {
+        const int b = tid * K + i;
+        if (b < p.B) mine += list[b] * per;
+    }
+    int inc = mine;                                   // inclusive scan in the wave
+#pragma unroll
+    for (int o = 1; o < 64; o <<= 1) {
+        const int up = __shfl_up(inc, o, 64);
+        if (lane >= o) inc += up;
+    }
+    if (lane == 63) wave_tot[wave] = inc;
+    __syncthreads();
+    int base = inc - mine;
+    for (int w = 0; w < wave; ++w) base += wave_tot[w];
+    // each thread replaces its own tile counts by its sequences' offsets
+    for (int i = 0; i < K; ++i) {
+        const int b = tid * K + i;
+        if (b < p.B) {
+            const int n = list[b] * per;
+            list[b] = base;
+            base += n;
+        }
+    }
+    if (tid == nt - 1) list[p.B] = base;
+    __syncthreads();
+    const int Wt = list[p.B];
+    return max(kDecListMinTiles, (Wt + workers - 1) / workers);
+}
+
 // WI (wave items): every wave is a worker of its own that takes whole items
 // (each one key chunk of one group) and writes their partials itself: no
 // merge of the waves, no barrier.  Used for split counts that give every
 // wave of the grid work; otherwise (WI = false) the four waves of a
 // workgroup share each item's keys and merge their states through LDS.
-template <int D, bool F8, bool WI>
+// LISTED (with WI): the split by the key counts, each wave's items being the
+// groups its run of tiles meets (decode_list_build).
+template <int D, bool F8, bool WI, bool LISTED>
 __global__ __launch_bounds__(NT)
 void attn_decode_split_kernel(DecParams p) {
     using L = DecLay<D, F8>;
     constexpr int TK = L::TK;
-    __shared__ __attribute__((aligned(16))) unsigned char lds[L::TOTAL];
+    __shared__ __attribute__((aligned(16))) unsigned char lds[L::TOTAL + (LISTED ? L::LIST : 0)];
 
     const int tid = threadIdx.x;
     const int lane = tid & 63;
@@ -141,34 +201,101 @@ void attn_decode_split_kernel(DecParams p) {
     unsigned char *ring = lds + wave * L::RING;
     float *merge_o = reinterpret_cast<float *>(lds + NWV * L::RING);
     float *merge_l = merge_o + L::MERGE;
+    typedef const __attribute__((address_space(4))) int cint;
+    // the sequence's key count (per sequence when given), read through the
+    // constant address space: a scalar load, outside the vector-load
+    // counter the tile waits rely on
+    auto seq_len = [&](int b) {
+        return p.seqlens ? min(max(((cint *)p.seqlens)[b], 0), p.Skv) : p.Skv;
+    };
 
     // Work items are (group, key range), range fastest, with group =
     // (sequence, KV head, block of query heads); worker w takes items
     // w, w + workers, ...  A worker is a workgroup, or with WI a wave.
     const int G = WI ? (int)gridDim.x * NWV : (int)gridDim.x;
     const int worker = WI ? (int)blockIdx.x * NWV + wave : (int)blockIdx.x;
-    const int nitems = p.B * p.Hkv * p.ncb * p.nsplit;
-    const int my_items = (worker < nitems) ? (nitems - worker + G - 1) / G : 0;
+    // Split by the key counts: this wave's run of tiles [s_lo, s_hi) of the
+    // groups laid end to end (see decode_list_build), whose items are the
+    // groups it meets, from g_first on (empty sequences' groups among them
+    // are items without keys)
+    int *const list = reinterpret_cast<int *>(lds + L::TOTAL);
+    const int per = p.Hkv * p.ncb;                   // groups per sequence
+    int my_items = 0, Ct = 1, s_lo = 0, s_hi = 0, g_first = 0;
+    // (lo, n) of sequence b: its first tile and the tiles of each group
+    auto seq_tiles = [&](int b, int &lo) {
+        lo = __builtin_amdgcn_readfirstlane(list[b]);
+        return (__builtin_amdgcn_readfirstlane(list[b + 1]) - lo) / per;
+    };
+    if constexpr (LISTED) {
+        // (the same in every lane: say so, so the item arithmetic stays scalar)
+        Ct = __builtin_amdgcn_readfirstlane(decode_list_build(p, list, G));
+        if (blockIdx.x == 0) {
+            // the run length and the offsets, for the merge
+            if (tid == 0) p.ws_hdr[0] = Ct;
+            for (int b = tid; b <= p.B; b += NT) p.ws_hdr[4 + b] = list[b];
+        }
+        const int Wt = __builtin_amdgcn_readfirstlane(list[p.B]);
+        const int64_t lo = (int64_t)worker * Ct;
+        if (lo < Wt) {
+            s_lo = (int)lo;
+            s_hi = (int)min(lo + Ct, (int64_t)Wt);
+            // the group holding tile t: sequence = the last b with
+            // list[b] <= t (it has tiles, as t < list[b + 1])
+            auto group_at = [&](int t) {
+                int a = 0, z = p.B - 1;
+                while (a < z) {
+                    const int mid = (a + z + 1) >> 1;
+                    if (__builtin_amdgcn_readfirstlane(list[mid]) <= t) a = mid;
+                    else z = mid - 1;
+                }
+                int l0;
+                const int n = seq_tiles(a, l0);
+                return a * per + (t - l0) / n;
+            };
+            g_first = group_at(s_lo);
+            my_items = group_at(s_hi - 1) - g_first + 1;
+        }
+    } else {
+        const int nitems = p.B * p.Hkv * p.ncb * p.nsplit;
+        my_items = (worker < nitems) ? (nitems - worker + G - 1) / G : 0;
+    }
 
     struct Item {
-        int b, hk, h0, ncols, sp, k_lo, nkeys, ntiles;
+        int b, hk, h0, ncols, sp, nsp, k_lo, nkeys, ntiles;
     };
     auto get_item = [&](int it) {
         Item r;
-        const int item = worker + G * it;
-        r.sp = item % p.nsplit;
-        int id = item / p.nsplit;
-        const int cb = id % p.ncb;
-        id /= p.ncb;
-        r.hk = id % p.Hkv;
-        r.b = id / p.Hkv;
-        r.k_lo = r.sp * p.chunk;
-        // the sequence's cache length (per sequence when given)
-        // (read through the constant address space: a scalar load, outside
-        // the vector-load counter the tile waits rely on)
-        typedef const __attribute__((address_space(4))) int cint;
-        const int len = p.seqlens ? min(max(((cint *)p.seqlens)[r.b], 0), p.Skv) : p.Skv;
-        r.nkeys = max(0, min(len, r.k_lo + p.chunk) - r.k_lo);
+        int id, cb;
+        if constexpr (LISTED) {
+            // group g_first + it (g_first = 0 for a wave without items):
+            // its tiles [sg, sg + n) meet this wave's run in [a, e); sp = 0
+            // for the group's first run, else the run continues a group an
+            // earlier wave began; nsp = the runs of the group
+            id = min(g_first + it, p.B * per - 1);
+            r.b = id / per;
+            const int i = id - r.b * per;
+            r.hk = i / p.ncb;
+            cb = i - r.hk * p.ncb;
+            int l0;
+            const int n = seq_tiles(r.b, l0);
+            const int sg = l0 + i * n;
+            r.sp = n > 0 ? worker - sg / Ct : 0;
+            r.nsp = n > 0 ? (sg + n - 1) / Ct - sg / Ct + 1 : 0;
+            const int a = max(s_lo, sg), e = min(s_hi, sg + n);
+            r.k_lo = n > 0 ? (a - sg) * 32 : 0;
+            r.nkeys = n > 0 ? max(0, min(seq_len(r.b), (e - sg) * 32) - r.k_lo) : 0;
+        } else {
+            const int item = worker + G * it;
+            r.sp = item % p.nsplit;
+            r.nsp = p.nsplit;
+            id = item / p.nsplit;
+            cb = id % p.ncb;
+            id /= p.ncb;
+            r.hk = id % p.Hkv;
+            r.b = id / p.Hkv;
+            r.k_lo = r.sp * p.chunk;
+            r.nkeys = max(0, min(seq_len(r.b), r.k_lo + p.chunk) - r.k_lo);
+        }
         r.ntiles = (r.nkeys + TK - 1) / TK;
         r.ncols = min(NCOL, p.group - NCOL * cb);
         r.h0 = r.hk * p.group + NCOL * cb;
@@ -437,9 +564,34 @@ void attn_decode_split_kernel(DecParams p) {
             // 1 / l, times the value scale of an fp8 cache
             const float inv = lt2 > 0.f ? (F8 ? p.v_scale : 1.f) / lt2 : 0.f;
             stores = true;
-            if (col < it.ncols) {
+            if (LISTED && it.nkeys == 0) {
+                // a group of an empty sequence: the merge writes its result
+            } else if (LISTED && it.nsp == 1) {
+                // the sequence's only chunk (split by the key counts): the
+                // result itself, which the merge then leaves alone
+                if (col < it.ncols) {
+                    const int h = it.h0 + col;
+                    __bf16 *op = p.o + ((int64_t)it.b * p.Hq + h) * D + 4 * g;
+#pragma unroll
+                    for (int db = 0; db < D / 32; ++db)
+#pragma unroll
+                        for (int rq = 0; rq < 4; ++rq)
+                            *reinterpret_cast<bf16x4 *>(op + 32 * db + 8 * rq) =
+                                to_bf16x4(oacc[db][4 * rq] * inv, oacc[db][4 * rq + 1] * inv,
+                                          oacc[db][4 * rq + 2] * inv, oacc[db][4 * rq + 3] * inv);
+                    if (g == 0 && p.lse != nullptr)
+                        p.lse[(int64_t)it.b * p.Hq + h] =
+                            lt2 > 0.f ? (m + fast_log2(lt2)) * kLn2 : -__builtin_inff();
+                }
+            } else if (col < it.ncols) {
                 const int h = it.h0 + col;
-                float *op = p.ws_o + (((int64_t)it.sp * p.B + it.b) * p.Hq + h) * D + 4 * g;
+                // the partial's row: split by the capacity, (sp, b, h); split
+                // by the key counts, (b, h) for a group's first run, else the
+                // wave's own continuation row
+                const int64_t row = !LISTED ? ((int64_t)it.sp * p.B + it.b) * p.Hq + h
+                                    : it.sp == 0 ? (int64_t)it.b * p.Hq + h
+                                                 : (int64_t)p.B * p.Hq + (int64_t)worker * p.ncm + col;
+                float *op = p.ws_o + row * D + 4 * g;
 #pragma unroll
                 for (int db = 0; db < D / 32; ++db)
 #pragma unroll
@@ -448,9 +600,7 @@ void attn_decode_split_kernel(DecParams p) {
                                           oacc[db][4 * rq + 2] * inv, oacc[db][4 * rq + 3] * inv};
                         *reinterpret_cast<f32x4 *>(op + 32 * db + 8 * rq) = v4;
                     }
-                if (g == 0)
-                    p.ws_lse[((int64_t)it.sp * p.B + it.b) * p.Hq + h] =
-                        lt2 > 0.f ? (m + fast_log2(lt2)) * kLn2 : -__builtin_inff();
+                if (g == 0) p.ws_lse[row] = lt2 > 0.f ? (m + fast_log2(lt2)) * kLn2 : -__builtin_inff();
             }
             continue;
         }
@@ -538,10 +688,14 @@ void attn_decode_split_kernel(DecParams p) {
 
 // Merge of the key-range partials: one 4-wave workgroup per (sequence,
 // query head); LSE = M + log(sum_s exp(lse_s - M)), O = sum_s exp(lse_s - LSE) O_s.
-// The splits are spread over the threads (for M and the sum) and over the
-// waves (for O, each wave taking splits w, w+4, ... with independent loads in
-// flight), then combined in a fixed order, so the result is deterministic.
+// The partials' LSE values are spread over the threads (read once, kept in
+// registers for M and the sum); the O rows over the waves, each wave taking
+// partials w, w+4, ... with eight loads in flight; the waves' sums are then
+// combined in a fixed order, so the result is deterministic.  A row may have
+// many partials (a long sequence split into many short runs): the loads, not
+// the arithmetic, set the time.
 constexpr int CW = 4;                        // waves of the merge kernel
+constexpr int CU_ = 8;                       // O loads in flight per wave
 
 __device__ __forceinline__ float wave_max(float x) {
 #pragma unroll
@@ -554,19 +708,43 @@ __device__ __forceinline__ float wave_sum(float x) {
     return x;
 }
 
-template <int D>
-__global__ __launch_bounds__(64 * CW) void attn_decode_combine_kernel(DecParams p) {
+template <int D, bool LISTED>
+// (at most 64 VGPRs: eight waves per SIMD, every CU holding eight rows at once)
+__global__ __launch_bounds__(64 * CW, 8) void attn_decode_combine_kernel(DecParams p) {
     constexpr int PER = D / 64;                     // output elements per lane
     __shared__ float red[CW];
     __shared__ float part[CW - 1][D];
     const int bh = blockIdx.x;                      // b * Hq + h
     const int t = threadIdx.x, lane = t & 63, wave = t >> 6;
     const int64_t stride = (int64_t)p.B * p.Hq;
-    const float *lse_p = p.ws_lse + bh;
+    // the partials of this row: one per chunk (split by the capacity), or
+    // (split by the key counts) one per run of the head's group -- the
+    // first in row bh, the others in the continuation rows of the waves
+    // w0 + 1, w0 + 2, ..; a group of one run has its result written already
+    int ns = p.nsplit, w0 = 0, ccol = 0;
+    if constexpr (LISTED) {
+        typedef const __attribute__((address_space(4))) int cint;
+        const cint *hdr = (const cint *)p.ws_hdr;
+        const int b = bh / p.Hq, h = bh - b * p.Hq;
+        const int hk = h / p.group, hc = h - hk * p.group;
+        const int i = hk * p.ncb + hc / NCOL;          // the head's group in its sequence
+        ccol = hc % NCOL;
+        const int per = p.Hkv * p.ncb, Ct = hdr[0], l0 = hdr[4 + b];
+        const int n = (hdr[5 + b] - l0) / per;          // tiles of the group
+        const int sg = l0 + i * n;
+        w0 = sg / Ct;
+        ns = n > 0 ? (sg + n - 1) / Ct - w0 + 1 : 0;
+        if (ns == 1) return;
+    }
+    auto row = [&](int s) -> int64_t {
+        if constexpr (!LISTED) return (int64_t)s * stride + bh;
+        return s == 0 ? bh : stride + (int64_t)(w0 + s) * p.ncm + ccol;
+    };
 
-    // M = max_s lse_s
-    float mx = -__builtin_inff();
-    for (int s = t; s < p.nsplit; s += 64 * CW) mx = fmaxf(mx, lse_p[s * stride]);
+    // M = max_s lse_s; thread t holds lse_t (and loops past 64 * CW partials)
+    const float lse_t = t < ns ? p.ws_lse[row(t)] : -__builtin_inff();
+    float mx = lse_t;
+    for (int s = t + 64 * CW; s < ns; s += 64 * CW) mx = fmaxf(mx, p.ws_lse[row(s)]);
     mx = wave_max(mx);
     if (lane == 0) red[wave] = mx;
     __syncthreads();
@@ -576,8 +754,8 @@ __global__ __launch_bounds__(64 * CW) void attn_decode_combine_kernel(DecParams 
     const float Mu = M == -__builtin_inff() ? 0.f : M;
     __syncthreads();
     // tot = sum_s exp(lse_s - M)
-    float tt = 0.f;
-    for (int s = t; s < p.nsplit; s += 64 * CW) tt += fast_exp2((lse_p[s * stride] - Mu) * kLog2e);
+    float tt = t < ns ? fast_exp2((lse_t - Mu) * kLog2e) : 0.f;
+    for (int s = t + 64 * CW; s < ns; s += 64 * CW) tt += fast_exp2((p.ws_lse[row(s)] - Mu) * kLog2e);
     tt = wave_sum(tt);
     if (lane == 0) red[wave] = tt;
     __syncthreads();
@@ -586,34 +764,35 @@ __global__ __launch_bounds__(64 * CW) void attn_decode_combine_kernel(DecParams 
     for (int w = 0; w < CW; ++w) tot += red[w];
     const float lse = tot > 0.f ? Mu + fast_log2(tot) * kLn2 : -__builtin_inff();
 
-    // O: wave w sums splits w, w+CW, ...; lane L holds elements PER*L ..
+    // O: wave w sums partials w, w+CW, ..., CU_ of them per round; lane L
+    // holds elements PER*L ..
     float acc[PER];
 #pragma unroll
     for (int e = 0; e < PER; ++e) acc[e] = 0.f;
     if (tot > 0.f) {
-        const float *o_p = p.ws_o + (int64_t)bh * D + PER * lane;
-        int s = wave;
+        const float *o_p = p.ws_o + PER * lane;
 #pragma unroll 1
-        for (; s + 3 * CW < p.nsplit; s += 4 * CW) {
-            float w4[4], v4[4][PER];
+        for (int s = wave; s < ns; s += CU_ * CW) {
+            float wu[CU_], vu[CU_][PER];
 #pragma unroll
-            for (int u = 0; u < 4; ++u) {
+            for (int u = 0; u < CU_; ++u) {
                 const int su = s + u * CW;
-                w4[u] = lse_p[su * stride];
+                wu[u] = -__builtin_inff();
 #pragma unroll
-                for (int e = 0; e < PER; ++e) v4[u][e] = o_p[su * stride * D + e];
+                for (int e = 0; e < PER; ++e) vu[u][e] = 0.f;
+                if (su < ns) {
+                    const int64_t ru = row(su);
+                    wu[u] = p.ws_lse[ru];
+#pragma unroll
+                    for (int e = 0; e < PER; ++e) vu[u][e] = o_p[ru * D + e];
+                }
             }
 #pragma unroll
-            for (int u = 0; u < 4; ++u) {
-                const float w = fast_exp2((w4[u] - lse) * kLog2e);
+            for (int u = 0; u < CU_; ++u) {
+                const float w = wu[u] == -__builtin_inff() ? 0.f : fast_exp2((wu[u] - lse) * kLog2e);
 #pragma unroll
-                for (int e = 0; e < PER; ++e) acc[e] += w * v4[u][e];
+                for (int e = 0; e < PER; ++e) acc[e] += w * vu[u][e];
             }
-        }
-        for (; s < p.nsplit; s += CW) {
-            const float w = fast_exp2((lse_p[s * stride] - lse) * kLog2e);
-#pragma unroll
-            for (int e = 0; e < PER; ++e) acc[e] += w * o_p[s * stride * D + e];
         }
     }
     if (wave > 0) {
@@ -644,6 +823,18 @@ hipError_t launch_t(DecParams p, hipStream_t s) {
     // split the keys and merge them, and the result goes out directly;
     // otherwise the key ranges of a sequence spread over the workgroups and
     // a second kernel merges their partials.
+    if (p.listed) {
+        // split by the key counts: a fixed grid (the workspace holds a row
+        // per wave of it), every wave a worker with its own run; the merge
+        // follows
+        hipLaunchKernelGGL((attn_decode_split_kernel<D, F8, true, true>), dim3(kDecListWGs), dim3(NT), 0,
+                           s, p);
+        e = hipGetLastError();
+        if (e != hipSuccess) return e;
+        hipLaunchKernelGGL((attn_decode_combine_kernel<D, true>), dim3((unsigned)(p.B * p.Hq)),
+                           dim3(64 * CW), 0, s, p);
+        return hipGetLastError();
+    }
     const int64_t groups = (int64_t)p.B * p.Hkv * p.ncb;
     const int64_t items = groups * p.nsplit;
     if (items > 0x7fffffff) return hipErrorInvalidConfiguration;
@@ -651,14 +842,14 @@ hipError_t launch_t(DecParams p, hipStream_t s) {
     if (blocks <= 0) return hipSuccess;
     // split items for every wave of the grid: waves take whole items
     if (p.nsplit > 1 && items >= (int64_t)NWV * cus)
-        hipLaunchKernelGGL((attn_decode_split_kernel<D, F8, true>), dim3((unsigned)blocks), dim3(NT), 0,
+        hipLaunchKernelGGL((attn_decode_split_kernel<D, F8, true, false>), dim3((unsigned)blocks), dim3(NT), 0,
                            s, p);
     else
-        hipLaunchKernelGGL((attn_decode_split_kernel<D, F8, false>), dim3((unsigned)blocks), dim3(NT),
+        hipLaunchKernelGGL((attn_decode_split_kernel<D, F8, false, false>), dim3((unsigned)blocks), dim3(NT),
                            0, s, p);
     e = hipGetLastError();
     if (e != hipSuccess || p.nsplit == 1) return e;
-    hipLaunchKernelGGL(attn_decode_combine_kernel<D>, dim3((unsigned)(p.B * p.Hq)), dim3(64 * CW), 0,
+    hipLaunchKernelGGL((attn_decode_combine_kernel<D, false>), dim3((unsigned)(p.B * p.Hq)), dim3(64 * CW), 0,
                        s, p);
     return hipGetLastError();
 }

@@ -96,6 +96,24 @@ attn_status_t decode_args_status(const void *q, const void *k_cache, const void 
     return ATTN_OK;
 }
 
+bool decode_list_ok(int B, int Hq, int Hkv, int Skv) {
+    // a list that fits the kernel's LDS, and tile positions (sequences x
+    // 32-key tiles x KV heads x query blocks, plus a run per wave) in an int
+    const int ncb = ceil_div(Hq / Hkv, kDecCols);
+    return B <= kDecListSeqs &&
+           prod_le(0x7fffffff - (1 << 20), {B, ceil_div(Skv, 32), Hkv, ncb});
+}
+
+size_t decode_list_ws_bytes(int B, int Hq, int Hkv, int d) {
+    // header (run length, per-sequence offsets), then fp32 partials and
+    // their LSE values: a row per (sequence, query head) and ncm per wave
+    const int ncm = Hq / Hkv < kDecCols ? Hq / Hkv : kDecCols;
+    const size_t rows = (size_t)B * Hq + (size_t)kDecListWGs * 4 * ncm;
+    return decode_list_hdr_bytes(B) + rows * (size_t)(d + 1) * sizeof(float);
+}
+
+size_t decode_list_hdr_bytes(int B) { return 16 + ((size_t)4 * (B + 1) + 15) / 16 * 16; }
+
 attn_status_t workspace_status(const void *workspace, size_t workspace_bytes, size_t need) {
     if (need == 0) return ATTN_OK;
     if (!workspace || workspace_bytes < need) return ATTN_ERR_WORKSPACE;

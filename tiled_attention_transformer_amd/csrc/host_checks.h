@@ -38,6 +38,12 @@ struct Fp8Scales {
 attn_status_t decode_args_status(const void *q, const void *k_cache, const void *v_cache,
                                  const void *o, const float *lse, int B, int Hq, int Hkv, int Skv,
                                  int d, float scale, int num_splits, const Fp8Scales *fp8);
+// Decode split by the per-sequence key counts: whether a batch can use it,
+// its workspace bytes, and the bytes of the workspace's header (the run
+// length and the per-sequence tile offsets, before the partials)
+bool decode_list_ok(int B, int Hq, int Hkv, int Skv);
+size_t decode_list_ws_bytes(int B, int Hq, int Hkv, int d);
+size_t decode_list_hdr_bytes(int B);
 // the workspace check of a decode call that needs `need` bytes
 attn_status_t workspace_status(const void *workspace, size_t workspace_bytes, size_t need);
 

@@ -86,6 +86,15 @@ struct DecParams {
     int nsplit, chunk;       // key chunks and keys per chunk
     float c;                 // scale * log2(e) (times the key scale of an fp8 cache)
     float v_scale;           // value scale of an fp8 cache (unused for bf16)
+    // split by the per-sequence key counts (seqlens given): the kernel lays
+    // the groups' tiles end to end and gives every wave an equal run; it
+    // writes the run length and the per-sequence tile offsets to ws_hdr
+    // (ws_hdr[0], ws_hdr[4 + b]) for the merge.  Partial rows: B * Hq for
+    // each group's first run, then ncm per wave for the run that continues a
+    // group begun by an earlier wave (ncm = query heads of a block).
+    int listed;
+    int *ws_hdr;
+    int ncm;
 };
 
 // k-means assignment: nearest centroid of every point

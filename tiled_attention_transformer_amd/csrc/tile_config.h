@@ -25,4 +25,14 @@ constexpr int kSchedItems = 1024;
 constexpr int kDecThreads = 256;
 constexpr int kDecCols = 32;
 
+// Decode with per-sequence key counts, split by the counts themselves (the
+// library's choice when the caller's workspace is large enough): the 32-key
+// tiles of every (sequence, KV head, query-head block) group are laid end to
+// end, and each wave of a grid of kDecListWGs four-wave workgroups takes an
+// equal run of them, at least kDecListMinTiles.  Up to kDecListSeqs
+// sequences.
+constexpr int kDecListWGs = 256;
+constexpr int kDecListMinTiles = 4;
+constexpr int kDecListSeqs = 2048;
+
 }  // namespace attn
