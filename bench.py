@@ -75,9 +75,9 @@ def decode_bytes(B, Hq, Hkv, Skv, d, kv_elem_bytes=2):
 TRAFFIC_PATH = os.path.join(ROOT, "profiles", "traffic.json")
 # which kernels make up each reported path (substrings of the rocprofv3 names)
 TRAFFIC_KERNELS = {"prefill": ["attn_fwd_pp_kernel<128, true, false, 4, false>"],
-                   "decode": ["attn_decode_split_kernel<128, false, true>",
-                              "attn_decode_combine_kernel<128>"],
-                   "decode_fp8": ["attn_decode_split_kernel<128, true, false>"],
+                   "decode": ["attn_decode_split_kernel<128, false, true, false>",
+                              "attn_decode_combine_kernel<128, false>"],
+                   "decode_fp8": ["attn_decode_split_kernel<128, true, false, false>"],
                    "kmeans": ["kmeans_assign_kernel<128, 128>"]}
 # paths whose kernels only run with a context line (absent from a run without it)
 TRAFFIC_OPTIONAL = {"decode_fp8", "kmeans"}
@@ -168,8 +168,8 @@ COUNTER_PASSES = [
      "SQ_LDS_BANK_CONFLICT", "SQ_WAIT_INST_LDS", "SQ_INSTS_VMEM", "SQ_ACTIVE_INST_ANY"],
 ]
 COUNTER_KERNELS = {"prefill": "attn_fwd_pp_kernel<128, true, false, 4, false>",
-                   "decode": "attn_decode_split_kernel<128, false, true>",
-                   "decode_fp8": "attn_decode_split_kernel<128, true, false>",
+                   "decode": "attn_decode_split_kernel<128, false, true, false>",
+                   "decode_fp8": "attn_decode_split_kernel<128, true, false, false>",
                    "kmeans": "kmeans_assign_kernel<128, 128>"}
 
 
@@ -288,7 +288,7 @@ def extra_workloads(api, dev, stream, which=EXTRAS, calls=20, dec_ms=None, dec_i
             "ms": round(ms, 5), "GB/s": round(gbs, 1), "frac_of_8000": round(gbs / PEAK_HBM_GBS, 4),
             "num_splits": api.attn_decode_pick_splits(spec["B"], spec["Hq"], spec["Hkv"], spec["Skv"]),
             "algorithmic_bytes": nb, "traffic": load_traffic("decode_auto"),
-            "kernel": "attn_decode_split_kernel<128, false, false> (whole sequences per "
+            "kernel": "attn_decode_split_kernel<128, false, false, false> (whole sequences per "
                       "workgroup, the four waves merged in the kernel)"}
     # decode with an fp8 KV cache (the decode workload's sizes)
     if "fp8" in which:
@@ -329,7 +329,7 @@ def fp8_decode(api, dev, stream, gen, d, timed, out, dec_ms):
     out["decode_fp8_kv_B64_Hq32_Hkv8_Skv4096_d128"] = {
         "ms": round(ms, 5), "GB/s": round(gbs, 1), "frac_of_8000": round(gbs / PEAK_HBM_GBS, 4),
         "algorithmic_bytes": nb, "traffic": load_traffic("decode_fp8"),
-        "kernel": "attn_decode_split_kernel<128, true, false> (library's split choice: "
+        "kernel": "attn_decode_split_kernel<128, true, false, false> (library's split choice: "
                   "whole sequences per workgroup)",
         "speedup_vs_bf16_cache": None if dec_ms is None else round(dec_ms / ms, 3)}
     del q, codes, o, lse, ws
@@ -367,6 +367,9 @@ def skewed_decode(api, dev, stream, gen, d, timed, out):
              "workspace_bytes": nbytes}
         if name != "split_by_lengths":
             r["num_splits"] = api.attn_decode_pick_splits(B, Hq, Hkv, cap) if ns == 0 else ns
+        else:
+            r["kernel"] = ("attn_decode_split_kernel<128, false, true, true> (an equal run of key "
+                           "tiles per wave) + attn_decode_combine_kernel<128, true>")
         line[name] = r
         del ws
     out["decode_varlen_skewed_B64_Hq32_Hkv8_cap32768_d128"] = line
@@ -639,9 +642,9 @@ def main():
             "roofline": {"bound": "hbm", "achieved": round(gbs, 1), "peak": PEAK_HBM_GBS,
                          "unit": "GB/s", "frac": round(gbs / PEAK_HBM_GBS, 4),
                          "traffic": load_traffic("decode"), "counters": load_counters("decode"),
-                         "kernel": "attn_decode_split_kernel<128, false, true> (%d key chunks "
+                         "kernel": "attn_decode_split_kernel<128, false, true, false> (%d key chunks "
                                    "per sequence, one chunk per wave at a time) + "
-                                   "attn_decode_combine_kernel<128> (LSE merge of the chunks)"
+                                   "attn_decode_combine_kernel<128, false> (LSE merge of the chunks)"
                                    % nsplit},
         },
         "kernel_hash": kernel_hash(),

@@ -39,6 +39,16 @@
 //    worker of its own instead (template parameter WI): it takes whole items
 //    and writes each one's partial itself, with no merge of the waves and
 //    no barrier;
+//  * with per-sequence key counts the split can follow the counts instead of
+//    the capacity (template parameter LISTED, with WI): every workgroup
+//    builds the same list of sequence offsets in LDS from the counts, the
+//    32-key tiles of all groups lie end to end, and wave w of the fixed
+//    1024-wave grid takes the run of tiles [w Ct, (w+1) Ct) with
+//    Ct = ceil(tiles / 1024), meeting one or more groups.  Every wave reads
+//    the same number of bytes whatever the mix of lengths; a group's first
+//    run writes its partial to the group's own row, a run that continues a
+//    group begun by an earlier wave to that wave's one continuation row, and
+//    a group inside one run writes its result directly;
 //  * at the end of an item the four waves merge their states through LDS
 //    (log-sum-exp weights, then a fixed-order sum, so results are
 //    deterministic) and the result goes out: bf16 O and LSE when the item is
