@@ -55,6 +55,19 @@ int main() {
     CHECK(decode_ws_bytes(1, 1, 128, 1) == 0);
     CHECK(decode_ws_bytes(65536, 256, 128, 65536) ==
           (size_t)65536 * 65536 * 256 * 129 * sizeof(float));
+    // split by the lengths: eligibility (list size, tile positions in an
+    // int with room for the runs), header and workspace bytes
+    CHECK(decode_list_ok(64, 32, 8, 32768) && decode_list_ok(1, 1, 1, 1));
+    CHECK(decode_list_ok(2048, 64, 1, 1024) && !decode_list_ok(2049, 64, 1, 1024));
+    CHECK(!decode_list_ok(2048, 8, 1, IM - 64) && !decode_list_ok(2048, 256, 1, 1 << 22));
+    CHECK(decode_list_ok(2048, 256, 1, 1 << 20));
+    CHECK(decode_list_ok(1, 1, 1, IM - 64));
+    CHECK(decode_list_hdr_bytes(1) == 32 && decode_list_hdr_bytes(3) == 32 &&
+          decode_list_hdr_bytes(4) == 48 && decode_list_hdr_bytes(2048) == 16 + 8208);
+    CHECK(decode_list_ws_bytes(64, 32, 8, 128) ==
+          decode_list_hdr_bytes(64) + (size_t)(64 * 32 + 1024 * 4) * 129 * sizeof(float));
+    CHECK(decode_list_ws_bytes(2048, 256, 1, 128) ==
+          decode_list_hdr_bytes(2048) + (size_t)(2048 * 256 + 1024 * 32) * 129 * sizeof(float));
     CHECK(decode_sizes_ok(64, 32, 8, 4096, 128));
     CHECK(!decode_sizes_ok(64, 32, 8, IM, 128) && !decode_sizes_ok(0, 32, 8, 4096, 128));
     CHECK(!decode_sizes_ok(IM, IM, IM, IM - 64, 128));
