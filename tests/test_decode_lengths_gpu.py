@@ -72,6 +72,8 @@ LISTED = [  # B, Hq, Hkv, Skv_max, d, lengths
     (MAX_SEQS, 4, 1, 1024, 64, "rand"),                              # the longest list
     (12, 8, 2, 5000, 128, [300] * 12),                               # every group over several runs
     (1024, 8, 8, 64, 64, [32] * 1024),                               # 8 groups a run: no merge
+    (2, 32, 8, 40000, 128, [40000, 1]),                              # few long groups: many runs each
+    (32, 8, 8, 3000, 64, "rand"),                                    # 256 groups
     (300, 8, 2, 100, 128, "rand"),                                   # groups whole and split
     (3, 8, 2, 700, 128, [-7, 800, 650]),                             # out-of-range lengths clamped
 ]
