@@ -1243,18 +1243,24 @@ void attn_fwd_pp_kernel(FwdParams p) {
     View cur = make_view(r0);
     View nx = make_view(next_tiled(r0));
     sq1 = nx.r;
+    // At the start every workgroup loads at once: only r0's rows and tiles
+    // 0 .. NS_-2 go out before the first barrier (tile 0 is waited for
+    // there); the next item's rows follow after it, under the first MFMA
+    // phase, and tile 1 is waited for after that phase, ahead of the
+    // barrier before the first M(0)
     load_q(item(r0), qf);
-    if (sq1 >= 0) load_q(item(sq1), qn);
     load_item(r0);
-    // tiles 0 .. NS_-2, complete before the first barrier
     for (int i = 0; i < NS_ - 1; ++i) issue_next();
-    wait_vmcnt<0>();
+    wait_vmcnt<(NS_ - 2) * L::PER_WAVE>();
 #pragma unroll
     for (int db = 0; db < D / 32; ++db) oacc[db] = f32x16{};
     lds_barrier();
     if (grp_b) lds_barrier();            // B idles through A's M(-1)
+    if (sq1 >= 0) load_q(item(sq1), qn);
     // M(-1): the scores of tile 0
     mphase_t(T_{}, F_{}, -1, LD0_{});
+    if (sq1 >= 0) wait_vmcnt<D / 16 + (NS_ - 3) * L::PER_WAVE>();
+    else wait_vmcnt<(NS_ - 3) * L::PER_WAVE>();
     if (cur.nt == 1) rows_advance();     // tile 0 was r0's last
     lds_barrier();
 
