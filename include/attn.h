@@ -184,7 +184,9 @@ attn_status_t attn_varlen_check(const int *cu_seqlens_host, int nseq, int total,
  * num_splits <= 0 lets the library choose (attn_decode_pick_splits): one
  * chunk when the (sequence, KV head, block of 32 query heads) groups alone
  * give each of an MI355X's 256 compute units a work item, else about one
- * work item per compute unit with chunks of at least 512 keys.
+ * work item per compute unit with chunks of at least 512 keys; then a few
+ * more chunks when they fill the last round of work items much better (384
+ * groups, 1.5 per compute unit, take 2 chunks).
  * workspace: DEVICE scratch of at least attn_decode_workspace_bytes(...)
  * bytes, 16-byte aligned, owned by the caller, may be reused between calls
  * on the same stream (not by calls that run concurrently).  When the split
@@ -351,7 +353,10 @@ size_t attn_decode_varlen_workspace_bytes(int B, int Hq, int Hkv, int Skv_max, i
  * about one work item per compute unit of an MI355X (256 items over the
  * (sequence, KV head, head block) groups), but chunks of at least 512 keys;
  * so 1 (whole sequences, no workspace) when the groups alone number 256 or
- * more. */
+ * more.  Of that count s0 and up to max(2 s0, s0 + 3) chunks, the one whose
+ * items fill the rounds of the workers best (256 workgroups, or 1024 waves
+ * once there are at least 1024 split items) is taken when it fills them by
+ * at least 0.15 more. */
 int attn_decode_pick_splits(int B, int Hq, int Hkv, int Skv);
 
 /* Static text for a status code (never NULL). */

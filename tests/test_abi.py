@@ -272,6 +272,12 @@ def test_decode_split_choice(lib):
     assert lib.attn_decode_pick_splits(1, 8, 1, 100000) == 196    # one group: capped by length
     assert lib.attn_decode_pick_splits(1, 1, 1, 100) == 1
     assert lib.attn_decode_pick_splits(1, 3, 2, 100) == 0
+    # balance: 384 groups are 1.5 items per workgroup (a half-empty second
+    # round); two chunks give 768, three full rounds
+    assert lib.attn_decode_pick_splits(48, 32, 8, 4096) == 2
+    assert lib.attn_decode_pick_splits(20, 32, 8, 4096) == 3        # 160 groups: 480 items
+    assert lib.attn_decode_pick_splits(96, 32, 8, 4096) == 1        # 768 groups: full rounds
+    assert lib.attn_decode_pick_splits(40, 32, 8, 8192) == 3        # 320 groups: 960 items
     auto = lib.attn_decode_workspace_bytes(1, 32, 8, 4096, 128, 0)
     assert auto == lib.attn_decode_workspace_bytes(1, 32, 8, 4096, 128, 8)
 

@@ -42,14 +42,37 @@ int pick_splits(int B, int Hq, int Hkv, int Skv) {
     // About one work item per compute unit (an MI355X has 256), but chunks of
     // at least 512 keys.  Measured on the decode kernels: more, shorter
     // chunks spend their time in per-item setup and in the merge of the
-    // partials, fewer leave compute units idle.
+    // partials, fewer leave compute units idle.  Then balance: the workers
+    // (the 256 workgroups, or the 1024 waves once there are that many split
+    // items) take the items in rounds, and a last round that is mostly empty
+    // leaves the GPU idle for its length (384 groups: 1.5 items per
+    // workgroup, the second round half empty); of s0 .. max(2 s0, s0 + 3)
+    // chunks the one with the fullest rounds wins, if it fills them by 0.15
+    // more than s0.
     const int ncb = ceil_div(Hq / Hkv, kDecCols);
     const int64_t base = (int64_t)B * Hkv * ncb;
-    int64_t s = (256 + base - 1) / base;
-    const int max_by_len = ceil_div(Skv, 512);
-    if (s > max_by_len) s = max_by_len;
-    if (s < 1) s = 1;
-    return (int)s;
+    const int64_t max_by_len = ceil_div(Skv, 512);
+    int64_t s0 = (256 + base - 1) / base;
+    if (s0 > max_by_len) s0 = max_by_len;
+    if (s0 < 1) s0 = 1;
+    auto fill = [&](int64_t s) {
+        const int64_t items = base * s;
+        const int64_t workers = (s > 1 && items >= 1024) ? 1024 : 256;
+        const int64_t rounds = (items + workers - 1) / workers;
+        return (double)items / (double)(rounds * workers);
+    };
+    int64_t best = s0;
+    double fbest = fill(s0);
+    const double f0 = fbest;
+    const int64_t s_hi = 2 * s0 > s0 + 3 ? 2 * s0 : s0 + 3;
+    for (int64_t s = s0 + 1; s <= s_hi && s <= max_by_len; ++s) {
+        const double f = fill(s);
+        if (f > fbest) {
+            best = s;
+            fbest = f;
+        }
+    }
+    return (int)(fbest >= f0 + 0.15 ? best : s0);
 }
 
 DecodeShape decode_shape(int B, int Hq, int Hkv, int Skv, int num_splits) {
