@@ -46,7 +46,8 @@ KERNEL_SOURCES = ["tiled_attention_transformer_amd/csrc/attn_fwd.hip",
                   "tiled_attention_transformer_amd/csrc/kmeans_assign.hip",
                   "tiled_attention_transformer_amd/csrc/tile_common.h",
                   "tiled_attention_transformer_amd/csrc/tile_config.h",
-                  "tiled_attention_transformer_amd/csrc/kernels.h"]
+                  "tiled_attention_transformer_amd/csrc/kernels.h",
+                  "tiled_attention_transformer_amd/csrc/fastdiv.h"]
 
 
 def kernel_hash() -> str:

@@ -9,6 +9,7 @@
 #include <math.h>
 #include <stdio.h>
 
+#include "fastdiv.h"
 #include "host_checks.h"
 
 using namespace attn::host;
@@ -39,6 +40,39 @@ int main() {
     CHECK(d_ok(64) && d_ok(128) && !d_ok(96) && !d_ok(0));
     CHECK(scale_ok(0.1f) && !scale_ok(0.f) && !scale_ok(-1.f) && !scale_ok(NAN) &&
           !scale_ok(INFINITY));
+
+    // the kernels' division by launch-fixed divisors: every divisor up to
+    // 70000 and powers of two and their neighbours up to 2^31 - 1, against
+    // numerators at the edges (0, multiples of d and their neighbours, the
+    // top of the 31-bit range) and a spread in between
+    {
+        long long bad = 0;
+        auto check_d = [&](uint32_t d) {
+            const attn::FastDiv f = attn::make_fastdiv(d);
+            auto one = [&](uint32_t n) {
+                if (attn::fastdiv_apply(n, f) != n / d) ++bad;
+            };
+            for (uint32_t n = 0; n < 2048; ++n) one(n);
+            for (uint64_t k = 1; k * d < 0x7fffffffull && k < 4096; k = k * 3 + 1) {
+                const uint32_t n = (uint32_t)(k * d);
+                one(n - 1);
+                one(n);
+                if (n + 1 <= 0x7fffffffu) one(n + 1);
+            }
+            for (uint32_t n = 0x7fffffffu; n > 0x7fffffffu - 4096; --n) one(n);
+            uint32_t x = d * 2654435761u;
+            for (int i = 0; i < 64; ++i) {
+                x = x * 1664525u + 1013904223u;
+                one(x & 0x7fffffffu);
+            }
+        };
+        for (uint32_t d = 1; d <= 70000; ++d) check_d(d);
+        for (int e = 17; e <= 31; ++e)
+            for (long long dd = (1ll << e) - 3; dd <= (1ll << e) + 3; ++dd)
+                if (dd >= 1 && dd < 0x7fffffffll) check_d((uint32_t)dd);
+        check_d(0x7ffffffeu);
+        CHECK(bad == 0);
+    }
 
     // decode sizing: split counts stay in [1, keys / 512] and chunks in int
     for (int skv : {1, 31, 32, 33, 511, 512, 4096, 1 << 20, IM - 64}) {

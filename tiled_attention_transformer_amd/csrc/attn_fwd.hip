@@ -133,18 +133,19 @@ struct FwdItem {
     int64_t qrow0, krow0;   // first query / key row of the sequence
 };
 
-// (cu_l: for a ragged batch, an LDS copy of the offsets, cu_seqlens_q at
-// cu_l[0 .. nseq] and cu_seqlens_k at cu_l[kSchedSeqs + 1 ..], else null)
+// (cu_l: for a ragged batch, an LDS copy of the offsets, 16 bytes per
+// sequence b: cu_seqlens_q[b], cu_seqlens_q[b + 1], cu_seqlens_k[b],
+// cu_seqlens_k[b + 1], so one read fetches them; else null)
 template <bool CAUSAL, bool VARLEN, bool SPLIT, int BR>
 __device__ __forceinline__ FwdItem fwd_item(const FwdParams &p, int it, const int *cu_l = nullptr) {
     FwdItem x;
     const int BH = p.nbatch * p.Hq;
-    const int rs = it / BH;
+    const int rs = (int)fdiv((uint32_t)it, p.fd_bh);
     const int bh = it - rs * BH;
     // split-KV items are (rank, split) pairs in rank-major order
-    const int rank = SPLIT ? rs / p.nsplit : rs;
+    const int rank = SPLIT ? (int)fdiv((uint32_t)rs, p.fd_split) : rs;
     x.sp = SPLIT ? rs - rank * p.nsplit : 0;
-    x.b = bh / p.Hq;
+    x.b = (int)fdiv((uint32_t)bh, p.fd_hq);
     x.h = bh - x.b * p.Hq;
     if constexpr (VARLEN) {
         // the offsets are never written by the kernel: read them through the
@@ -153,10 +154,12 @@ __device__ __forceinline__ FwdItem fwd_item(const FwdParams &p, int it, const in
         typedef const __attribute__((address_space(4))) int cint;
         int qs, qe, ks, ke;
         if (cu_l != nullptr) {
-            qs = __builtin_amdgcn_readfirstlane(cu_l[x.b]);
-            qe = __builtin_amdgcn_readfirstlane(cu_l[x.b + 1]);
-            ks = __builtin_amdgcn_readfirstlane(cu_l[kSchedSeqs + 1 + x.b]);
-            ke = __builtin_amdgcn_readfirstlane(cu_l[kSchedSeqs + 2 + x.b]);
+            typedef int i32x4 __attribute__((ext_vector_type(4)));
+            const i32x4 r = *reinterpret_cast<const i32x4 *>(cu_l + 4 * x.b);
+            qs = __builtin_amdgcn_readfirstlane(r[0]);
+            qe = __builtin_amdgcn_readfirstlane(r[1]);
+            ks = __builtin_amdgcn_readfirstlane(r[2]);
+            ke = __builtin_amdgcn_readfirstlane(r[3]);
         } else {
             cint *cq = (cint *)p.cu_q, *ck = (cint *)p.cu_k;
             qs = cq[x.b];
@@ -185,7 +188,7 @@ __device__ __forceinline__ FwdItem fwd_item(const FwdParams &p, int it, const in
     x.t0 = 0;
     if constexpr (SPLIT) {
         // the tile's own key tiles cut into nsplit shares of equal length
-        const int ct = (x.nt + p.nsplit - 1) / p.nsplit;
+        const int ct = (int)fdiv((uint32_t)(x.nt + p.nsplit - 1), p.fd_split);
         x.t0 = min(x.sp * ct, x.nt);
         x.nt = min(ct, x.nt - x.t0);
     }
@@ -288,12 +291,14 @@ __device__ int fwd_sched_build(const FwdParams &p, int *sm) {
     }
     __syncthreads();
     // the level table is done with: it now keeps a copy of the offsets for
-    // the walk's item lookups (LDS reads instead of chains of scalar loads
+    // the walk's item lookups (one LDS read instead of chains of scalar loads
     // at every item change), in the layout fwd_item takes
-    static_assert(kSchedLevels >= 2 * (kSchedSeqs + 1), "room for both offset arrays");
-    for (int b = tid; b <= nseq; b += nth) {
-        s_lev[b] = p.cu_q[b];
-        s_lev[kSchedSeqs + 1 + b] = p.cu_k[b];
+    static_assert(kSchedLevels >= 4 * kSchedSeqs, "room for the offset records");
+    for (int b = tid; b < nseq; b += nth) {
+        s_lev[4 * b] = p.cu_q[b];
+        s_lev[4 * b + 1] = p.cu_q[b + 1];
+        s_lev[4 * b + 2] = p.cu_k[b];
+        s_lev[4 * b + 3] = p.cu_k[b + 1];
     }
     __syncthreads();
     return cnt;
@@ -368,7 +373,7 @@ void attn_fwd_kernel(FwdParams p) {
             const FwdItem x = item(r);
             l_tiles = x.nt;
             l_keys = x.Skv - x.t0 * BC;
-            l_off = (x.krow0 + (int64_t)x.t0 * BC) * hd_k + (int64_t)(x.h / p.group) * D;
+            l_off = (x.krow0 + (int64_t)x.t0 * BC) * hd_k + (int64_t)fdiv((uint32_t)x.h, p.fd_group) * D;
         }
     };
     auto issue_next = [&]() {
@@ -860,6 +865,7 @@ void attn_fwd_pp_kernel(FwdParams p) {
     constexpr int SCHED_INTS = VARLEN ? 2 * kSchedSeqs + kSchedLevels + kSchedItems : 0;
     __shared__ __attribute__((aligned(16))) __bf16 lds[NS_ * L::STAGE + 2 * SCHED_INTS];
     int *const sched = reinterpret_cast<int *>(lds + NS_ * L::STAGE);
+    static_assert((NS_ * L::STAGE) % 8 == 0 && kSchedSeqs % 4 == 0, "16-byte offset records");
 
     const int tid = threadIdx.x;
     const int lane = tid & 63;
@@ -889,11 +895,14 @@ void attn_fwd_pp_kernel(FwdParams p) {
     const int64_t hd_k = (int64_t)p.Hkv * D;
 
     auto item = [&](int r) { return item_of(at(r)); };
-    auto next_tiled = [&](int r) -> int {
+    // the next position after r whose item has key tiles (-1: none), and
+    // that item, decoded once for the caller
+    auto next_tiled = [&](int r, FwdItem &x) -> int {
         for (int s = r + 1;; ++s) {
             const int it = at(s);
             if (it < 0) return -1;
-            if (item_of(it).nt > 0) return s;
+            x = item_of(it);
+            if (x.nt > 0) return s;
         }
     };
 
@@ -922,13 +931,12 @@ void attn_fwd_pp_kernel(FwdParams p) {
     const bool last_is_v = wave >= L::KR;
     int l_r = -1, l_tiles = 0, l_keys = 0, l_stage = 0;
     int64_t l_off = 0;
-    auto load_item = [&](int r) {
+    auto load_item = [&](int r, const FwdItem &x) {
         l_r = r;
         if (r >= 0) {
-            const FwdItem x = item(r);
             l_tiles = x.nt;
             l_keys = x.Skv;
-            l_off = x.krow0 * hd_k + (int64_t)(x.h / p.group) * D;
+            l_off = x.krow0 * hd_k + (int64_t)fdiv((uint32_t)x.h, p.fd_group) * D;
         }
     };
     // The next tile of the stream: issue_begin() advances the stream and
@@ -949,7 +957,11 @@ void attn_fwd_pp_kernel(FwdParams p) {
             vb = p.v + l_off;
             l_off += BC * hd_k;
             l_keys -= BC;
-            if (--l_tiles == 0) load_item(next_tiled(l_r));
+            if (--l_tiles == 0) {
+                FwdItem x;
+                const int r = next_tiled(l_r, x);
+                load_item(r, x);
+            }
         }
         t_kr = buffer_rsrc(kb, nbytes);
         t_vr = buffer_rsrc(vb, nbytes);
@@ -1023,12 +1035,11 @@ void attn_fwd_pp_kernel(FwdParams p) {
         if (CAUSAL) wk = min(x.Skv, min(w0 + 32, x.Sq) + (x.Skv - x.Sq));
         return wk > 0 ? min(x.nt, (wk + BC - 1) / BC) : 0;
     };
-    auto make_view = [&](int r) {
+    auto make_view = [&](int r, const FwdItem &x) {
         View v;
         v.r = r;
         v.nt = v.ntw = v.Skv = v.off = v.wrow0 = v.qr = 0;
         if (r >= 0) {
-            const FwdItem x = item(r);
             v.nt = x.nt;
             v.ntw = wave_tiles(x);
             v.Skv = x.Skv;
@@ -1230,33 +1241,36 @@ void attn_fwd_pp_kernel(FwdParams p) {
     auto rows_advance = [&]() {
 #pragma unroll
         for (int t = 0; t < D / 16; ++t) qf[t] = qn[t];
-        sq1 = sq1 >= 0 ? next_tiled(sq1) : -1;
-        if (sq1 >= 0) load_q(item(sq1), qn);
+        FwdItem x;
+        sq1 = sq1 >= 0 ? next_tiled(sq1, x) : -1;
+        if (sq1 >= 0) load_q(x, qn);
     };
 
-    const int r0 = next_tiled(-1);
+    FwdItem x0, x1;
+    const int r0 = next_tiled(-1, x0);
     write_empty(-1, r0);
     if (r0 < 0) {
         wait_vmcnt<0>();
         return;
     }
-    View cur = make_view(r0);
-    View nx = make_view(next_tiled(r0));
+    View cur = make_view(r0, x0);
+    const int r1 = next_tiled(r0, x1);
+    View nx = make_view(r1, x1);
     sq1 = nx.r;
     // At the start every workgroup loads at once: only r0's rows and tiles
     // 0 .. NS_-2 go out before the first barrier (tile 0 is waited for
     // there); the next item's rows follow after it, under the first MFMA
     // phase, and tile 1 is waited for after that phase, ahead of the
     // barrier before the first M(0)
-    load_q(item(r0), qf);
-    load_item(r0);
+    load_q(x0, qf);
+    load_item(r0, x0);
     for (int i = 0; i < NS_ - 1; ++i) issue_next();
     wait_vmcnt<(NS_ - 2) * L::PER_WAVE>();
 #pragma unroll
     for (int db = 0; db < D / 32; ++db) oacc[db] = f32x16{};
     lds_barrier();
     if (grp_b) lds_barrier();            // B idles through A's M(-1)
-    if (sq1 >= 0) load_q(item(sq1), qn);
+    if (sq1 >= 0) load_q(x1, qn);
     // M(-1): the scores of tile 0
     mphase_t(T_{}, F_{}, -1, LD0_{});
     if (sq1 >= 0) wait_vmcnt<D / 16 + (NS_ - 3) * L::PER_WAVE>();
@@ -1306,7 +1320,9 @@ void attn_fwd_pp_kernel(FwdParams p) {
             lsum = 0.f;
 #pragma unroll
             for (int db = 0; db < D / 32; ++db) oacc[db] = f32x16{};
-            nx = make_view(next_tiled(cur.r));
+            FwdItem xn;
+            const int rn = next_tiled(cur.r, xn);
+            nx = make_view(rn, xn);
         }
     }
     if (!grp_b) lds_barrier();           // A's barrier for B's last phase
@@ -1360,6 +1376,10 @@ hipError_t launch_t(const FwdParams &p_in, hipStream_t s) {
     if (items <= 0) return hipSuccess;
     if (items > 0x7fffffff) return hipErrorInvalidConfiguration;
     p.nitems = (int)items;
+    p.fd_bh = make_fastdiv((uint32_t)(p.nbatch * p.Hq));
+    p.fd_hq = make_fastdiv((uint32_t)p.Hq);
+    p.fd_group = make_fastdiv((uint32_t)p.group);
+    p.fd_split = make_fastdiv((uint32_t)(SPLIT ? p.nsplit : 1));
     int grid = p.nitems;
     if constexpr (VARLEN && NW == 8) {
         // fewer 256-row items than CUs: 128-row items on 4-wave workgroups

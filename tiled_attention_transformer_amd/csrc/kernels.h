@@ -8,6 +8,7 @@
 
 #include <atomic>
 
+#include "fastdiv.h"
 #include "tile_config.h"
 
 namespace attn {
@@ -18,6 +19,9 @@ constexpr float kLog2e = 1.44269504088896340736f;
 // Slack (log2 units) before the online softmax moves its reference max:
 // weights exp2(s*c - m) stay <= 2^8, far from fp32/bf16 overflow.
 constexpr float kRescaleSlack = 8.0f;
+
+// n / d for 0 <= n < 2^31, with the constants make_fastdiv(d) (fastdiv.h)
+__device__ __forceinline__ uint32_t fdiv(uint32_t n, FastDiv f) { return (__umulhi(n, f.m) + n) >> f.s; }
 
 // Compute units of the current device.  Cached per device after the first
 // query: the attribute query costs host time on every launch otherwise,
@@ -67,6 +71,9 @@ struct FwdParams {
     // ragged batch on a persistent grid with a cost-sorted item list (set by
     // the launcher when the list fits the kSched* bounds)
     int compact;
+    // the item decode's divisors (nbatch * Hq, Hq, group, nsplit), set by the
+    // launcher
+    FastDiv fd_bh, fd_hq, fd_group, fd_split;
 };
 
 struct DecParams {
