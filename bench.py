@@ -47,7 +47,8 @@ KERNEL_SOURCES = ["tiled_attention_transformer_amd/csrc/attn_fwd.hip",
                   "tiled_attention_transformer_amd/csrc/tile_common.h",
                   "tiled_attention_transformer_amd/csrc/tile_config.h",
                   "tiled_attention_transformer_amd/csrc/kernels.h",
-                  "tiled_attention_transformer_amd/csrc/fastdiv.h"]
+                  "tiled_attention_transformer_amd/csrc/fastdiv.h",
+                  "tiled_attention_transformer_amd/csrc/exp2_poly.h"]
 
 
 def kernel_hash() -> str:
@@ -236,7 +237,7 @@ def load_counters(kind: str):
     return t["kernels"][kind]["derived"]
 
 
-EXTRAS = ("decode_auto", "fp8", "skewed", "kmeans", "long", "ragged")
+EXTRAS = ("decode_auto", "fp8", "skewed", "kmeans", "long", "ragged", "exp2_poly")
 
 
 def extra_workloads(api, dev, stream, which=EXTRAS, calls=20, dec_ms=None, dec_inputs=None):
@@ -302,7 +303,39 @@ def extra_workloads(api, dev, stream, which=EXTRAS, calls=20, dec_ms=None, dec_i
         long_causal(api, dev, stream, gen, d, timed, out)
     if "ragged" in which:
         ragged_causal(api, dev, stream, gen, d, timed, out)
+    if "exp2_poly" in which:
+        exp2_poly_prefill(api, dev, stream, gen, d, timed, out)
     return out
+
+
+def exp2_poly_prefill(api, dev, stream, gen, d, timed, out):
+    """The causal prefill workload (B4 H16 S2048) and the long one (B1 H32
+    S16384) with 0 (attn_fwd), 4, 8 and 16 of each lane's 32 exponentials per
+    key tile on the library's exp2 polynomial (attn_fwd_exp2_poly), timed
+    one after the other on the same inputs."""
+    import torch
+    res = {}
+    for name, (B, H, S, seed, n) in (("B4_H16_S2048", (4, 16, 2048, 2, 50)),
+                                     ("B1_H32_S16384", (1, 32, 16384, 3, 10))):
+        gen.manual_seed(seed)
+        q, k, v = (torch.randn((B, S, H, d), generator=gen, device=dev, dtype=torch.float32)
+                   .to(torch.bfloat16) for _ in range(3))
+        o = torch.empty_like(q)
+        lse = torch.empty((B, H, S), dtype=torch.float32, device=dev)
+        fl = prefill_flops(B, H, S, S, d, True)
+        line = {}
+        for share in (0, 4, 8, 16):
+            if share == 0:
+                fn = lambda: api.attn_fwd(q, k, v, o=o, lse=lse, causal=True, stream=stream)
+            else:
+                fn = (lambda sh: lambda: api.attn_fwd_exp2_poly(q, k, v, sh, o=o, lse=lse,
+                                                                causal=True, stream=stream))(share)
+            ms = timed(fn, n=n)
+            line["poly_%d_of_32" % share] = {
+                "ms": round(ms, 5), "frac_of_2500": round(fl / (ms * 1e-3) / 1e12 / PEAK_BF16_TFLOPS, 4)}
+        res["causal_" + name + "_d128"] = line
+        del q, k, v, o, lse
+    out["prefill_exp2_poly_share"] = res
 
 
 def fp8_decode(api, dev, stream, gen, d, timed, out, dec_ms):

@@ -77,7 +77,8 @@ typedef enum {
     ATTN_ERR_SEQLENS = 7,        /* malformed cumulative sequence offsets        */
     ATTN_ERR_HIP = 8,            /* the HIP runtime reported an error on launch  */
     ATTN_ERR_SCALE = 9,          /* scale is not finite and > 0                  */
-    ATTN_ERR_SCRATCH_LIMIT = 10  /* the sizes need more than the fixed scratch   */
+    ATTN_ERR_SCRATCH_LIMIT = 10, /* the sizes need more than the fixed scratch   */
+    ATTN_ERR_OPTION = 11         /* an option is outside its documented values   */
 } attn_status_t;
 
 /* Size of the fixed device scratch that attn_decode_noalloc uses (bytes). */
@@ -94,6 +95,35 @@ typedef enum {
 attn_status_t attn_fwd(const void *q, const void *k, const void *v, void *o, float *lse,
                        int B, int Hq, int Hkv, int Sq, int Skv, int d, float scale,
                        int causal, hipStream_t stream);
+
+/*
+ * attn_fwd with part of the softmax's exponentials computed by a polynomial
+ * on the fused multiply-add path instead of the hardware exponential
+ * (lecompute.fr, "FlashAttention-4 : limites du calcul matriciel", section
+ * "Déplacer une partie des exponentielles": moving a share of the
+ * exponentials onto the FMA units so that both kinds of unit carry part of
+ * the softmax).  Same arguments and layouts as attn_fwd, plus:
+ *   poly_per_32 : of each lane's 32 exponentials per 64-key tile, how many
+ *                 go to the polynomial: 0 (this is then attn_fwd exactly,
+ *                 bit for bit), 4, 8 or 16; any other value returns
+ *                 ATTN_ERR_OPTION before any launch.
+ * The polynomial is exp2(x) = 2^floor(x) * p(x - floor(x)) with a cubic p,
+ * p(0) = 1, fitted for the smallest maximum relative error on [0, 1) by
+ * Remez's exchange (relative error at most 8.6e-5; the weights are rounded
+ * to bfloat16, relative 2^-9, before the P V product).  Masked scores still
+ * give weight exactly 0.  Every fixed batch runs the two-group (ping-pong)
+ * kernel on this path, whatever its size; the debug modes 2 and 4 do not
+ * apply to it.  Errors as attn_fwd, plus ATTN_ERR_OPTION.  On gfx950 the
+ * hardware exponential is not the prefill's limit (the softmax phase is
+ * bound by vector-instruction issue, and the polynomial takes 7 vector
+ * instructions where the exponential takes one), so this is a lever, not
+ * the default: measured slower than attn_fwd at every share (causal B4 H16
+ * S2048 d128: 2.5 %, 4.3 % and 9.1 % at 4, 8 and 16; B1 H32 S16384: 3.4 %,
+ * 6.3 % and 13.1 %).
+ */
+attn_status_t attn_fwd_exp2_poly(const void *q, const void *k, const void *v, void *o,
+                                 float *lse, int B, int Hq, int Hkv, int Sq, int Skv, int d,
+                                 float scale, int causal, int poly_per_32, hipStream_t stream);
 
 /*
  * Prefill with the key range split across workgroups (split-KV), for shapes

@@ -30,7 +30,7 @@ pytestmark = pytest.mark.skipif(_gpu_visible(), reason="host-only ABI tests (fak
 ROOT = os.path.dirname(os.path.dirname(os.path.abspath(__file__)))
 HEADER = os.path.join(ROOT, "include", "attn.h")
 
-OK, NULLPTR, SHAPE, BAD_D, GQA, ALIGN, WS, SEQ, HIP, SCALE, SCRATCH = range(11)
+OK, NULLPTR, SHAPE, BAD_D, GQA, ALIGN, WS, SEQ, HIP, SCALE, SCRATCH, OPTION = range(12)
 P = 1 << 20          # a 16-byte aligned fake address (never dereferenced)
 
 
@@ -47,7 +47,7 @@ def lib():
 
 def test_library_exports_every_declared_symbol(lib):
     names = declared_functions()
-    assert len(names) == 15, names
+    assert len(names) == 16, names
     raw = ctypes.CDLL(_lib.LIB_PATH)
     for n in names:
         assert hasattr(raw, n), n
@@ -55,7 +55,7 @@ def test_library_exports_every_declared_symbol(lib):
 
 
 def test_status_strings(lib):
-    for s in range(11):
+    for s in range(12):
         text = lib.attn_status_string(s)
         assert text and text != b"unknown status"
     assert lib.attn_status_string(99) == b"unknown status"
@@ -86,6 +86,21 @@ def test_fwd_validation(lib):
     # the first failing rule wins, in a fixed order
     assert fwd(lib, q=None, d=96) == NULLPTR
     assert fwd(lib, d=96, Hq=3, Hkv=2) == BAD_D
+
+
+def fwd_poly(lib, poly, q=P, B=1, d=128, scale=0.1):
+    return lib.attn_fwd_exp2_poly(q, P, P, P, None, B, 2, 2, 8, 8, d, scale, 1, poly, None)
+
+
+def test_fwd_exp2_poly_validation(lib):
+    # only the documented shares are accepted; the size checks come first
+    for bad in (-1, 1, 2, 3, 5, 12, 32, 64):
+        assert fwd_poly(lib, bad) == OPTION, bad
+    assert fwd_poly(lib, 8, q=None) == NULLPTR
+    assert fwd_poly(lib, 7, B=0) == SHAPE
+    assert fwd_poly(lib, 8, d=96) == BAD_D
+    assert fwd_poly(lib, 4, scale=0.0) == SCALE
+    assert fwd_poly(lib, 16, q=P + 8) == ALIGN
 
 
 def varlen(lib, cu_q=P, cu_k=P, nseq=2, tq=10, tk=10, mq=6, mk=6, Hq=2, Hkv=1, d=64,

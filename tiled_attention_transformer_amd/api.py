@@ -73,6 +73,17 @@ def attn_fwd(q, k, v, o=None, lse=None, scale=None, causal=False, want_lse=True,
     lse ``[B,Hq,Sq]`` fp32 (``None`` when ``want_lse`` is false and no lse is
     given).  scale defaults to 1/sqrt(d).
     """
+    return _fwd(q, k, v, o, lse, scale, causal, want_lse, stream, None)
+
+
+def attn_fwd_exp2_poly(q, k, v, poly_per_32, o=None, lse=None, scale=None, causal=False,
+                       want_lse=True, stream=None):
+    """``attn_fwd`` with ``poly_per_32`` (0, 4, 8 or 16) of each lane's 32
+    exponentials per key tile computed by the library's exp2 polynomial."""
+    return _fwd(q, k, v, o, lse, scale, causal, want_lse, stream, int(poly_per_32))
+
+
+def _fwd(q, k, v, o, lse, scale, causal, want_lse, stream, poly):
     for t, n in ((q, "q"), (k, "k"), (v, "v")):
         _need(t, n, torch.bfloat16, 4)
     B, Sq, Hq, d = q.shape
@@ -91,9 +102,14 @@ def attn_fwd(q, k, v, o=None, lse=None, scale=None, causal=False, want_lse=True,
         _need(lse, "lse", torch.float32, 3)
         if tuple(lse.shape) != (B, Hq, Sq):
             raise ValueError("lse must be [B,Hq,Sq]")
-    st = _lib.load().attn_fwd(_ptr(q), _ptr(k), _ptr(v), _ptr(o), _ptr(lse), B, Hq, Hkv, Sq, Skv,
-                              d, _scale(scale, d), int(bool(causal)), _stream(stream))
-    _check(st, "attn_fwd")
+    args = (_ptr(q), _ptr(k), _ptr(v), _ptr(o), _ptr(lse), B, Hq, Hkv, Sq, Skv, d,
+            _scale(scale, d), int(bool(causal)))
+    if poly is None:
+        st = _lib.load().attn_fwd(*args, _stream(stream))
+        _check(st, "attn_fwd")
+    else:
+        st = _lib.load().attn_fwd_exp2_poly(*args, poly, _stream(stream))
+        _check(st, "attn_fwd_exp2_poly")
     return o, lse
 
 

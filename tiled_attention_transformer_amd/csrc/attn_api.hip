@@ -49,11 +49,12 @@ attn_status_t finish(hipError_t e, hipStream_t stream) {
 attn_status_t fwd_impl(const void *q, const void *k, const void *v, void *o, float *lse, int B,
                        int Hq, int Hkv, int Sq, int Skv, int d, float scale, int causal,
                        int num_splits, void *workspace, size_t workspace_bytes,
-                       hipStream_t stream) {
+                       hipStream_t stream, int exp2_poly = 0) {
     int ntiles = 0;
     const attn_status_t st = fwd_args_status(q, k, v, o, lse, B, Hq, Hkv, Sq, Skv, d, scale,
                                              &ntiles);
     if (st != ATTN_OK) return st;
+    if (exp2_poly != 0 && exp2_poly != 4 && exp2_poly != 8 && exp2_poly != 16) return ATTN_ERR_OPTION;
     attn::FwdParams p{};
     p.q = (const __bf16 *)q;
     p.k = (const __bf16 *)k;
@@ -69,6 +70,7 @@ attn_status_t fwd_impl(const void *q, const void *k, const void *v, void *o, flo
     p.ntiles = ntiles;
     p.c = scale * attn::kLog2e;
     p.debug = debug_flags();
+    p.exp2_poly = exp2_poly;
     const int ns = num_splits > 0 ? num_splits : fwd_pick_splits(B, Hq, Sq, Skv, causal != 0);
     if (ns <= 1) return finish(attn::launch_fwd(p, d, causal != 0, false, stream), stream);
     const attn_status_t ws = workspace_status(workspace, workspace_bytes,
@@ -168,6 +170,7 @@ const char *attn_status_string(attn_status_t s) {
         case ATTN_ERR_HIP: return "HIP runtime error at launch";
         case ATTN_ERR_SCALE: return "scale must be finite and > 0";
         case ATTN_ERR_SCRATCH_LIMIT: return "the split partials need more than the fixed scratch of attn_decode_noalloc";
+        case ATTN_ERR_OPTION: return "an option is outside its documented set of values";
     }
     return "unknown status";
 }
@@ -176,6 +179,13 @@ attn_status_t attn_fwd(const void *q, const void *k, const void *v, void *o, flo
                        int Hq, int Hkv, int Sq, int Skv, int d, float scale, int causal,
                        hipStream_t stream) {
     return fwd_impl(q, k, v, o, lse, B, Hq, Hkv, Sq, Skv, d, scale, causal, 1, nullptr, 0, stream);
+}
+
+attn_status_t attn_fwd_exp2_poly(const void *q, const void *k, const void *v, void *o, float *lse,
+                                 int B, int Hq, int Hkv, int Sq, int Skv, int d, float scale,
+                                 int causal, int poly_per_32, hipStream_t stream) {
+    return fwd_impl(q, k, v, o, lse, B, Hq, Hkv, Sq, Skv, d, scale, causal, 1, nullptr, 0, stream,
+                    poly_per_32);
 }
 
 size_t attn_fwd_splitkv_workspace_bytes(int B, int Hq, int Sq, int Skv, int d, int causal,

@@ -87,6 +87,7 @@
 
 #include "kernels.h"
 #include "tile_common.h"
+#include "exp2_poly.h"
 
 namespace attn {
 
@@ -852,10 +853,16 @@ void attn_fwd_kernel(FwdParams p) {
 //
 // Tile loads go out spread over the MFMA phases, where the vector ALUs are
 // idle, and are waited for a whole step later (details at the walk below).
-template <int D, bool CAUSAL, bool VARLEN, int NS_, bool POISON>
+//
+// EMU > 0: of each lane's 32 exponentials per key tile, EMU (every 32/EMU-th)
+// are computed by the polynomial of exp2_poly.h on the FMA path instead of
+// the hardware exponential (the same page, section "Déplacer une partie des
+// exponentielles").
+template <int D, bool CAUSAL, bool VARLEN, int NS_, bool POISON, int EMU = 0>
 __global__ __launch_bounds__(512) __attribute__((amdgpu_waves_per_eu(2, 2)))
 void attn_fwd_pp_kernel(FwdParams p) {
     static_assert(NS_ >= 3 && NS_ <= 4, "the schedule needs tiles n, n+1 and a free stage");
+    static_assert(EMU >= 0 && EMU <= 32 && (EMU == 0 || 32 % EMU == 0), "a whole share of the 32");
     constexpr int NW = 8;
     constexpr int BR = 32 * NW;
     using L = FwdLay<D, NW>;
@@ -1205,7 +1212,12 @@ void attn_fwd_pp_kernel(FwdParams p) {
 #pragma unroll
         for (int f = 0; f < 32; ++f) {
             const int kb = f >> 4, r = f & 15;
-            s[kb][r] = fast_exp2(__builtin_fmaf(s[kb][r], c, -m_use));
+            const float x = __builtin_fmaf(s[kb][r], c, -m_use);
+            if constexpr (EMU > 0) {
+                s[kb][r] = f % (32 / EMU) == 32 / EMU - 1 ? exp2_poly(x) : fast_exp2(x);
+            } else {
+                s[kb][r] = fast_exp2(x);
+            }
             rs += s[kb][r];
         }
 #pragma unroll
@@ -1365,6 +1377,27 @@ __global__ __launch_bounds__(256) void attn_fwd_merge_kernel(FwdParams p) {
     if (p.lse != nullptr && lane == 0) p.lse[row] = lse;
 }
 
+// The fixed-batch ping-pong kernel with p.exp2_poly of each lane's 32
+// exponentials per tile on the polynomial (4, 8 or 16), on `grid` workgroups.
+template <int D, bool CAUSAL>
+hipError_t launch_poly(const FwdParams &p, int grid, hipStream_t s) {
+    const dim3 g((unsigned)grid), b(512);
+    switch (p.exp2_poly) {
+    case 4:
+        hipLaunchKernelGGL((attn_fwd_pp_kernel<D, CAUSAL, false, NS, false, 4>), g, b, 0, s, p);
+        break;
+    case 8:
+        hipLaunchKernelGGL((attn_fwd_pp_kernel<D, CAUSAL, false, NS, false, 8>), g, b, 0, s, p);
+        break;
+    case 16:
+        hipLaunchKernelGGL((attn_fwd_pp_kernel<D, CAUSAL, false, NS, false, 16>), g, b, 0, s, p);
+        break;
+    default:
+        return hipErrorInvalidValue;
+    }
+    return hipGetLastError();
+}
+
 template <int D, bool CAUSAL, bool VARLEN, bool SPLIT, int NW = 8>
 hipError_t launch_t(const FwdParams &p_in, hipStream_t s) {
     FwdParams p = p_in;
@@ -1407,6 +1440,9 @@ hipError_t launch_t(const FwdParams &p_in, hipStream_t s) {
         const hipError_t e = current_cu_count(&cus);
         if (e != hipSuccess) return e;
         if constexpr (NW == 8 && !SPLIT) {
+            // the polynomial share of the exponentials: the ping-pong kernel
+            // at every grid size (it walks any number of items per workgroup)
+            if (p.exp2_poly > 0) return launch_poly<D, CAUSAL>(p, cus > 0 && grid > cus ? cus : grid, s);
             // fewer 256-row items than CUs: 128-row items on 4-wave
             // workgroups occupy more CUs (one wave per SIMD instead of two)
             if (cus > 0 && items < cus && p.Sq > 128)

@@ -68,6 +68,10 @@ struct FwdParams {
     // debug bits (host only, chosen at launch): 2 = NaN-poison retired LDS
     // stages, 4 = 3-stage K/V ring, 6 = both (fixed-batch prefill)
     int debug;
+    // fixed-batch prefill: of each lane's 32 exponentials per key tile, this
+    // many (0, 4, 8 or 16) by the polynomial of exp2_poly.h (host only,
+    // chosen at launch)
+    int exp2_poly;
     // ragged batch on a persistent grid with a cost-sorted item list (set by
     // the launcher when the list fits the kSched* bounds)
     int compact;
