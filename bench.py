@@ -76,7 +76,7 @@ def decode_bytes(B, Hq, Hkv, Skv, d, kv_elem_bytes=2):
 
 TRAFFIC_PATH = os.path.join(ROOT, "profiles", "traffic.json")
 # which kernels make up each reported path (substrings of the rocprofv3 names)
-TRAFFIC_KERNELS = {"prefill": ["attn_fwd_pp_kernel<128, true, false, 4, false>"],
+TRAFFIC_KERNELS = {"prefill": ["attn_fwd_pp_kernel<128, true, false, 4, false, 0>"],
                    "decode": ["attn_decode_split_kernel<128, false, true, false>",
                               "attn_decode_combine_kernel<128, false>"],
                    "decode_fp8": ["attn_decode_split_kernel<128, true, false, false>"],
@@ -169,7 +169,7 @@ COUNTER_PASSES = [
     ["GRBM_GUI_ACTIVE", "SQ_INSTS_VALU", "SQ_INSTS_SALU", "SQ_INSTS_LDS", "SQ_ACTIVE_INST_LDS",
      "SQ_LDS_BANK_CONFLICT", "SQ_WAIT_INST_LDS", "SQ_INSTS_VMEM", "SQ_ACTIVE_INST_ANY"],
 ]
-COUNTER_KERNELS = {"prefill": "attn_fwd_pp_kernel<128, true, false, 4, false>",
+COUNTER_KERNELS = {"prefill": "attn_fwd_pp_kernel<128, true, false, 4, false, 0>",
                    "decode": "attn_decode_split_kernel<128, false, true, false>",
                    "decode_fp8": "attn_decode_split_kernel<128, true, false, false>",
                    "kmeans": "kmeans_assign_kernel<128, 128>"}
@@ -668,7 +668,7 @@ def main():
         "prefill_ms": {"mean": round(pre_avg, 5), "cold": round(cold_prefill_ms, 5)},
         "roofline": {"bound": "mfma", "achieved": round(tflops, 2), "peak": PEAK_BF16_TFLOPS,
                      "unit": "TFLOP/s", "frac": round(tflops / PEAK_BF16_TFLOPS, 4),
-                     "traffic": traffic, "kernel": "attn_fwd_pp_kernel<128, true, false, 4, false>",
+                     "traffic": traffic, "kernel": "attn_fwd_pp_kernel<128, true, false, 4, false, 0>",
                      "counters": load_counters("prefill")},
         "decode": {
             "value": round(gbs, 1), "unit": "GB/s",

@@ -70,9 +70,8 @@ attn_status_t fwd_impl(const void *q, const void *k, const void *v, void *o, flo
     p.ntiles = ntiles;
     p.c = scale * attn::kLog2e;
     p.debug = debug_flags();
-    p.exp2_poly = exp2_poly;
     const int ns = num_splits > 0 ? num_splits : fwd_pick_splits(B, Hq, Sq, Skv, causal != 0);
-    if (ns <= 1) return finish(attn::launch_fwd(p, d, causal != 0, false, stream), stream);
+    if (ns <= 1) return finish(attn::launch_fwd(p, d, causal != 0, false, stream, exp2_poly), stream);
     const attn_status_t ws = workspace_status(workspace, workspace_bytes,
                                               fwd_ws_bytes(B, Hq, Sq, d, ns));
     if (ws != ATTN_OK) return ws;

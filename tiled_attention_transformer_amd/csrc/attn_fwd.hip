@@ -1341,6 +1341,7 @@ void attn_fwd_pp_kernel(FwdParams p) {
     wait_vmcnt<0>();                     // no load may outlive the workgroup
 }
 
+
 // Merge of the split-KV shares, one wave per query row: LSE = M + log(sum_s
 // exp(lse_s - M)), O = sum_s exp(lse_s - LSE) O_s (the decode merge, per row).
 template <int D>
@@ -1377,12 +1378,12 @@ __global__ __launch_bounds__(256) void attn_fwd_merge_kernel(FwdParams p) {
     if (p.lse != nullptr && lane == 0) p.lse[row] = lse;
 }
 
-// The fixed-batch ping-pong kernel with p.exp2_poly of each lane's 32
+// The fixed-batch ping-pong kernel with `share` of each lane's 32
 // exponentials per tile on the polynomial (4, 8 or 16), on `grid` workgroups.
 template <int D, bool CAUSAL>
-hipError_t launch_poly(const FwdParams &p, int grid, hipStream_t s) {
+hipError_t launch_poly(const FwdParams &p, int share, int grid, hipStream_t s) {
     const dim3 g((unsigned)grid), b(512);
-    switch (p.exp2_poly) {
+    switch (share) {
     case 4:
         hipLaunchKernelGGL((attn_fwd_pp_kernel<D, CAUSAL, false, NS, false, 4>), g, b, 0, s, p);
         break;
@@ -1399,7 +1400,7 @@ hipError_t launch_poly(const FwdParams &p, int grid, hipStream_t s) {
 }
 
 template <int D, bool CAUSAL, bool VARLEN, bool SPLIT, int NW = 8>
-hipError_t launch_t(const FwdParams &p_in, hipStream_t s) {
+hipError_t launch_t(const FwdParams &p_in, hipStream_t s, int exp2_poly = 0) {
     FwdParams p = p_in;
     // the host counts 256-row tiles; the 4-wave variant has 128-row ones (a
     // ragged batch: twice the count, an upper bound for every sequence; the
@@ -1442,7 +1443,7 @@ hipError_t launch_t(const FwdParams &p_in, hipStream_t s) {
         if constexpr (NW == 8 && !SPLIT) {
             // the polynomial share of the exponentials: the ping-pong kernel
             // at every grid size (it walks any number of items per workgroup)
-            if (p.exp2_poly > 0) return launch_poly<D, CAUSAL>(p, cus > 0 && grid > cus ? cus : grid, s);
+            if (exp2_poly > 0) return launch_poly<D, CAUSAL>(p, exp2_poly, cus > 0 && grid > cus ? cus : grid, s);
             // fewer 256-row items than CUs: 128-row items on 4-wave
             // workgroups occupy more CUs (one wave per SIMD instead of two)
             if (cus > 0 && items < cus && p.Sq > 128)
@@ -1482,16 +1483,20 @@ hipError_t launch_t(const FwdParams &p_in, hipStream_t s) {
 
 }  // namespace
 
-hipError_t launch_fwd(const FwdParams &p, int d, bool causal, bool varlen, hipStream_t s) {
+hipError_t launch_fwd(const FwdParams &p, int d, bool causal, bool varlen, hipStream_t s,
+                      int exp2_poly) {
+    if (varlen && exp2_poly != 0) return hipErrorInvalidValue;
     if (d == 128) {
         if (varlen)
             return causal ? launch_t<128, true, true, false>(p, s) : launch_t<128, false, true, false>(p, s);
-        return causal ? launch_t<128, true, false, false>(p, s) : launch_t<128, false, false, false>(p, s);
+        return causal ? launch_t<128, true, false, false>(p, s, exp2_poly)
+                      : launch_t<128, false, false, false>(p, s, exp2_poly);
     }
     if (d == 64) {
         if (varlen)
             return causal ? launch_t<64, true, true, false>(p, s) : launch_t<64, false, true, false>(p, s);
-        return causal ? launch_t<64, true, false, false>(p, s) : launch_t<64, false, false, false>(p, s);
+        return causal ? launch_t<64, true, false, false>(p, s, exp2_poly)
+                      : launch_t<64, false, false, false>(p, s, exp2_poly);
     }
     return hipErrorInvalidValue;
 }

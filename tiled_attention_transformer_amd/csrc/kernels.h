@@ -68,10 +68,6 @@ struct FwdParams {
     // debug bits (host only, chosen at launch): 2 = NaN-poison retired LDS
     // stages, 4 = 3-stage K/V ring, 6 = both (fixed-batch prefill)
     int debug;
-    // fixed-batch prefill: of each lane's 32 exponentials per key tile, this
-    // many (0, 4, 8 or 16) by the polynomial of exp2_poly.h (host only,
-    // chosen at launch)
-    int exp2_poly;
     // ragged batch on a persistent grid with a cost-sorted item list (set by
     // the launcher when the list fits the kSched* bounds)
     int compact;
@@ -116,7 +112,10 @@ struct AssignParams {
     int N, K;
 };
 
-hipError_t launch_fwd(const FwdParams &p, int d, bool causal, bool varlen, hipStream_t s);
+// exp2_poly: for fixed batches, of each lane's 32 exponentials per key tile
+// this many (0, 4, 8 or 16) by the polynomial of exp2_poly.h
+hipError_t launch_fwd(const FwdParams &p, int d, bool causal, bool varlen, hipStream_t s,
+                      int exp2_poly = 0);
 hipError_t launch_fwd_split(const FwdParams &p, int d, bool causal, hipStream_t s);
 hipError_t launch_decode(const DecParams &p, int d, bool fp8, hipStream_t s);
 hipError_t launch_kmeans_assign(const AssignParams &p, int d, hipStream_t s);
