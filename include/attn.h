@@ -22,7 +22,9 @@
  *    (lse), passed as raw DEVICE pointers.  The caller allocates and owns
  *    every buffer; the library allocates nothing.  The only state it keeps
  *    between calls is a per-device cache of the compute-unit count (read
- *    once, a property of the device), so calls are thread-safe.
+ *    once, a property of the device) and, for attn_decode_noalloc alone, its
+ *    fixed device array and that array's per-device address (below); every
+ *    other entry point is thread-safe.
  *  * Pointers to bf16 tensors must be 16-byte aligned; lse and the decode
  *    workspace 4- and 16-byte aligned respectively.
  *  * Head grouping (GQA/MQA): query head h reads KV head h / (Hq / Hkv);
