@@ -82,9 +82,10 @@ def test_poly_share_deterministic(api, dev):
 
 
 def test_poly_causal_prefill_workload_every_row(api, dev):
-    """Workload 2 (B4 H16 S2048 d128, causal) with a quarter of the
-    exponentials on the polynomial: every row against the C oracle, and the
-    distance to the hardware-exponential path printed for the record."""
+    """Workload 2 (B4 H16 S2048 d128, causal) with 4, 8 and 16 of each
+    lane's 32 exponentials per tile on the polynomial: every row against the
+    C oracle, and the distance to the hardware-exponential path printed for
+    the record."""
     spec, data = si.make_workload("causal_prefill")
     o_ref, lse_ref = cpu.attn_full(data["q"], data["k"], data["v"], spec["scale"], True)
     o_hw, l_hw = run(api, dev, data, spec["scale"], True, None)
@@ -96,3 +97,17 @@ def test_poly_causal_prefill_workload_every_row(api, dev):
         print("workload 2 poly %d: max|dO| %.4g max|dLSE| %.3g vs oracle; vs hardware exp2: "
               "max|dO| %.4g max|dLSE| %.3g" % (poly, *err, np.abs(o - o_hw).max(),
                                                  np.abs(lse - l_hw).max()), flush=True)
+
+
+@pytest.mark.parametrize("spread", [2.0, 4.0, 8.0])
+def test_poly_share_sharp_logits(api, dev, spread):
+    """Logits at 2-8x the default spread (rows dominated by a few keys, most
+    weights far below 1, where a polynomial's relative error matters most)
+    with half of the exponentials on the polynomial: the same bars."""
+    B, Sq, Skv, Hq, Hkv, d, causal = 2, 333, 333, 4, 2, 128, True
+    scale = float(np.float32(spread / np.sqrt(d)))
+    data = si.make_prefill(1500 + int(spread), B, Hq, Hkv, Sq, Skv, d)
+    o, lse = run(api, dev, data, scale, causal, 16)
+    o_ref, lse_ref = cpu.attn_full(data["q"], data["k"], data["v"], scale, causal)
+    err = assert_close(bf16_to_np(o), o_ref, f32_to_np(lse), lse_ref, "sharp x%g poly 16" % spread)
+    print("sharp logits x%g, poly 16 of 32: max|dO| %.4g max|dLSE| %.3g" % (spread, *err), flush=True)
