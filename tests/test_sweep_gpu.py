@@ -13,7 +13,12 @@ The random shapes keep the logits within twice the default spread (scale
 times query size at most 2 / sqrt(d)); a separate band takes them to 2-8x,
 where the weights concentrate on a few keys, and prints the max |dO| it
 reaches against the same bars.
+
+ATTN_SWEEP_SCALE=k (environment, default 1) draws k times as many shapes
+per family from the same seeds; the first draws are the default cases.
 """
+import os
+
 import numpy as np
 import pytest
 
@@ -71,12 +76,15 @@ def _draw_prefill(n, seed=2027):
     return cases
 
 
-PREFILL = _draw_prefill(24)
+_K = max(1, int(os.environ.get("ATTN_SWEEP_SCALE", "1")))
+PREFILL = _draw_prefill(24 * _K)
 
 
 @pytest.mark.parametrize("case", PREFILL, ids=lambda c: "%d_B%d_Sq%d_Skv%d_Hq%d_Hkv%d_d%d_%s_s%d" % (
     *c[:7], "causal" if c[7] else "full", c[8]))
 def test_random_prefill_and_splitkv(api, dev, case):
+    """attn_fwd, attn_fwd_splitkv (the case's split count) and
+    attn_fwd_exp2_poly (4, 8 or 16 of 32 by case) against the oracle."""
     import torch
     i, B, Sq, Skv, Hq, Hkv, d, causal, splits = case
     rng = np.random.default_rng(500 + i)
@@ -87,10 +95,14 @@ def test_random_prefill_and_splitkv(api, dev, case):
     q, k, v = (to_dev(data[x], dev) for x in "qkv")
     o1, l1 = api.attn_fwd(q, k, v, scale=scale, causal=causal)
     o2, l2 = api.attn_fwd_splitkv(q, k, v, scale=scale, causal=causal, num_splits=splits)
+    share = (4, 8, 16)[i % 3]
+    o3, l3 = api.attn_fwd_exp2_poly(q, k, v, share, scale=scale, causal=causal)
     torch.cuda.synchronize()
     o_ref, lse_ref = cpu.attn_full(data["q"], data["k"], data["v"], scale, causal)
     assert_close(bf16_to_np(o1), o_ref, f32_to_np(l1), lse_ref, "attn_fwd %s" % (case,))
     assert_close(bf16_to_np(o2), o_ref, f32_to_np(l2), lse_ref, "attn_fwd_splitkv %s" % (case,))
+    assert_close(bf16_to_np(o3), o_ref, f32_to_np(l3), lse_ref,
+                 "attn_fwd_exp2_poly %d %s" % (share, case))
     if causal and Sq > Skv:
         dead = Sq - Skv
         for o in (o1, o2):
@@ -115,7 +127,7 @@ def _draw_sharp(n, seed=2031):
     return cases
 
 
-SHARP = _draw_sharp(12)
+SHARP = _draw_sharp(12 * _K)
 
 
 @pytest.mark.parametrize("case", SHARP, ids=lambda c: "%d_B%d_Sq%d_Skv%d_Hq%d_Hkv%d_d%d_%s_x%.2f" % (
@@ -170,7 +182,7 @@ def _draw_varlen(n, seed=2028):
     return cases
 
 
-VARLEN = _draw_varlen(12)
+VARLEN = _draw_varlen(12 * _K)
 
 
 @pytest.mark.parametrize("case", VARLEN, ids=lambda c: "%d_d%d_Hq%d_Hkv%d_%s_n%d" % (
@@ -216,7 +228,7 @@ def _draw_decode(n, seed=2029):
     return cases
 
 
-DECODE = _draw_decode(16)
+DECODE = _draw_decode(16 * _K)
 
 
 @pytest.mark.parametrize("case", DECODE, ids=lambda c: "%d_%s_B%d_Hq%d_Hkv%d_Skv%d_d%d_s%d_p%d" % c)
