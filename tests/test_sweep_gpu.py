@@ -105,7 +105,7 @@ def test_random_prefill_and_splitkv(api, dev, case):
                  "attn_fwd_exp2_poly %d %s" % (share, case))
     if causal and Sq > Skv:
         dead = Sq - Skv
-        for o in (o1, o2):
+        for o in (o1, o2, o3):
             assert torch.count_nonzero(o[:, :dead].float()).item() == 0
 
 
