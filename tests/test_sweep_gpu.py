@@ -128,6 +128,13 @@ def _draw_sharp(n, seed=2031):
 
 
 SHARP = _draw_sharp(12 * _K)
+# Case 109 (drawn from ATTN_SWEEP_SCALE=10 on): max |dO| 0.0231 at 5.92x the
+# default spread.  The cause is modelled on the host in
+# tests/test_sharp_limit.py: a dominant key whose bf16 weight is inexact
+# under rescale skipping, at |O| >= 4.  Strict: a pass means the limit moved.
+_SHARP_LIMIT = {109: "bf16 weights under rescale skipping at |O| >= 4 (tests/test_sharp_limit.py)"}
+SHARP = [pytest.param(c, marks=pytest.mark.xfail(strict=True, reason=_SHARP_LIMIT[c[0]]))
+         if c[0] in _SHARP_LIMIT else c for c in SHARP]
 
 
 @pytest.mark.parametrize("case", SHARP, ids=lambda c: "%d_B%d_Sq%d_Skv%d_Hq%d_Hkv%d_d%d_%s_x%.2f" % (
