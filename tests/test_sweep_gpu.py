@@ -14,6 +14,8 @@ times query size at most 2 / sqrt(d)); a separate band takes them to 2-8x,
 where the weights concentrate on a few keys, and prints the max |dO| it
 reaches against the same bars.
 
+A second sharp band runs the decode at 2-8x.
+
 ATTN_SWEEP_SCALE=k (environment, default 1) draws k times as many shapes
 per family from the same seeds; the first draws are the default cases.
 """
@@ -296,3 +298,39 @@ def test_random_decode(api, dev, case):
                                          dense_v[b:b + 1, :n], scale)
                 o_ref[b], lse_ref[b] = ob[0], lb[0]
     assert_close(bf16_to_np(o), o_ref, f32_to_np(lse), lse_ref, str(case))
+
+
+def _draw_sharp_decode(n, seed=2032):
+    """Decode shapes for the sharp-logit band (2-8x the default spread)."""
+    rng = np.random.default_rng(seed)
+    cases = []
+    for i in range(n):
+        d = int(rng.choice([64, 128]))
+        Hkv = int(rng.choice([1, 2, 8]))
+        Hq = Hkv * int(rng.choice([1, 4, 8]))
+        B = int(rng.choice([1, 4, 16]))
+        Skv = _length(rng, 3000)
+        splits = int(rng.choice([0, 1, 8]))
+        spread = float(np.exp(rng.uniform(np.log(2.0), np.log(8.0))))
+        cases.append((i, B, Hq, Hkv, Skv, d, splits, round(spread, 3)))
+    return cases
+
+
+SHARP_DECODE = _draw_sharp_decode(8 * _K)
+
+
+@pytest.mark.parametrize("case", SHARP_DECODE, ids=lambda c: "%d_B%d_Hq%d_Hkv%d_Skv%d_d%d_s%d_x%.2f" % c)
+def test_sharp_logits_decode(api, dev, case):
+    """Decode at 2-8x the default logit spread (same rescale skipping and
+    bf16 weights as the prefill, so the same limit at |O| >= 4 applies):
+    the same bars; the max |dO| is printed."""
+    import torch
+    i, B, Hq, Hkv, Skv, d, splits, spread = case
+    scale = float(np.float32(spread / np.sqrt(d)))
+    data = si.make_decode(1300 + i, B, Hq, Hkv, Skv, d)
+    q, k, v = (to_dev(data[x], dev) for x in "qkv")
+    o, lse = api.attn_decode(q, k, v, scale=scale, num_splits=splits)
+    torch.cuda.synchronize()
+    o_ref, lse_ref = cpu.decode_full(data["q"], data["k"], data["v"], scale)
+    err = assert_close(bf16_to_np(o), o_ref, f32_to_np(lse), lse_ref, "sharp decode %s" % (case,))
+    print("sharp decode x%.2f %s: max|dO| %.4g max|dLSE| %.3g" % (spread, case[:7], *err), flush=True)
