@@ -5,7 +5,8 @@ no-allocation decode exists).  The calls below are captured once, on a side
 stream, with every buffer allocated beforehand; the graph is then replayed
 several times, with the caller's own eager work, output poisoning and
 synchronisations between replays, and every replay must give the bits of the
-eager calls: a causal prefill, the no-allocation decode (its fixed scratch,
+eager calls: a causal prefill, the same with a polynomial share of the
+exponentials, the no-allocation decode (its fixed scratch,
 an explicit 8-way split with the merge kernel), a decode with the caller's
 workspace, and a decode split by the per-sequence lengths (whose kernel
 rewrites the workspace header every call).  Nothing in the library records a
@@ -40,6 +41,7 @@ def test_graph_replays_match_eager(api, dev):
 
     # outputs and workspaces, allocated before any capture
     o_p, l_p = torch.empty_like(q), torch.empty((2, 8, 300), dtype=torch.float32, device=dev)
+    o_e, l_e = torch.empty_like(q), torch.empty((2, 8, 300), dtype=torch.float32, device=dev)
     o_n, l_n = torch.empty_like(dq), torch.empty((8, 16), dtype=torch.float32, device=dev)
     o_w, l_w = torch.empty_like(dq), torch.empty((8, 16), dtype=torch.float32, device=dev)
     ws_w = torch.empty(api.attn_decode_workspace_bytes(8, 16, 4, 2000, 128, 8), dtype=torch.uint8,
@@ -50,13 +52,14 @@ def test_graph_replays_match_eager(api, dev):
 
     def calls(stream=None):
         api.attn_fwd(q, k, v, o=o_p, lse=l_p, scale=scale, causal=True, stream=stream)
+        api.attn_fwd_exp2_poly(q, k, v, 8, o=o_e, lse=l_e, scale=scale, causal=True, stream=stream)
         api.attn_decode_noalloc(dq, dk, dv, o=o_n, lse=l_n, scale=scale, num_splits=8, stream=stream)
         api.attn_decode(dq, dk, dv, o=o_w, lse=l_w, scale=scale, num_splits=8, workspace=ws_w,
                         stream=stream)
         api.attn_decode_varlen(rq, rk, rv, lengths, o=o_r, lse=l_r, scale=scale, workspace=ws_r,
                                stream=stream)
 
-    outs = (o_p, l_p, o_n, l_n, o_w, l_w, o_r, l_r)
+    outs = (o_p, l_p, o_e, l_e, o_n, l_n, o_w, l_w, o_r, l_r)
     calls()                          # eager (also looks up the no-allocation scratch)
     torch.cuda.synchronize()
     eager = [t.clone() for t in outs]
@@ -82,7 +85,8 @@ def test_graph_replays_match_eager(api, dev):
         (x @ x).sum().item()
         g.replay()
         torch.cuda.synchronize()
-        for name, got, want in zip(("prefill O", "prefill LSE", "no-alloc O", "no-alloc LSE",
+        for name, got, want in zip(("prefill O", "prefill LSE", "poly-share O", "poly-share LSE",
+                                    "no-alloc O", "no-alloc LSE",
                                     "decode O", "decode LSE", "by-length O", "by-length LSE"),
                                    outs, eager):
             assert torch.equal(got.view(torch.uint8), want.view(torch.uint8)), \
